@@ -1,0 +1,10 @@
+"""fp64 CPU oracle for exact scaled-dot-product attention — TEST INFRASTRUCTURE ONLY.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import this
+package.  It shares no code with the GPU path and imports nothing from it.
+"""
+from .attention import (attention, attention_head, attention_rows, decode, host_cores, kv_head,
+                        masked_softmax, merge_partials, scores, useful_flops, visibility, visible_pairs)
+
+__all__ = ["attention", "attention_head", "attention_rows", "decode", "host_cores", "kv_head",
+           "masked_softmax", "merge_partials", "scores", "useful_flops", "visibility", "visible_pairs"]

@@ -1,0 +1,375 @@
+"""Checks that pin the fp64 oracle to facts fixed by the attention articles and by
+mathematics, independently of the oracle's own code.
+
+Each ``check_*`` raises AssertionError on a mismatch.  ``test_oracle.py`` runs every check;
+``test_oracle_mutants.py`` plants plausible mistakes in the oracle and requires that each
+one trips at least one check.
+
+Articles cited (by title and section):
+  [DS-Attn]  "003-注意力机制详解：从基础Attention到DeepSeek的优化策略" (lakecityint.com)
+  [LLM-Attn] "LLM中的Attention实现及优化" (zeeklog.com)
+  [MQA-GQA]  tqpw.cn article on MQA → GQA → FlashAttention
+  [Deep-Opt] "注意力机制深度优化" (kler.cn)
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "worked_example.json")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------------------------------------
+# Pure-Python brute force: a triple loop written from the definition with math.exp / math.fsum.
+# Visibility is spelled differently from the oracle on purpose (distance from the query's
+# position instead of index comparisons).
+
+def brute_force(q, k, v, scale, causal, window):
+    B, Hq, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    group = Hq // Hkv
+    O = np.zeros((B, Hq, Lq, v.shape[3]))
+    LSE = np.zeros((B, Hq, Lq))
+    for b in range(B):
+        for h in range(Hq):
+            kh = h // group
+            for i in range(Lq):
+                pos = i + Lk - Lq
+                keys = []
+                for j in range(Lk):
+                    dist = pos - j                   # how far back key j lies
+                    if causal and dist < 0:
+                        continue
+                    if window and dist >= window:
+                        continue
+                    keys.append(j)
+                if not keys:
+                    O[b, h, i] = 0.0
+                    LSE[b, h, i] = -math.inf
+                    continue
+                s = [scale * math.fsum(float(q[b, h, i, c]) * float(k[b, kh, j, c]) for c in range(d)) for j in keys]
+                mx = max(s)
+                w = [math.exp(x - mx) for x in s]
+                tot = math.fsum(w)
+                for c in range(v.shape[3]):
+                    O[b, h, i, c] = math.fsum(wj * float(v[b, kh, j, c]) for wj, j in zip(w, keys)) / tot
+                LSE[b, h, i] = mx + math.log(tot)
+    return O, LSE
+
+
+TINY_SHAPES = [
+    # (Hq, Hkv, Lq, Lk, d)
+    (1, 1, 1, 1, 1),
+    (2, 1, 3, 5, 3),
+    (4, 2, 5, 3, 4),
+    (2, 2, 7, 7, 8),
+    (4, 1, 12, 12, 2),
+    (2, 1, 12, 9, 5),
+]
+TINY_MODES = [(False, 0), (True, 0), (True, 1), (True, 2), (True, 5)]
+
+
+def check_brute_force(seed=11):
+    rng = _rng(seed)
+    for (Hq, Hkv, Lq, Lk, d) in TINY_SHAPES:
+        q = rng.standard_normal((1, Hq, Lq, d))
+        k = rng.standard_normal((1, Hkv, Lk, d))
+        v = rng.standard_normal((1, Hkv, Lk, d))
+        scale = 0.7
+        for causal, window in TINY_MODES:
+            O, L = oracle.attention(q, k, v, scale=scale, causal=causal, window=window)
+            Ob, Lb = brute_force(q, k, v, scale, causal, window)
+            assert np.array_equal(np.isneginf(L), np.isneginf(Lb)), (Hq, Hkv, Lq, Lk, d, causal, window)
+            fin = np.isfinite(Lb)
+            assert np.max(np.abs(O - Ob)) <= 1e-12, (Hq, Hkv, Lq, Lk, d, causal, window)
+            assert np.max(np.abs(L[fin] - Lb[fin]), initial=0) <= 1e-12, (Hq, Hkv, Lq, Lk, d, causal, window)
+
+
+# ---------------------------------------------------------------------------------------------
+# Library routine: torch's CPU scaled_dot_product_attention in float64 (square shapes only,
+# because its is_causal is aligned top-left; GQA through enable_gqa, which expands KV heads
+# to consecutive query heads).
+
+def check_torch_sdpa(seed=12):
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(seed)
+    for (B, Hq, Hkv, L, d) in [(2, 4, 4, 33, 16), (1, 8, 2, 40, 8), (1, 6, 1, 17, 32)]:
+        q = rng.standard_normal((B, Hq, L, d))
+        k = rng.standard_normal((B, Hkv, L, d))
+        v = rng.standard_normal((B, Hkv, L, d))
+        for causal in (False, True):
+            scale = 1.0 / math.sqrt(d)
+            O, _ = oracle.attention(q, k, v, scale=scale, causal=causal)
+            ref = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                                                 is_causal=causal, scale=scale, enable_gqa=(Hq != Hkv)).numpy()
+            assert np.max(np.abs(O - ref)) <= 1e-12, (B, Hq, Hkv, L, d, causal)
+
+
+# ---------------------------------------------------------------------------------------------
+# Invariants and closed forms.
+
+def check_softmax_rows(seed=13):
+    """Rows of P sum to one, P >= 0, P is exactly 0 where masked ([DS-Attn §一] safe softmax)."""
+    rng = _rng(seed)
+    for (Lq, Lk, causal, window) in [(9, 9, False, 0), (9, 9, True, 0), (9, 14, True, 3), (14, 9, True, 0)]:
+        S = rng.standard_normal((Lq, Lk)) * 5
+        vis = oracle.visibility(Lq, Lk, causal, window)
+        P, lse = oracle.masked_softmax(S, vis)
+        nonempty = vis.any(axis=1)
+        assert np.all(P >= 0)
+        assert np.all(P[~vis] == 0.0)
+        assert np.max(np.abs(P[nonempty].sum(axis=1) - 1.0), initial=0) <= 1e-13
+        assert np.all(P[~nonempty] == 0.0) and np.all(np.isneginf(lse[~nonempty]))
+        # LSE is the log of the visible sum of exp(S) (direct evaluation; scores are small here)
+        direct = np.array([math.log(math.fsum(math.exp(S[i, j]) for j in range(Lk) if vis[i, j]))
+                           for i in range(Lq) if nonempty[i]])
+        assert np.max(np.abs(lse[nonempty] - direct)) <= 1e-12
+
+
+def check_constant_scores(seed=14):
+    """scale = 0 makes every visible weight equal: O_i = mean of the visible V rows and
+    LSE_i = ln(number of visible keys)."""
+    rng = _rng(seed)
+    B, Hq, Hkv, L, d = 1, 4, 2, 11, 6
+    q = rng.standard_normal((B, Hq, L, d))
+    k = rng.standard_normal((B, Hkv, L, d))
+    v = rng.standard_normal((B, Hkv, L, d))
+    O, LSE = oracle.attention(q, k, v, scale=0.0)
+    for h in range(Hq):
+        assert np.allclose(O[0, h], np.broadcast_to(v[0, h // 2].mean(axis=0), (L, d)), atol=1e-13)
+        assert np.allclose(LSE[0, h], math.log(L), atol=1e-13)
+    O, LSE = oracle.attention(q, k, v, scale=0.0, causal=True)
+    for h in range(Hq):
+        for i in range(L):
+            assert np.allclose(O[0, h, i], v[0, h // 2, :i + 1].mean(axis=0), atol=1e-13)
+            assert abs(LSE[0, h, i] - math.log(i + 1)) <= 1e-13
+    O, LSE = oracle.attention(q, k, v, scale=0.0, causal=True, window=4)
+    for i in range(L):
+        lo = max(0, i - 3)
+        assert np.allclose(O[0, 0, i], v[0, 0, lo:i + 1].mean(axis=0), atol=1e-13)
+        assert abs(LSE[0, 0, i] - math.log(i + 1 - lo)) <= 1e-13
+
+
+def check_causal_boundary(seed=15):
+    """Causal row 0 sees only key 0: O = V_0 and LSE = scale q_0.k_0.  With one key and no
+    mask every row returns V_0.  With Lq > Lk (bottom-right alignment) the first Lq - Lk rows
+    see nothing: O = 0 and LSE = -inf."""
+    rng = _rng(seed)
+    q = rng.standard_normal((1, 2, 8, 5))
+    k = rng.standard_normal((1, 2, 8, 5))
+    v = rng.standard_normal((1, 2, 8, 5))
+    O, LSE = oracle.attention(q, k, v, scale=0.3, causal=True)
+    for h in range(2):
+        assert np.allclose(O[0, h, 0], v[0, h, 0], atol=1e-15)
+        assert abs(LSE[0, h, 0] - 0.3 * float(q[0, h, 0] @ k[0, h, 0])) <= 1e-13
+    O, LSE = oracle.attention(q, k[:, :, :1], v[:, :, :1], scale=0.3)
+    assert np.allclose(O, np.broadcast_to(v[:, :, :1], O.shape), atol=1e-15)
+    O, LSE = oracle.attention(q, k[:, :, :3], v[:, :, :3], scale=0.3, causal=True)
+    assert np.all(O[:, :, :5] == 0.0) and np.all(np.isneginf(LSE[:, :, :5]))
+    assert np.allclose(O[0, 0, 5], v[0, 0, 0], atol=1e-15)       # position 0: key 0 only
+    assert np.all(np.isfinite(LSE[:, :, 5:]))
+
+
+def check_window_convention(seed=16):
+    """[LLM-Attn] each token attends to at most the previous W tokens, read as W keys counting
+    itself: W = 1 gives O_i = V_i and LSE_i = scale q_i.k_i; W >= L equals plain causal;
+    W = L - 1 differs from causal only in the last row."""
+    rng = _rng(seed)
+    L = 10
+    q = rng.standard_normal((1, 2, L, 4))
+    k = rng.standard_normal((1, 2, L, 4))
+    v = rng.standard_normal((1, 2, L, 4))
+    O, LSE = oracle.attention(q, k, v, scale=0.5, causal=True, window=1)
+    assert np.allclose(O, v, atol=1e-15)
+    assert np.allclose(LSE, 0.5 * np.einsum("bhid,bhid->bhi", q, k), atol=1e-13)
+    Oc, Lc = oracle.attention(q, k, v, scale=0.5, causal=True)
+    for W in (L, L + 5):
+        Ow, Lw = oracle.attention(q, k, v, scale=0.5, causal=True, window=W)
+        assert np.array_equal(Ow, Oc) and np.array_equal(Lw, Lc)
+    Ow, Lw = oracle.attention(q, k, v, scale=0.5, causal=True, window=L - 1)
+    assert np.array_equal(Ow[:, :, :L - 1], Oc[:, :, :L - 1])
+    assert np.all(np.abs(Ow[:, :, L - 1] - Oc[:, :, L - 1]) > 0)
+
+
+def check_gqa_mapping(seed=17):
+    """Hkv = Hq is plain MHA; GQA/MQA equal MHA over K/V repeated to consecutive query heads
+    ([LLM-Attn] repeat_kv; [MQA-GQA §2.1] MQA broadcasts one K/V to every head)."""
+    rng = _rng(seed)
+    B, Hq, L, d = 2, 8, 9, 4
+    q = rng.standard_normal((B, Hq, L, d))
+    for Hkv in (8, 4, 2, 1):
+        k = rng.standard_normal((B, Hkv, L, d))
+        v = rng.standard_normal((B, Hkv, L, d))
+        g = Hq // Hkv
+        for causal in (False, True):
+            O, LSE = oracle.attention(q, k, v, scale=0.4, causal=causal)
+            krep, vrep = np.repeat(k, g, axis=1), np.repeat(v, g, axis=1)
+            Om, Lm = oracle.attention(q, krep, vrep, scale=0.4, causal=causal)
+            assert np.array_equal(O, Om) and np.array_equal(LSE, Lm)
+            # per-head restatement: head h uses K/V head h // g, checked head by head
+            for h in range(Hq):
+                Oh, _ = oracle.attention(q[:, h:h + 1], k[:, h // g:h // g + 1], v[:, h // g:h // g + 1],
+                                         scale=0.4, causal=causal)
+                assert np.array_equal(Oh[:, 0], O[:, h])
+
+
+def check_pv_invariants(seed=18):
+    """O(V + 1 c^T) = O(V) + c; O(alpha V) = alpha O(V); without a mask, permuting the keys and
+    values together leaves O unchanged."""
+    rng = _rng(seed)
+    q = rng.standard_normal((1, 2, 7, 5))
+    k = rng.standard_normal((1, 2, 7, 5))
+    v = rng.standard_normal((1, 2, 7, 5))
+    c = rng.standard_normal(5)
+    for causal, window in [(False, 0), (True, 0), (True, 3)]:
+        O, _ = oracle.attention(q, k, v, scale=0.6, causal=causal, window=window)
+        O2, _ = oracle.attention(q, k, v + c, scale=0.6, causal=causal, window=window)
+        assert np.allclose(O2, O + c, atol=1e-13)
+        O3, _ = oracle.attention(q, k, -2.5 * v, scale=0.6, causal=causal, window=window)
+        assert np.allclose(O3, -2.5 * O, atol=1e-13)
+    perm = rng.permutation(7)
+    O, L = oracle.attention(q, k, v, scale=0.6)
+    Op, Lp = oracle.attention(q, k[:, :, perm], v[:, :, perm], scale=0.6)
+    assert np.allclose(O, Op, atol=1e-13) and np.allclose(L, Lp, atol=1e-13)
+
+
+def check_lse_identity(seed=19):
+    """sum over visible j of exp(S_ij - LSE_i) = 1 and O_i = sum_j exp(S_ij - LSE_i) V_j."""
+    rng = _rng(seed)
+    Lq, Lk, d = 6, 10, 3
+    q = rng.standard_normal((1, 1, Lq, d))
+    k = rng.standard_normal((1, 1, Lk, d))
+    v = rng.standard_normal((1, 1, Lk, d))
+    for causal, window in [(False, 0), (True, 0), (True, 4)]:
+        O, LSE = oracle.attention(q, k, v, scale=0.8, causal=causal, window=window)
+        for i in range(Lq):
+            pos = i + Lk - Lq
+            js = [j for j in range(Lk) if (not causal or j <= pos) and (window == 0 or pos - j < window)]
+            s = [0.8 * float(q[0, 0, i] @ k[0, 0, j]) for j in js]
+            w = [math.exp(x - LSE[0, 0, i]) for x in s]
+            assert abs(math.fsum(w) - 1.0) <= 1e-13
+            assert np.allclose(O[0, 0, i], sum(wj * v[0, 0, j] for wj, j in zip(w, js)), atol=1e-13)
+
+
+def check_split_merge(seed=20):
+    """Attention over disjoint key chunks, merged by their LSEs, equals attention over all
+    keys (the cross-chunk form of the rescale step of [DS-Attn §二])."""
+    rng = _rng(seed)
+    Lq, Lk, d = 5, 23, 4
+    q = rng.standard_normal((1, 2, Lq, d))
+    k = rng.standard_normal((1, 2, Lk, d))
+    v = rng.standard_normal((1, 2, Lk, d))
+    O, LSE = oracle.attention(q, k, v, scale=0.5)
+    for bounds in ([0, 8, 16, 23], [0, 1, 23], [0, 11, 12, 20, 23]):
+        parts = [oracle.attention(q, k[:, :, a:b], v[:, :, a:b], scale=0.5) for a, b in zip(bounds, bounds[1:])]
+        Om, Lm = oracle.merge_partials([p[0] for p in parts], [p[1] for p in parts])
+        assert np.max(np.abs(Om - O)) <= 1e-12 and np.max(np.abs(Lm - LSE)) <= 1e-12
+    # a chunk that sees nothing (LSE = -inf) does not change the result
+    empty_o = np.zeros_like(O)
+    empty_l = np.full_like(LSE, -np.inf)
+    Om, Lm = oracle.merge_partials([O, empty_o], [LSE, empty_l])
+    assert np.max(np.abs(Om - O)) <= 1e-15 and np.max(np.abs(Lm - LSE)) <= 1e-15
+    Om, Lm = oracle.merge_partials([empty_o], [empty_l])
+    assert np.all(Om == 0) and np.all(np.isneginf(Lm))
+
+
+def check_decode_is_last_row(seed=21):
+    """A decode query is the newest token: its result equals the last row of causal prefill
+    over the same sequence, with or without a window."""
+    rng = _rng(seed)
+    Hq, Hkv, d = 4, 2, 6
+    lens = [1, 5, 9, 13]
+    N = len(lens)
+    T = sum(lens) + 7
+    kp = rng.standard_normal((T, Hkv, d))
+    vp = rng.standard_normal((T, Hkv, d))
+    offs = [2, 3 + 1, 3 + 5 + 1, 3 + 5 + 9 + 2]
+    qd = rng.standard_normal((N, Hq, d))
+    for W in (0, 1, 4, 100):
+        O, LSE = oracle.decode(qd, kp, vp, offs, lens, scale=0.35, window=W)
+        for s, (o, n) in enumerate(zip(offs, lens)):
+            ks = kp[o:o + n].transpose(1, 0, 2)[None]
+            vs = vp[o:o + n].transpose(1, 0, 2)[None]
+            qs = np.zeros((1, Hq, n, d))
+            qs[0, :, n - 1] = qd[s]
+            Op, Lp = oracle.attention(qs, ks, vs, scale=0.35, causal=True, window=W)
+            assert np.max(np.abs(O[s] - Op[0, :, n - 1])) <= 1e-13
+            assert np.max(np.abs(LSE[s] - Lp[0, :, n - 1])) <= 1e-13
+
+
+def check_pool_addressing(seed=22):
+    """Sequences placed in any order, with NaN rows between them, give the same result as a
+    packed pool ([DS-Attn §三.3]: sequences in one pool told apart by offset)."""
+    rng = _rng(seed)
+    Hq, Hkv, d = 2, 1, 3
+    lens = np.array([4, 1, 6])
+    kseq = [rng.standard_normal((n, Hkv, d)) for n in lens]
+    vseq = [rng.standard_normal((n, Hkv, d)) for n in lens]
+    qd = rng.standard_normal((3, Hq, d))
+    packed_k, packed_v = np.concatenate(kseq), np.concatenate(vseq)
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    O1, L1 = oracle.decode(qd, packed_k, packed_v, offs, lens, scale=0.9)
+    order, gaps = [2, 0, 1], [3, 0, 5, 2]
+    T = int(lens.sum()) + sum(gaps)
+    pk = np.full((T, Hkv, d), np.nan)
+    pv = np.full((T, Hkv, d), np.nan)
+    offs2 = np.zeros(3, np.int64)
+    pos = 0
+    for slot, s in enumerate(order):
+        pos += gaps[slot]
+        offs2[s] = pos
+        pk[pos:pos + lens[s]], pv[pos:pos + lens[s]] = kseq[s], vseq[s]
+        pos += lens[s]
+    O2, L2 = oracle.decode(qd, pk, pv, offs2, lens, scale=0.9)
+    assert np.all(np.isfinite(O2)) and np.array_equal(O1, O2) and np.array_equal(L1, L2)
+    # an empty sequence yields O = 0 and LSE = -inf
+    O3, L3 = oracle.decode(qd, pk, pv, offs2, np.array([4, 0, 6]), scale=0.9)
+    assert np.all(O3[1] == 0) and np.all(np.isneginf(L3[1]))
+
+
+def check_golden():
+    """Hand-derived exact values (tests/golden/worked_example.json)."""
+    g = json.load(open(GOLDEN))
+    scale = math.log(2.0)
+    q, k, v = (np.array(g[x], dtype=np.float64) for x in ("q", "k", "v"))
+    fr = np.vectorize(lambda s: float(Fraction(s)))
+    for case in g["cases"]:
+        O, LSE = oracle.attention(q, k, v, scale=scale, causal=case["causal"], window=case["window"])
+        assert np.max(np.abs(O - fr(np.array(case["o"])))) <= 1e-14, case
+        assert np.max(np.abs(LSE - np.log(fr(np.array(case["lse_exp"]))))) <= 1e-14, case
+    dec = g["decode"]
+    kp = np.array([[float(x) for x in row] for row in dec["pool_k"]])[:, None, :]
+    vp = np.array([[float(x) for x in row] for row in dec["pool_v"]])[:, None, :]
+    qd = np.array(dec["q"], dtype=np.float64)[:, None, :]
+    for case in dec["cases"]:
+        O, LSE = oracle.decode(qd, kp, vp, dec["offsets"], dec["lens"], scale=scale, window=case["window"])
+        assert np.max(np.abs(O[:, 0] - fr(np.array(case["o"])))) <= 1e-14, case
+        assert np.max(np.abs(LSE[:, 0] - np.log(fr(np.array(case["lse_exp"]))))) <= 1e-14, case
+
+
+def check_visible_pairs():
+    """The pair count used for useful FLOPs equals the number of True entries of the mask,
+    and the closed forms: Lq*Lk; L(L+1)/2 causal; W(W+1)/2 + (L-W)W with a window W < L."""
+    for (Lq, Lk, causal, W) in [(7, 7, False, 0), (7, 7, True, 0), (9, 5, True, 0), (5, 9, True, 0),
+                                (20, 20, True, 6), (20, 20, True, 25), (13, 20, True, 4)]:
+        assert oracle.visible_pairs(Lq, Lk, causal, W) == int(oracle.visibility(Lq, Lk, causal, W).sum())
+    assert oracle.visible_pairs(64, 64, False, 0) == 64 * 64
+    assert oracle.visible_pairs(64, 64, True, 0) == 64 * 65 // 2
+    assert oracle.visible_pairs(64, 64, True, 16) == 16 * 17 // 2 + (64 - 16) * 16
+
+
+ALL_CHECKS = [check_golden, check_brute_force, check_torch_sdpa, check_softmax_rows, check_constant_scores,
+              check_causal_boundary, check_window_convention, check_gqa_mapping, check_pv_invariants,
+              check_lse_identity, check_split_merge, check_decode_is_last_row, check_pool_addressing,
+              check_visible_pairs]

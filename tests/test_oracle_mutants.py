@@ -1,0 +1,133 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and require that each one fails at
+least one pin.  This shows the pins can tell a wrong oracle from a right one."""
+import importlib
+
+import numpy as np
+import pytest
+
+import oracle_pins as pins
+
+mod = importlib.import_module("oracle.attention")
+
+
+def _interleaved_kv_head(h, Hq, Hkv):
+    return h % Hkv
+
+
+def _window_one_too_wide(rows, Lq, Lk, causal, window):
+    p = rows[:, None] + (Lk - Lq)
+    j = np.arange(Lk)[None, :]
+    vis = np.ones((len(rows), Lk), dtype=bool)
+    if causal:
+        vis &= j <= p
+    if window > 0:
+        vis &= j >= p - window
+    return vis
+
+
+def _causal_top_left(rows, Lq, Lk, causal, window):
+    p = rows[:, None]
+    j = np.arange(Lk)[None, :]
+    vis = np.ones((len(rows), Lk), dtype=bool)
+    if causal:
+        vis &= j <= p
+    if window > 0:
+        vis &= j > p - window
+    return vis
+
+
+def _scale_dropped(q, k, scale):
+    return np.asarray(q, np.float64) @ np.asarray(k, np.float64).T
+
+
+def _scale_squared(q, k, scale):
+    return scale * scale * (np.asarray(q, np.float64) @ np.asarray(k, np.float64).T)
+
+
+def _make_softmax(variant):
+    orig = mod.masked_softmax
+
+    def f(S, vis):
+        if variant == "bias":       # large negative bias instead of exclusion
+            S2 = np.where(vis, S, S - 1e4)
+            m = S2.max(axis=1)
+            E = np.exp(S2 - m[:, None])
+            l = E.sum(axis=1)
+            return E / l[:, None], m + np.log(l)
+        P, lse = orig(S, vis)
+        if variant == "lse_no_max":  # dropped the max term of the LSE
+            m = np.where(vis.any(axis=1), np.where(vis, S, -np.inf).max(axis=1), 0.0)
+            return P, lse - m
+        if variant == "no_normalise":
+            E = np.where(vis, np.exp(S - np.where(vis, S, -np.inf).max(axis=1, keepdims=True)), 0.0)
+            return E, lse
+        if variant == "log2_lse":
+            return P, lse / np.log(2.0)
+        raise AssertionError(variant)
+    return f
+
+
+def _merge_unweighted(outs, lses):
+    outs, lses = np.asarray(outs, np.float64), np.asarray(lses, np.float64)
+    return outs.mean(axis=0), np.log(np.exp(lses).sum(axis=0))
+
+
+def _decode_window_from_start(q, k_pool, v_pool, offsets, lens, scale=None, window=0, threads=None, seqs=None):
+    # the window counted from the oldest key instead of the newest
+    N, Hq, d = np.asarray(q).shape
+    scale = 1 / np.sqrt(d) if scale is None else scale
+    O = np.zeros((N, Hq, d)); L = np.zeros((N, Hq))
+    for s in range(N):
+        a, n = int(offsets[s]), int(lens[s])
+        nn = min(n, window) if window else n
+        for h in range(Hq):
+            kh = h // (Hq // k_pool.shape[1])
+            o, l = mod.attention_head(np.asarray(q)[s, h][None], k_pool[a:a + nn, kh], v_pool[a:a + nn, kh], scale,
+                                      False, 0)
+            O[s, h], L[s, h] = o[0], l[0]
+    return O, L
+
+
+MUTANTS = {
+    "gqa_interleaved": ("kv_head", _interleaved_kv_head),
+    "window_off_by_one": ("_visibility_rows", _window_one_too_wide),
+    "causal_top_left": ("_visibility_rows", _causal_top_left),
+    "scale_dropped": ("scores", _scale_dropped),
+    "scale_squared": ("scores", _scale_squared),
+    "mask_as_bias": ("masked_softmax", "bias"),
+    "lse_missing_max": ("masked_softmax", "lse_no_max"),
+    "softmax_not_normalised": ("masked_softmax", "no_normalise"),
+    "lse_base2": ("masked_softmax", "log2_lse"),
+    "merge_unweighted": ("merge_partials", _merge_unweighted),
+}
+
+
+def _run_all_checks():
+    failed = []
+    for check in pins.ALL_CHECKS:
+        try:
+            check()
+        except Exception as e:  # AssertionError or a shape error from a broken oracle
+            failed.append(check.__name__)
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, repl = MUTANTS[name]
+    if attr == "masked_softmax":
+        repl = _make_softmax(repl)
+    monkeypatch.setattr(mod, attr, repl)
+    import oracle
+    if hasattr(oracle, attr):
+        monkeypatch.setattr(oracle, attr, repl)
+    failed = _run_all_checks()
+    assert failed, f"mutant {name} passed every pin"
+
+
+def test_decode_window_mutant_is_caught(monkeypatch):
+    import oracle
+    monkeypatch.setattr(oracle, "decode", _decode_window_from_start)
+    monkeypatch.setattr(mod, "decode", _decode_window_from_start)
+    failed = _run_all_checks()
+    assert failed

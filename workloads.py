@@ -1,0 +1,168 @@
+"""Seeded synthetic workloads shared by the oracle tests, the GPU parity tests and bench.py.
+
+This module only draws numbers and lays buffers out. It holds none of the attention
+arithmetic, so neither side of a parity comparison borrows the other's maths from here.
+
+Every tensor is drawn as float32 N(0, 1) from a seeded ``torch.Generator`` in the order
+q, k, v and then rounded to the working dtype (``Tensor.to`` rounds to nearest even).
+The shapes follow the attention articles' own workloads: a 1024-token MHA block, a
+4096-token GQA model with 32 query heads over 8 KV heads and head size 128, a 16k
+sequence under a 4k sliding window, and a decode batch whose KV caches sit in one pooled
+buffer addressed by per-sequence offsets.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class PrefillConfig:
+    name: str
+    dtype: str          # "f32" or "bf16"
+    B: int
+    Hq: int
+    Hkv: int
+    Lq: int
+    Lk: int
+    d: int
+    causal: bool
+    window: int
+    seed: int
+    return_lse: bool = True
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.d))
+
+
+@dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    n_seq: int
+    Hq: int
+    Hkv: int
+    d: int
+    len_lo: int
+    len_hi: int
+    lens_seed: int
+    value_seed: int
+    window: int = 0
+    max_gap: int = 255  # poisoned rows placed between sequences in the pool
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.d))
+
+
+# The five workloads the hot path is specified on (the tiny fp32 one in two mask modes).
+PREFILL = {
+    "mha_f32_L128": PrefillConfig("mha_f32_L128", "f32", 1, 2, 2, 128, 128, 64, False, 0, 1001),
+    "mha_f32_L128_causal": PrefillConfig("mha_f32_L128_causal", "f32", 1, 2, 2, 128, 128, 64, True, 0, 1001),
+    "mha_bf16_L1024": PrefillConfig("mha_bf16_L1024", "bf16", 4, 16, 16, 1024, 1024, 64, False, 0, 1002),
+    "gqa_causal_bf16_L4096": PrefillConfig("gqa_causal_bf16_L4096", "bf16", 2, 32, 8, 4096, 4096, 128, True, 0, 1003),
+    "swa_gqa_bf16_L16384_W4096": PrefillConfig("swa_gqa_bf16_L16384_W4096", "bf16", 1, 32, 8, 16384, 16384, 128,
+                                               True, 4096, 1004),
+}
+
+DECODE = {
+    "gqa_decode_bf16": DecodeConfig("gqa_decode_bf16", 64, 32, 8, 128, 1024, 32768, 1005, 1005),
+    "mqa_decode_bf16": DecodeConfig("mqa_decode_bf16", 64, 32, 1, 128, 1024, 32768, 1005, 1006),
+}
+
+
+def normal(shape, gen: torch.Generator, device, dtype) -> torch.Tensor:
+    """float32 N(0, 1) from ``gen``, then rounded to ``dtype``."""
+    x = torch.randn(*shape, generator=gen, device=device, dtype=torch.float32)
+    return x.to(dtype)
+
+
+def make_generator(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def prefill_inputs(B, Hq, Hkv, Lq, Lk, d, *, seed, dtype=torch.bfloat16, device="cpu"):
+    """q [B, Hq, Lq, d], k and v [B, Hkv, Lk, d], contiguous, drawn in the order q, k, v."""
+    g = make_generator(seed, device)
+    q = normal((B, Hq, Lq, d), g, device, dtype)
+    k = normal((B, Hkv, Lk, d), g, device, dtype)
+    v = normal((B, Hkv, Lk, d), g, device, dtype)
+    return q, k, v
+
+
+def prefill_inputs_for(cfg: PrefillConfig, device="cpu"):
+    return prefill_inputs(cfg.B, cfg.Hq, cfg.Hkv, cfg.Lq, cfg.Lk, cfg.d, seed=cfg.seed,
+                          dtype=cfg.torch_dtype, device=device)
+
+
+def decode_lens(n_seq: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """KV lengths uniform on [lo, hi] (both ends included)."""
+    return np.random.default_rng(seed).integers(lo, hi, size=n_seq, endpoint=True).astype(np.int32)
+
+
+@dataclass
+class PoolLayout:
+    lens: np.ndarray        # int32 [n_seq]
+    offsets: np.ndarray     # int64 [n_seq], first pool row of each sequence
+    total_rows: int         # pool rows T, gaps included
+    gaps: list = field(default_factory=list)  # (start, length) of each poisoned gap
+
+
+def pool_layout(lens: np.ndarray, seed: int, max_gap: int = 255, shuffle: bool = True) -> PoolLayout:
+    """Place sequences in one pool in a seeded random order, with a seeded gap of 0..max_gap
+    rows before each one and after the last.  Offsets are in token rows."""
+    rng = np.random.default_rng(seed + 7919)
+    n = len(lens)
+    order = rng.permutation(n) if shuffle else np.arange(n)
+    gaps = rng.integers(0, max_gap, size=n + 1, endpoint=True) if max_gap > 0 else np.zeros(n + 1, np.int64)
+    offsets = np.zeros(n, np.int64)
+    pos = 0
+    gap_list = []
+    for slot, s in enumerate(order):
+        if gaps[slot]:
+            gap_list.append((pos, int(gaps[slot])))
+        pos += int(gaps[slot])
+        offsets[s] = pos
+        pos += int(lens[s])
+    if gaps[n]:
+        gap_list.append((pos, int(gaps[n])))
+    pos += int(gaps[n])
+    return PoolLayout(lens=np.asarray(lens, np.int32), offsets=offsets, total_rows=pos, gaps=gap_list)
+
+
+def decode_inputs(n_seq, Hq, Hkv, d, lens, *, seed, device="cpu", dtype=torch.bfloat16,
+                  max_gap=255, shuffle=True, poison=float("nan")):
+    """q [n_seq, Hq, d]; k_pool, v_pool [T, Hkv, d]; offsets int64; lens int32.
+
+    Rows of the pool that belong to no sequence are filled with ``poison`` so that a kernel
+    reading outside its sequence shows up as a non-finite output."""
+    layout = pool_layout(np.asarray(lens), seed, max_gap=max_gap, shuffle=shuffle)
+    g = make_generator(seed, device)
+    q = normal((n_seq, Hq, d), g, device, dtype)
+    k_pool = normal((layout.total_rows, Hkv, d), g, device, dtype)
+    v_pool = normal((layout.total_rows, Hkv, d), g, device, dtype)
+    for start, length in layout.gaps:
+        k_pool[start:start + length] = poison
+        v_pool[start:start + length] = poison
+    offsets = torch.from_numpy(layout.offsets).to(device)
+    lens_t = torch.from_numpy(layout.lens).to(device)
+    return q, k_pool, v_pool, offsets, lens_t, layout
+
+
+def decode_inputs_for(cfg: DecodeConfig, device="cpu"):
+    lens = decode_lens(cfg.n_seq, cfg.len_lo, cfg.len_hi, cfg.lens_seed)
+    return decode_inputs(cfg.n_seq, cfg.Hq, cfg.Hkv, cfg.d, lens, seed=cfg.value_seed, device=device,
+                         max_gap=cfg.max_gap)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact upcast of a float32 or bfloat16 tensor to a float64 numpy array."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
