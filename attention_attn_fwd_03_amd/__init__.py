@@ -1,0 +1,171 @@
+"""attnfwd: fused exact attention forward and pooled-KV decode for MI355X (gfx950).
+
+A thin ctypes binding over libattnfwd.so (include/attn.h).  Torch tensors supply device
+memory and the current stream; every step of the computation runs in the library's HIP
+kernels.  There is no fallback: without the built library or a GPU the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattnfwd.so")
+
+ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(6)
+
+EXPORTS = ["attn_fwd", "attn_fwd_f32", "attn_decode_workspace_size", "attn_decode", "attn_status_str",
+           "attn_fwd_plan", "attn_fwd_schedule", "attn_decode_plan"]
+
+
+class FwdPlanInfo(ctypes.Structure):
+    _fields_ = [("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32), ("threads", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32), ("num_q_tiles", ctypes.c_int32), ("heads_per_xcd", ctypes.c_int32),
+                ("num_workgroups", ctypes.c_int64), ("tiles_per_head", ctypes.c_int64),
+                ("masked_tiles_per_head", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libattnfwd.so (built in-tree by build.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run attention_attn_fwd_03_amd.build.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64, ctypes.c_size_t
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, vp]
+    L.attn_fwd.restype = i32
+    L.attn_fwd_f32.argtypes = L.attn_fwd.argtypes
+    L.attn_fwd_f32.restype = i32
+    L.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32]
+    L.attn_decode_workspace_size.restype = sz
+    L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, i32, f32, vp, sz, vp]
+    L.attn_decode.restype = i32
+    L.attn_status_str.argtypes = [i32]
+    L.attn_status_str.restype = ctypes.c_char_p
+    L.attn_fwd_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(FwdPlanInfo)]
+    L.attn_fwd_plan.restype = i32
+    L.attn_fwd_schedule.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, i64]
+    L.attn_fwd_schedule.restype = i32
+    L.attn_decode_plan.argtypes = [i32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    L.attn_decode_plan.restype = i32
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().attn_status_str(int(status)).decode()
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        raise RuntimeError(status_str(status))
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _require_gpu(*tensors):
+    import torch
+    for t in tensors:
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError("attnfwd works on GPU tensors only")
+        if not t.is_contiguous():
+            raise ValueError("attnfwd needs contiguous tensors")
+
+
+def attn_fwd(q, k, v, *, causal: bool = False, window: int = 0, scale: float | None = None,
+             return_lse: bool = False, out=None, lse_out=None):
+    """Exact attention forward.  q [B, Hq, Lq, d]; k, v [B, Hkv, Lk, d]; bf16 or fp32 (all alike).
+
+    Returns O [B, Hq, Lq, d] (same dtype), and LSE [B, Hq, Lq] fp32 (natural log) when
+    ``return_lse``.  ``scale`` defaults to 1/sqrt(d)."""
+    import torch
+    _require_gpu(q, k, v)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("expected 4-d tensors [B, H, L, d]")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q, k, v must all be bfloat16 or all float32")
+    B, Hq, Lq, d = q.shape
+    Bk, Hkv, Lk, dk = k.shape
+    if Bk != B or dk != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch between q, k and v")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    _require_gpu(o)
+    lse = None
+    if return_lse:
+        lse = torch.empty((B, Hq, Lq), device=q.device, dtype=torch.float32) if lse_out is None else lse_out
+    fn = lib().attn_fwd if q.dtype == torch.bfloat16 else lib().attn_fwd_f32
+    _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr() if lse is not None else None,
+              B, Hq, Hkv, Lq, Lk, d, int(bool(causal)), int(window), float(scale), _stream()))
+    return (o, lse) if return_lse else o
+
+
+def decode_workspace_size(n_seq: int, Hq: int, d: int, max_len: int) -> int:
+    return int(lib().attn_decode_workspace_size(n_seq, Hq, d, max_len))
+
+
+def attn_decode(q, k_pool, v_pool, offsets, lens, *, max_len: int, window: int = 0, scale: float | None = None,
+                return_lse: bool = False, workspace=None, out=None, lse_out=None):
+    """Decode one query token per sequence against a pooled KV cache.
+
+    q [N, Hq, d] bf16; k_pool, v_pool [T, Hkv, d] bf16; offsets int64 [N] (first pool row of
+    each sequence); lens int32 [N]; max_len >= max(lens).  Returns O [N, Hq, d] bf16 and,
+    when ``return_lse``, LSE [N, Hq] fp32."""
+    import torch
+    _require_gpu(q, k_pool, v_pool, offsets, lens)
+    if q.dtype != torch.bfloat16 or k_pool.dtype != torch.bfloat16 or v_pool.dtype != torch.bfloat16:
+        raise ValueError("decode takes bfloat16 q and pools")
+    if offsets.dtype != torch.int64 or lens.dtype != torch.int32:
+        raise ValueError("offsets must be int64 and lens int32")
+    N, Hq, d = q.shape
+    T, Hkv, dk = k_pool.shape
+    if dk != d or tuple(v_pool.shape) != tuple(k_pool.shape) or offsets.numel() != N or lens.numel() != N:
+        raise ValueError("shape mismatch between q, pools, offsets and lens")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = decode_workspace_size(N, Hq, d, max_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    o = torch.empty_like(q) if out is None else out
+    lse = None
+    if return_lse:
+        lse = torch.empty((N, Hq), device=q.device, dtype=torch.float32) if lse_out is None else lse_out
+    _check(lib().attn_decode(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), offsets.data_ptr(), lens.data_ptr(),
+                             o.data_ptr(), lse.data_ptr() if lse is not None else None, N, Hq, Hkv, d, T,
+                             int(max_len), int(window), float(scale), workspace.data_ptr(),
+                             workspace.numel() * workspace.element_size(), _stream()))
+    return (o, lse) if return_lse else o
+
+
+def fwd_plan(B, Hq, Hkv, Lq, Lk, d, causal=False, window=0, f32=False) -> dict:
+    info = FwdPlanInfo()
+    _check(lib().attn_fwd_plan(B, Hq, Hkv, Lq, Lk, d, int(bool(causal)), int(window), int(bool(f32)),
+                               ctypes.byref(info)))
+    return {name: getattr(info, name) for name, _ in FwdPlanInfo._fields_}
+
+
+def fwd_schedule(B, Hq, Hkv, Lq, Lk, d, causal=False, window=0, f32=False) -> np.ndarray:
+    """[num_workgroups, 3] array of (batch, query head, query tile) per workgroup index."""
+    n = fwd_plan(B, Hq, Hkv, Lq, Lk, d, causal, window, f32)["num_workgroups"]
+    out = np.zeros((n, 3), dtype=np.int32)
+    _check(lib().attn_fwd_schedule(B, Hq, Hkv, Lq, Lk, d, int(bool(causal)), int(window), int(bool(f32)),
+                                   out.ctypes.data, out.size))
+    return out
+
+
+def decode_plan(max_len: int) -> tuple[int, int]:
+    c, n = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().attn_decode_plan(int(max_len), ctypes.byref(c), ctypes.byref(n)))
+    return c.value, n.value

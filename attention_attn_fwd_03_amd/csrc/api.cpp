@@ -1,0 +1,200 @@
+// C ABI: argument validation, launch planning and kernel launches.  Nothing here touches the
+// device before every argument has been checked.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/attn.h"
+#include "kernels.hpp"
+#include "plan.hpp"
+
+using namespace attnfwd;
+
+namespace {
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int Hq,
+              int Hkv, int Lq, int Lk, int d, int causal, int window, float scale) {
+  if (!q || !k || !v || !o) return ATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || Lk <= 0 || d <= 0 || window < 0) return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (window > 0 && !causal) return ATTN_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
+  (void)lse;
+  // Element offsets are computed in size_t on the device, block indices in 32 bits.
+  const int64_t n_qt = (Lq + 127) / 128;
+  if ((int64_t)B * Hq * n_qt >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+FwdArgs make_fwd_args(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                      int Lq, int Lk, int d, int causal, int window, float scale, bool f32) {
+  (void)d;
+  FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Lq = Lq;
+  a.Lk = Lk;
+  a.group = Hq / Hkv;
+  a.causal = causal;
+  a.window = window;
+  a.c = std::fabs(scale) * kLog2eHost;
+  a.negate = scale < 0.f;
+  const int bq = prefill_block_q(f32);
+  a.n_qt = (Lq + bq - 1) / bq;
+  a.heads_per_xcd = prefill_heads_per_xcd(B, Hq);
+  return a;
+}
+
+int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Lq,
+               int Lk, int d, int causal, int window, float scale, void* stream, bool f32) {
+  const int st = check_fwd(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d, causal, window, scale);
+  if (st != ATTN_OK) return st;
+  const FwdArgs a = make_fwd_args(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d, causal, window, scale, f32);
+  const hipError_t e = launch_prefill(a, f32, d, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Lq,
+             int Lk, int d, int causal, int window, float scale, void* stream) {
+  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d, causal, window, scale, stream, false);
+}
+
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int Hq, int Hkv,
+                 int Lq, int Lk, int d, int causal, int window, float scale, void* stream) {
+  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d, causal, window, scale, stream, true);
+}
+
+size_t attn_decode_workspace_size(int n_seq, int Hq, int d, int max_len) {
+  if (n_seq <= 0 || Hq <= 0 || max_len < 1 || (d != 64 && d != 128)) return 0;
+  return decode_workspace_bytes(n_seq, Hq, d, max_len);
+}
+
+int attn_decode(const void* q, const void* k_pool, const void* v_pool, const int64_t* offsets,
+                const int32_t* lens, void* o, float* lse, int n_seq, int Hq, int Hkv, int d, int64_t pool_rows,
+                int max_len, int window, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_pool || !v_pool || !offsets || !lens || !o) return ATTN_ERR_NULL;
+  if (n_seq <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_len < 1 || window < 0 || pool_rows < 0)
+    return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
+  if (n_seq > 65535) return ATTN_ERR_SHAPE;
+  const int group = Hq / Hkv;
+  const int hblocks = (group + 31) / 32;
+  if ((int64_t)Hkv * hblocks > 65535) return ATTN_ERR_SHAPE;
+  const size_t need = decode_workspace_bytes(n_seq, Hq, d, max_len);
+  if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_ERR_UNSUPPORTED;
+
+  DecArgs a;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.offsets = offsets;
+  a.lens = lens;
+  a.o = o;
+  a.lse = lse;
+  a.ws = static_cast<float*>(workspace);
+  a.pool_rows = pool_rows;
+  a.n_seq = n_seq;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.group = group;
+  a.hblocks = hblocks;
+  a.max_len = max_len;
+  a.window = window;
+  a.n_chunks = decode_num_chunks(max_len);
+  a.c = std::fabs(scale) * kLog2eHost;
+  a.negate = scale < 0.f;
+  const hipError_t e = launch_decode(a, d, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+const char* attn_status_str(int status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_NULL: return "ATTN_ERR_NULL: a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "ATTN_ERR_SHAPE: invalid size (non-positive, Hq % Hkv != 0, or too large)";
+    case ATTN_ERR_UNSUPPORTED:
+      return "ATTN_ERR_UNSUPPORTED: unsupported head size, window without causal, non-finite scale or "
+             "misaligned pointer";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: decode workspace missing or too small";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP: kernel launch failed";
+    default: return "unknown attn status";
+  }
+}
+
+int attn_fwd_plan(int B, int Hq, int Hkv, int Lq, int Lk, int d, int causal, int window, int dtype_f32,
+                  attn_fwd_plan_info* out) {
+  static const int kDummy[4] = {0, 0, 0, 0};  // aligned stand-in pointers: validation only
+  const void* p = kDummy;
+  if (!out) return ATTN_ERR_NULL;
+  const int st = check_fwd(p, p, p, p, nullptr, B, Hq, Hkv, Lq, Lk, d, causal, window, 1.0f);
+  if (st != ATTN_OK) return st;
+  const bool f32 = dtype_f32 != 0;
+  const int bq = prefill_block_q(f32), bk = prefill_block_k(f32);
+  out->block_q = bq;
+  out->block_k = bk;
+  out->threads = prefill_threads(f32);
+  out->lds_bytes = prefill_lds_bytes(f32, d);
+  out->num_q_tiles = (Lq + bq - 1) / bq;
+  out->heads_per_xcd = prefill_heads_per_xcd(B, Hq);
+  out->num_workgroups = (int64_t)out->num_q_tiles * B * Hq;
+  int64_t tiles = 0, masked = 0;
+  for (int qt = 0; qt < out->num_q_tiles; ++qt) {
+    const KeyRange r = key_range(qt * bq, bq, Lq, Lk, bk, causal, window);
+    for (int kt = r.kt_lo; kt <= r.kt_hi; ++kt) {
+      ++tiles;
+      if (!tile_full(kt * bk, qt * bq, bq, Lq, Lk, bk, causal, window)) ++masked;
+    }
+  }
+  out->tiles_per_head = tiles;
+  out->masked_tiles_per_head = masked;
+  return ATTN_OK;
+}
+
+int attn_fwd_schedule(int B, int Hq, int Hkv, int Lq, int Lk, int d, int causal, int window, int dtype_f32,
+                      int32_t* out, int64_t out_len) {
+  attn_fwd_plan_info info;
+  const int st = attn_fwd_plan(B, Hq, Hkv, Lq, Lk, d, causal, window, dtype_f32, &info);
+  if (st != ATTN_OK) return st;
+  if (!out) return ATTN_ERR_NULL;
+  if (out_len < 3 * info.num_workgroups) return ATTN_ERR_SHAPE;
+  for (int64_t bid = 0; bid < info.num_workgroups; ++bid) {
+    const PrefillTile t =
+        prefill_tile((int)bid, B, Hq, Hq / Hkv, info.num_q_tiles, causal, info.heads_per_xcd);
+    out[3 * bid + 0] = t.b;
+    out[3 * bid + 1] = t.hq;
+    out[3 * bid + 2] = t.qt;
+  }
+  return ATTN_OK;
+}
+
+int attn_decode_plan(int max_len, int32_t* chunk_keys, int32_t* num_chunks) {
+  if (!chunk_keys || !num_chunks) return ATTN_ERR_NULL;
+  if (max_len < 1) return ATTN_ERR_SHAPE;
+  *chunk_keys = kDecodeChunk;
+  *num_chunks = decode_num_chunks(max_len);
+  return ATTN_OK;
+}
+
+}  // extern "C"

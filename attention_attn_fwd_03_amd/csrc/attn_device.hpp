@@ -1,0 +1,84 @@
+// Device-side building blocks shared by the prefill and decode kernels (gfx950 / CDNA4).
+//
+// Layout facts used throughout (checked on the hardware with a lane-layout probe):
+//  * v_mfma_f32_32x32x16_bf16: lane l supplies A[m = l%32][k = 8*(l/32) + e] and
+//    B[k = 8*(l/32) + e][n = l%32] for e = 0..7; it receives C[m][n = l%32] for
+//    m = 8*(i/4) + 4*(l/32) + i%4, i = 0..15.
+//  * v_mfma_f32_32x32x2_f32: lane l supplies A[l%32][l/32] and B[l/32][l%32]; same C layout.
+//  * ds_read_b64_tr_b16: inside each 16-lane group, lane i receives element i%4 of the 8-byte
+//    piece addressed by lane 4c + i/4, for c = 0..3.  If lane j of the group addresses row
+//    r0 + j/4, columns c0 + 4*(j%4) .. +3 of a row-major 16-bit matrix, lane i receives
+//    rows r0..r0+3 of column c0 + i: a column read, which is how V reaches the MFMA A operand.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attnfwd {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) unsigned short lds_u16;
+
+// log2(e): scores are kept in base 2 so that exp becomes one v_exp_f32.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// The reference maximum of a row is only raised when a new tile's maximum exceeds it by more
+// than this many binary orders; until then probabilities are computed against the stale
+// reference (they stay below 2^kRescaleSlack) and the accumulator is not rescaled.  The
+// final O = acc / l is unchanged because acc and l share the reference.
+constexpr float kRescaleSlack = 8.0f;
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_32x32x2(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Reductions over the lane pair (l, l ^ 32).  v_permlane32_swap with both operands = x hands
+// back {x[l], x[l - 32]} in lanes >= 32 and {x[l], x[l + 32]} in lanes < 32 (as the pair of
+// results in some order), so a symmetric reduction of the two results is the pair's value.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                            false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                            false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(unsigned, v);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(unsigned short b) {
+  return __builtin_bit_cast(float, ((unsigned)b) << 16);
+}
+
+// Transposed 4 x 16-bit read from LDS (see the header comment).
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_generic_ptr) {
+  const lds_i16x4* p = (const lds_i16x4*)(lds_u16*)lds_generic_ptr;
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_i16x4*>(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// Online-softmax state of one query row as held by one lane.  Lanes l and l ^ 32 hold the
+// same row and keep identical m; each keeps the partial sum over the keys it holds.
+struct RowState {
+  float m;   // reference maximum, base-2 scaled units (score * |scale| * log2 e); -inf at start
+  float l;   // this lane's partial sum of probabilities, relative to m
+};
+
+}  // namespace attnfwd

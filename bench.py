@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Throughput of the attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  * prefill: attn_fwd on the causal GQA workload (B=2, Hq=32, Hkv=8, L=4096, d=128, bf16,
+    LSE returned), and
+  * decode: attn_decode on the GQA decode batch (64 sequences, Hq=32, Hkv=8, d=128, KV lengths
+    uniform in [1024, 32768], one pooled K/V buffer with poisoned gaps).
+Inputs are generated on the device before timing.  The reported value is the prefill's useful
+TFLOP/s (4*d per visible (query, key) pair per query head); the decode's KV-read GB/s is
+reported beside it.  Kernel times come from HIP events recorded on the stream the kernels run
+on, over the timed steps.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+  python bench.py --suite        # one JSON line per workload (all five), for the tables
+  python bench.py --copy-calib   # a plain device copy of known size, to scale HBM counters
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk/CU)
+PEAK_F32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+# ---- work and byte counts (closed forms) ------------------------------------------------------
+
+def visible_pairs(Lq: int, Lk: int, causal: bool, window: int) -> int:
+    """Visible (query, key) pairs of one head: Lq*Lk without a mask; with causal masking (query
+    i at position i + Lk - Lq) each row sees min(p+1, Lk) keys, at most W of them with a window."""
+    total = 0
+    if not causal:
+        return Lq * Lk
+    delta = Lk - Lq
+    # rows whose position p = i + delta is < 0 see nothing
+    for_rows = range(max(0, -delta), Lq)
+    if window <= 0:
+        # sum over p of min(p + 1, Lk)
+        for i in for_rows:
+            total += min(i + delta + 1, Lk)
+        return total
+    for i in for_rows:
+        p = i + delta
+        total += min(p, Lk - 1) - max(0, p - window + 1) + 1
+    return total
+
+
+def prefill_flops(c) -> int:
+    return 4 * c.d * c.B * c.Hq * visible_pairs(c.Lq, c.Lk, c.causal, c.window)
+
+
+def prefill_bytes(c) -> int:
+    esz = 4 if c.dtype == "f32" else 2
+    return (2 * c.B * c.Hq * c.Lq * c.d + 2 * c.B * c.Hkv * c.Lk * c.d) * esz + 4 * c.B * c.Hq * c.Lq
+
+
+def decode_bytes(n_tokens: int, n_seq: int, Hq: int, Hkv: int, d: int) -> int:
+    """One read of every live K and V row, one read of q, one write of O (bf16) and LSE (fp32),
+    plus offsets and lens."""
+    return 2 * n_tokens * Hkv * d * 2 + 2 * n_seq * Hq * d * 2 + 4 * n_seq * Hq + 12 * n_seq
+
+
+def decode_flops(n_tokens: int, Hq: int, Hkv: int, d: int) -> int:
+    return 4 * d * n_tokens * Hq
+
+
+# ---- timing helpers ---------------------------------------------------------------------------
+
+def _events(n):
+    import torch
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def cpu_baseline(c, q, k, v):
+    """The oracle as it stands, on the host cores, over the whole prefill workload."""
+    import numpy as np
+    import oracle
+    import workloads as wl
+    qn, kn, vn = wl.to_f64(q), wl.to_f64(k), wl.to_f64(v)
+    t0 = time.perf_counter()
+    oracle.attention(qn, kn, vn, scale=c.scale, causal=c.causal, window=c.window)
+    dt = time.perf_counter() - t0
+    return {"value": prefill_flops(c) / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.host_cores(), "kind": "oracle",
+            "sample": f"all of {c.name} (B={c.B}, Hq={c.Hq}, Hkv={c.Hkv}, L={c.Lq}, d={c.d}, causal), fp64 numpy, "
+                      f"{dt:.1f} s wall", "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--suite", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="profile helper: run only one half of the step")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the attention kernels here run on a single device and this "
+              "build has no multi-GPU path (prefill shards by KV head with no communication; see the "
+              "design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_attn_fwd_03_amd as af
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    af.lib()  # fail loudly if the HIP library is missing
+    dev = "cuda"
+
+    if args.copy_calib:
+        n = 1 << 30
+        x = torch.empty(n, dtype=torch.uint8, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes_read": n, "copy_calib_bytes_written": n}), flush=True)
+        return
+
+    if args.suite:
+        return run_suite(args)
+
+    cp = wl.PREFILL["gqa_causal_bf16_L4096"]
+    cd = wl.DECODE["gqa_decode_bf16"]
+    q, k, v = wl.prefill_inputs_for(cp, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], device=dev, dtype=torch.float32)
+    lens = wl.decode_lens(cd.n_seq, cd.len_lo, cd.len_hi, cd.lens_seed)
+    qd, kp, vp, offs, lens_t, layout = wl.decode_inputs(cd.n_seq, cd.Hq, cd.Hkv, cd.d, lens, seed=cd.value_seed,
+                                                        device=dev, max_gap=cd.max_gap)
+    max_len = int(lens.max())
+    od = torch.empty_like(qd)
+    lsed = torch.empty((cd.n_seq, cd.Hq), device=dev, dtype=torch.float32)
+    ws = torch.empty(af.decode_workspace_size(cd.n_seq, cd.Hq, cd.d, max_len), device=dev, dtype=torch.uint8)
+    torch.cuda.synchronize()
+
+    do_pre = args.only in (None, "prefill")
+    do_dec = args.only in (None, "decode")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        if do_pre:
+            af.attn_fwd(q, k, v, causal=cp.causal, window=cp.window, scale=cp.scale, return_lse=True, out=o,
+                        lse_out=lse)
+        if ev is not None:
+            ev[1].record()
+        if do_dec:
+            af.attn_decode(qd, kp, vp, offs, lens_t, max_len=max_len, scale=cd.scale, return_lse=True,
+                           workspace=ws, out=od, lse_out=lsed)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [_events(3) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+        if (i + 1) % 10 == 0 or i + 1 == args.steps:
+            print(f"# step {i + 1}/{args.steps} enqueued", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    pre_avg = sum(pre_ms) / len(pre_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    n_tok = int(lens.sum())
+    pflops = prefill_flops(cp)
+    dbytes = decode_bytes(n_tok, cd.n_seq, cd.Hq, cd.Hkv, cd.d)
+    pre_tflops = pflops / (pre_avg * 1e-3) / 1e12 if do_pre else 0.0
+    dec_gbs = dbytes / (dec_avg * 1e-3) / 1e9 if do_dec else 0.0
+
+    line = {
+        "metric": "prefill attn TFLOP/s (% MFMA peak) + decode KV-read GB/s (% HBM peak), 1 GPU",
+        "value": round(pre_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) q/k/v (bf16), decode pool with seeded lengths and NaN gaps",
+        "config": {
+            "workload": "prefill gqa_causal_bf16_L4096 + decode gqa_decode_bf16",
+            "prefill": {"B": cp.B, "Hq": cp.Hq, "Hkv": cp.Hkv, "L": cp.Lq, "d": cp.d, "causal": cp.causal,
+                        "window": cp.window, "lse": True, "useful_gflop": round(pflops / 1e9, 3),
+                        "kernel_ms": round(pre_avg, 4), "kernel_ms_min": round(min(pre_ms), 4)},
+            "decode": {"n_seq": cd.n_seq, "Hq": cd.Hq, "Hkv": cd.Hkv, "d": cd.d, "kv_tokens": n_tok,
+                       "max_len": max_len, "algorithmic_gb": round(dbytes / 1e9, 4),
+                       "kernels_ms": round(dec_avg, 4), "kernels_ms_min": round(min(dec_ms), 4),
+                       "GB/s": round(dec_gbs, 1), "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4)},
+            "parallelism": "single GPU",
+        },
+        "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "fwd_bf16_kernel<128,64>",
+                     "per_launch": f"{pflops / 1e9:.1f} GFLOP useful (4*d per visible pair, 64 heads)"},
+        "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                            "kernels": "decode_split_kernel<128> + decode_merge_kernel<128>",
+                            "per_launch": f"{dbytes / 1e9:.3f} GB (one read of live K/V rows + q, O, LSE)"},
+    }
+    if not args.no_cpu_baseline and do_pre:
+        print("# timing the oracle on the host", file=sys.stderr, flush=True)
+        cb = cpu_baseline(cp, q.cpu(), k.cpu(), v.cpu())
+        line["cpu_baseline"] = {kk: cb[kk] for kk in ("value", "unit", "cores", "kind", "sample")}
+    print(json.dumps(line), flush=True)
+
+
+def run_suite(args):
+    """One JSON line per workload: median kernel time over timed calls, TFLOP/s or GB/s."""
+    import torch
+    import attention_attn_fwd_03_amd as af
+    import workloads as wl
+    dev = "cuda"
+    reps, warm = max(args.steps, 10), max(args.warmup, 3)
+
+    def timeit(fn):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        ev = [_events(2) for _ in range(reps)]
+        for e in ev:
+            e[0].record()
+            fn()
+            e[1].record()
+        torch.cuda.synchronize()
+        ts = sorted(e[0].elapsed_time(e[1]) for e in ev)
+        return ts[len(ts) // 2], ts[0]
+
+    for name, c in wl.PREFILL.items():
+        q, k, v = wl.prefill_inputs_for(c, device=dev)
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], device=dev, dtype=torch.float32)
+        med, mn = timeit(lambda: af.attn_fwd(q, k, v, causal=c.causal, window=c.window, scale=c.scale,
+                                             return_lse=True, out=o, lse_out=lse))
+        fl = prefill_flops(c)
+        peak = PEAK_F32_MFMA_TFLOPS if c.dtype == "f32" else PEAK_BF16_TFLOPS
+        tf = fl / (med * 1e-3) / 1e12
+        print(json.dumps({"workload": name, "kind": "prefill", "dtype": c.dtype, "median_ms": round(med, 4),
+                          "min_ms": round(mn, 4), "useful_gflop": round(fl / 1e9, 4), "TFLOP/s": round(tf, 2),
+                          "frac_mfma_peak": round(tf / peak, 4), "peak_TFLOP/s": peak,
+                          "GB/s_algorithmic": round(prefill_bytes(c) / (med * 1e-3) / 1e9, 1)}), flush=True)
+        del q, k, v, o, lse
+    for name, c in wl.DECODE.items():
+        lens = wl.decode_lens(c.n_seq, c.len_lo, c.len_hi, c.lens_seed)
+        max_len = int(lens.max())
+        # Several replicas of the pool are rotated so that the 256 MB last-level cache cannot hold the
+        # working set between calls.
+        pool_bytes = 2 * (int(lens.sum()) + 256 * 65) * c.Hkv * c.d * 2
+        n_rep = max(1, min(8, math.ceil(2.0e9 / pool_bytes)))
+        reps_data = []
+        for r in range(n_rep):
+            qd, kp, vp, offs, lens_t, layout = wl.decode_inputs(c.n_seq, c.Hq, c.Hkv, c.d, lens,
+                                                                seed=c.value_seed + 100 * r, device=dev,
+                                                                max_gap=c.max_gap)
+            reps_data.append((qd, kp, vp, offs, lens_t))
+        od = torch.empty_like(reps_data[0][0])
+        lsed = torch.empty((c.n_seq, c.Hq), device=dev, dtype=torch.float32)
+        ws = torch.empty(af.decode_workspace_size(c.n_seq, c.Hq, c.d, max_len), device=dev, dtype=torch.uint8)
+        it = [0]
+
+        def call():
+            qd, kp, vp, offs, lens_t = reps_data[it[0] % n_rep]
+            it[0] += 1
+            af.attn_decode(qd, kp, vp, offs, lens_t, max_len=max_len, scale=c.scale, return_lse=True,
+                           workspace=ws, out=od, lse_out=lsed)
+        med, mn = timeit(call)
+        n_tok = int(lens.sum())
+        by = decode_bytes(n_tok, c.n_seq, c.Hq, c.Hkv, c.d)
+        gbs = by / (med * 1e-3) / 1e9
+        print(json.dumps({"workload": name, "kind": "decode", "dtype": "bf16", "median_ms": round(med, 4),
+                          "min_ms": round(mn, 4), "kv_tokens": n_tok, "pool_replicas": n_rep,
+                          "algorithmic_gb": round(by / 1e9, 4), "GB/s": round(gbs, 1),
+                          "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                          "useful_gflop": round(decode_flops(n_tok, c.Hq, c.Hkv, c.d) / 1e9, 3)}), flush=True)
+        del reps_data
+
+
+if __name__ == "__main__":
+    main()

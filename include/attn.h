@@ -1,0 +1,119 @@
+/* attnfwd — fused exact attention forward and pooled-KV decode for AMD MI355X (gfx950).
+ *
+ * Computes O = softmax(scale * Q K^T + mask) V and the row log-sum-exp without writing the
+ * score matrix to memory.  The operation is the plain scaled dot-product attention of
+ * "003-注意力机制详解：从基础Attention到DeepSeek的优化策略" (§一), evaluated with the tiled
+ * online softmax of its §二, with:
+ *   - GQA / MQA: query head h reads KV head h / (Hq / Hkv), i.e. consecutive query heads share
+ *     a KV head, as repeat_kv expands them in "LLM中的Attention实现及优化" — without copying;
+ *     Hq must be a multiple of Hkv (the tqpw.cn MQA/GQA article, §3.1, asserts h % g == 0);
+ *   - causal masking ("注意力机制深度优化", §一.2), aligned bottom-right when Lq != Lk: query row
+ *     i sits at position i + (Lk - Lq) and sees keys j <= i + (Lk - Lq);
+ *   - a sliding window of W ("LLM中的Attention实现及优化": each token sees at most the previous
+ *     W tokens), read as the W most recent positions counting the query's own;
+ *   - decode against a KV cache pool shared by many sequences and addressed by offsets
+ *     ("003-注意力机制详解…", §三.3).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller, 16-byte aligned, row-major
+ *     and contiguous.  The library allocates nothing, frees nothing and keeps no state besides
+ *     read-only kernel code.  Inputs are not modified; outputs must not alias inputs.
+ *   - Calls enqueue work on `stream` (a hipStream_t; NULL = the default stream) and return
+ *     without synchronising.  Argument errors are detected on the host, before any device work,
+ *     and returned as a status.  Device faults surface at the caller's next synchronisation.
+ *   - scale is explicit (1/sqrt(d) is the usual choice); any finite value, including 0 and
+ *     negative values, is accepted.
+ *   - A query row that sees no key gets O = 0 and LSE = -inf.  NaN/Inf inputs propagate.
+ *   - Head dimension d must be 64 or 128.
+ */
+#ifndef ATTNFWD_ATTN_H
+#define ATTNFWD_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,       /* a size <= 0 (n_seq may not be 0 either), Hq % Hkv != 0, window < 0,
+                               max_len < 1, pool_rows < 0, or a size too large to index */
+  ATTN_ERR_UNSUPPORTED = 3, /* d not in {64, 128}; window > 0 without causal; scale not finite;
+                               a pointer not 16-byte aligned */
+  ATTN_ERR_WORKSPACE = 4,   /* decode workspace NULL or smaller than attn_decode_workspace_size */
+  ATTN_ERR_HIP = 5          /* the HIP runtime refused a launch */
+} attn_status;
+
+/* Prefill / full attention, bfloat16 tensors (uint16 storage, round-to-nearest-even results).
+ *   q [B, Hq, Lq, d], k and v [B, Hkv, Lk, d], o [B, Hq, Lq, d]  (bf16)
+ *   lse [B, Hq, Lq] fp32, natural log; may be NULL (not written).
+ *   causal: 0 or 1.  window: 0 = none, W > 0 keeps keys p - W < j <= p (requires causal).
+ * Scores and the softmax are fp32; probabilities are rounded to bf16 for the P.V product,
+ * which accumulates in fp32 ("003-注意力机制详解…", §三.1 mixed precision). */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int Lq, int Lk, int d,
+             int causal, int window, float scale, void* stream);
+
+/* Same as attn_fwd with fp32 tensors throughout (q, k, v, o are float*). */
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                 int B, int Hq, int Hkv, int Lq, int Lk, int d,
+                 int causal, int window, float scale, void* stream);
+
+/* Bytes of device workspace attn_decode needs for these sizes (0 if a size is invalid). */
+size_t attn_decode_workspace_size(int n_seq, int Hq, int d, int max_len);
+
+/* Decode: one new query token per sequence against its cached keys and values.
+ *   q, o [n_seq, Hq, d] bf16;  k_pool, v_pool [pool_rows, Hkv, d] bf16.
+ *   offsets[n_seq] int64: pool row of each sequence's first token (any order, gaps allowed).
+ *   lens[n_seq] int32: cached tokens of each sequence, 0 <= lens[s] <= max_len, counting the
+ *   query token itself (its K/V are the last row).  The query sees all lens[s] keys, or only
+ *   the last `window` of them when window > 0.
+ *   lse [n_seq, Hq] fp32, natural log; may be NULL.
+ *   workspace: caller-owned device memory of at least attn_decode_workspace_size(...) bytes,
+ *   fully rewritten by each call; calls that share a workspace must not overlap in time.
+ * offsets and lens live in device memory and are checked on the device: a sequence with
+ * lens < 0, lens > max_len, offsets < 0 or offsets + lens > pool_rows is not read, and its
+ * outputs (o rows and lse) are set to NaN. */
+int attn_decode(const void* q, const void* k_pool, const void* v_pool,
+                const int64_t* offsets, const int32_t* lens, void* o, float* lse,
+                int n_seq, int Hq, int Hkv, int d, int64_t pool_rows, int max_len, int window,
+                float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* attn_status_str(int status);
+
+/* ---- planner introspection (host only, no device work; used by tests and tooling) ---- */
+
+typedef struct {
+  int32_t block_q;            /* query rows per workgroup */
+  int32_t block_k;            /* keys per K/V tile */
+  int32_t threads;            /* threads per workgroup */
+  int32_t lds_bytes;          /* LDS per workgroup */
+  int32_t num_q_tiles;        /* ceil(Lq / block_q) */
+  int32_t heads_per_xcd;      /* > 0 when blocks are banded by XCD */
+  int64_t num_workgroups;     /* grid size */
+  int64_t tiles_per_head;     /* K/V tiles visited, summed over the query tiles of one head */
+  int64_t masked_tiles_per_head; /* of which straddle a mask boundary */
+} attn_fwd_plan_info;
+
+/* Fill *out with the launch plan attn_fwd (dtype_f32 = 0) or attn_fwd_f32 (dtype_f32 = 1)
+ * would use.  Returns the same status the call itself would return for these sizes. */
+int attn_fwd_plan(int B, int Hq, int Hkv, int Lq, int Lk, int d, int causal, int window,
+                  int dtype_f32, attn_fwd_plan_info* out);
+
+/* Write, for every workgroup index bid < num_workgroups, the (batch, query head, query tile)
+ * it computes: out[3*bid + 0..2].  `out` is host memory of 3 * num_workgroups int32. */
+int attn_fwd_schedule(int B, int Hq, int Hkv, int Lq, int Lk, int d, int causal, int window,
+                      int dtype_f32, int32_t* out, int64_t out_len);
+
+/* Keys per decode chunk and number of chunks for max_len. */
+int attn_decode_plan(int max_len, int32_t* chunk_keys, int32_t* num_chunks);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTNFWD_ATTN_H */

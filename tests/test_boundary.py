@@ -1,0 +1,189 @@
+"""C-ABI boundary on the host: the library loads, exports what include/attn.h declares, rejects
+bad arguments before touching the device, and plans tiles exactly as the mask requires.
+No compute call is made here (no GPU needed)."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import attention_attn_fwd_03_amd as af
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+# Fake, 16-byte aligned "device" addresses: never dereferenced, because every call below is
+# rejected by host-side validation first.
+P = 0x10000
+MISALIGNED = 0x10008
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_loads_and_exports_header_symbols():
+    L = af.lib()
+    names = declared_functions()
+    assert set(names) == set(af.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for s in range(6):
+        assert af.status_str(s).startswith("ATTN_")
+    assert "unknown" in af.status_str(99)
+
+
+def fwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, Hq=4, Hkv=2, Lq=64, Lk=64, d=128, causal=1, window=0,
+             scale=0.125, stream=None)
+    a.update(kw)
+    return af.lib().attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Lq"], a["Lk"],
+                             a["d"], a["causal"], a["window"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), af.ATTN_ERR_NULL), (dict(k=None), af.ATTN_ERR_NULL), (dict(v=None), af.ATTN_ERR_NULL),
+    (dict(o=None), af.ATTN_ERR_NULL),
+    (dict(B=0), af.ATTN_ERR_SHAPE), (dict(Hq=-1), af.ATTN_ERR_SHAPE), (dict(Lq=0), af.ATTN_ERR_SHAPE),
+    (dict(Lk=0), af.ATTN_ERR_SHAPE), (dict(Hq=6, Hkv=4), af.ATTN_ERR_SHAPE), (dict(window=-1), af.ATTN_ERR_SHAPE),
+    (dict(causal=2), af.ATTN_ERR_SHAPE), (dict(B=1 << 20, Hq=1 << 10, Hkv=1 << 10, Lq=1 << 10), af.ATTN_ERR_SHAPE),
+    (dict(d=96), af.ATTN_ERR_UNSUPPORTED), (dict(d=256), af.ATTN_ERR_UNSUPPORTED),
+    (dict(causal=0, window=16), af.ATTN_ERR_UNSUPPORTED),
+    (dict(scale=math.inf), af.ATTN_ERR_UNSUPPORTED), (dict(scale=math.nan), af.ATTN_ERR_UNSUPPORTED),
+    (dict(q=MISALIGNED), af.ATTN_ERR_UNSUPPORTED), (dict(o=MISALIGNED), af.ATTN_ERR_UNSUPPORTED),
+])
+def test_fwd_rejects_bad_arguments(kw, status):
+    assert fwd(**kw) == status
+    # the fp32 entry point validates identically
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, Hq=4, Hkv=2, Lq=64, Lk=64, d=128, causal=1, window=0, scale=0.125)
+    a.update(kw)
+    assert af.lib().attn_fwd_f32(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Lq"],
+                                 a["Lk"], a["d"], a["causal"], a["window"], a["scale"], None) == status
+
+
+def dec(**kw):
+    a = dict(q=P, kp=P, vp=P, offs=P, lens=P, o=P, lse=None, N=4, Hq=8, Hkv=2, d=128, T=1000, max_len=100, window=0,
+             scale=0.1, ws=P, ws_bytes=1 << 30)
+    a.update(kw)
+    return af.lib().attn_decode(a["q"], a["kp"], a["vp"], a["offs"], a["lens"], a["o"], a["lse"], a["N"], a["Hq"],
+                                a["Hkv"], a["d"], a["T"], a["max_len"], a["window"], a["scale"], a["ws"],
+                                a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), af.ATTN_ERR_NULL), (dict(kp=None), af.ATTN_ERR_NULL), (dict(vp=None), af.ATTN_ERR_NULL),
+    (dict(offs=None), af.ATTN_ERR_NULL), (dict(lens=None), af.ATTN_ERR_NULL), (dict(o=None), af.ATTN_ERR_NULL),
+    (dict(N=0), af.ATTN_ERR_SHAPE), (dict(Hq=0), af.ATTN_ERR_SHAPE), (dict(Hq=8, Hkv=3), af.ATTN_ERR_SHAPE),
+    (dict(max_len=0), af.ATTN_ERR_SHAPE), (dict(window=-2), af.ATTN_ERR_SHAPE), (dict(T=-1), af.ATTN_ERR_SHAPE),
+    (dict(N=70000), af.ATTN_ERR_SHAPE),
+    (dict(d=32), af.ATTN_ERR_UNSUPPORTED), (dict(scale=-math.inf), af.ATTN_ERR_UNSUPPORTED),
+    (dict(kp=MISALIGNED), af.ATTN_ERR_UNSUPPORTED),
+    (dict(ws=None), af.ATTN_ERR_WORKSPACE), (dict(ws_bytes=16), af.ATTN_ERR_WORKSPACE),
+])
+def test_decode_rejects_bad_arguments(kw, status):
+    assert dec(**kw) == status
+
+
+def test_decode_workspace_size():
+    chunk, n = af.decode_plan(32768)
+    assert n == math.ceil(32768 / chunk)
+    assert af.decode_workspace_size(64, 32, 128, 32768) == 64 * 32 * n * (128 + 2) * 4
+    assert af.decode_workspace_size(3, 5, 64, 1) == 3 * 5 * 1 * 66 * 4
+    assert af.decode_workspace_size(0, 32, 128, 10) == 0
+    assert af.decode_workspace_size(4, 32, 96, 10) == 0
+    with pytest.raises(RuntimeError):
+        af.decode_plan(0)
+
+
+# --------------------------------------------------------------------------------------------
+# Tile planning against a brute-force view of the mask.
+
+def brute_tiles(Lq, Lk, causal, window, bq, bk):
+    """Per query tile: the K tiles holding at least one visible pair, and of those, the ones
+    not fully visible for every valid row (or cut by the end of the keys)."""
+    p = np.arange(Lq)[:, None] + (Lk - Lq)
+    j = np.arange(Lk)[None, :]
+    vis = np.ones((Lq, Lk), bool)
+    if causal:
+        vis &= j <= p
+    if window:
+        vis &= j > p - window
+    visited, masked = 0, 0
+    for qs in range(0, Lq, bq):
+        rows = vis[qs:qs + bq]
+        kts = [kt for kt in range(math.ceil(Lk / bk)) if rows[:, kt * bk:(kt + 1) * bk].any()]
+        if kts:
+            assert kts == list(range(kts[0], kts[-1] + 1))  # the band is contiguous
+        visited += len(kts)
+        for kt in kts:
+            blk = rows[:, kt * bk:(kt + 1) * bk]
+            if blk.shape[1] < bk or not blk.all():
+                masked += 1
+    return visited, masked
+
+
+PLAN_CASES = [
+    (128, 128, False, 0), (128, 128, True, 0), (1000, 1000, True, 0), (4097, 4097, True, 0),
+    (4096, 4096, True, 0), (1, 1, True, 0), (65, 200, True, 0), (300, 70, True, 0), (300, 70, False, 0),
+    (2000, 2000, True, 1), (2000, 2000, True, 63), (2000, 2000, True, 129), (2000, 2000, True, 2000),
+    (2000, 2000, True, 5000), (777, 1500, True, 300), (16384, 16384, True, 4096), (1024, 1024, False, 0),
+]
+
+
+@pytest.mark.parametrize("f32", [False, True])
+@pytest.mark.parametrize("Lq,Lk,causal,window", PLAN_CASES)
+def test_plan_visits_exactly_the_visible_band(Lq, Lk, causal, window, f32):
+    info = af.fwd_plan(1, 8, 2, Lq, Lk, 128, causal, window, f32)
+    visited, masked = brute_tiles(Lq, Lk, causal, window, info["block_q"], info["block_k"])
+    assert info["tiles_per_head"] == visited
+    assert info["masked_tiles_per_head"] == masked
+    assert info["num_q_tiles"] == math.ceil(Lq / info["block_q"])
+
+
+def test_plan_skips_the_causal_upper_triangle():
+    """Causal L=4096: about half of the dense tiles are never visited ("注意力机制深度优化"
+    §一.2 claims the skip saves work; here the saving is exact)."""
+    info = af.fwd_plan(2, 32, 8, 4096, 4096, 128, True, 0)
+    dense = info["num_q_tiles"] * math.ceil(4096 / info["block_k"])
+    assert info["tiles_per_head"] == sum(2 * (i + 1) for i in range(32))  # BQ = 2 BK
+    assert info["tiles_per_head"] / dense < 0.52
+    # with the 4k window at 16k only the band around the diagonal is visited
+    info = af.fwd_plan(1, 32, 8, 16384, 16384, 128, True, 4096)
+    assert info["tiles_per_head"] <= 128 * (4096 // 64 + 3)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,L,causal", [(2, 32, 8, 4096, True), (4, 16, 16, 1024, False),
+                                                (1, 2, 2, 128, True), (3, 5, 1, 300, True), (1, 32, 8, 16384, True)])
+def test_schedule_is_a_bijection(B, Hq, Hkv, L, causal):
+    sched = af.fwd_schedule(B, Hq, Hkv, L, L, 128, causal)
+    info = af.fwd_plan(B, Hq, Hkv, L, L, 128, causal)
+    n_qt = info["num_q_tiles"]
+    assert len(sched) == B * Hq * n_qt
+    seen = {tuple(r) for r in sched}
+    assert len(seen) == len(sched)
+    assert all(0 <= b < B and 0 <= h < Hq and 0 <= t < n_qt for b, h, t in seen)
+    if causal:  # heaviest query tiles are dispatched first: the tile index never increases
+        assert np.all(np.diff(sched[:, 2]) <= 0) or info["heads_per_xcd"]
+        for x in range(8 if info["heads_per_xcd"] else 1):
+            part = sched[x::8] if info["heads_per_xcd"] else sched
+            assert np.all(np.diff(part[:, 2]) <= 0)
+
+
+def test_schedule_bands_heads_by_xcd():
+    """Blocks bid with equal bid % 8 (one XCD) cover a contiguous band of B*Hq/8 heads, so the
+    query heads sharing a KV head stay on one L2."""
+    B, Hq, Hkv, L = 2, 32, 8, 4096
+    sched = af.fwd_schedule(B, Hq, Hkv, L, L, 128, True)
+    band = B * Hq // 8
+    for x in range(8):
+        heads = {int(b) * Hq + int(h) for b, h, _ in sched[x::8]}
+        assert heads == set(range(x * band, (x + 1) * band))
+        kv = {(bh // Hq, (bh % Hq) // (Hq // Hkv)) for bh in heads}
+        assert len(kv) == band // (Hq // Hkv)
