@@ -44,8 +44,20 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+    check_loadable(tmp)
     os.replace(tmp, LIB)
     return LIB
+
+
+def check_loadable(path: str) -> None:
+    """Refuse a library with unresolved symbols (e.g. a kernel whose host launch stub was not
+    emitted): load it with every symbol bound now, as the GPU machine would at first use."""
+    import ctypes
+    try:
+        ctypes.CDLL(path, mode=os.RTLD_NOW | os.RTLD_LOCAL)
+    except OSError as e:
+        os.unlink(path)
+        raise RuntimeError(f"built library does not load: {e}") from None
 
 
 if __name__ == "__main__":

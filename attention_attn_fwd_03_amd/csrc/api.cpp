@@ -15,6 +15,18 @@ namespace {
 
 constexpr float kLog2eHost = 1.4426950408889634f;
 
+// The kernels scale scores by c = |scale| * log2(e) > 0.  A negative scale flips the sign of Q
+// (exact); a zero scale zeroes Q and uses c = 1, which gives the same all-zero scores.
+void set_scale(float scale, float& c, int& qmode) {
+  if (scale == 0.f) {
+    c = 1.f;
+    qmode = 2;
+  } else {
+    c = std::fabs(scale) * kLog2eHost;
+    qmode = scale < 0.f ? 1 : 0;
+  }
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int Hq,
@@ -51,8 +63,7 @@ FwdArgs make_fwd_args(const void* q, const void* k, const void* v, void* o, floa
   a.group = Hq / Hkv;
   a.causal = causal;
   a.window = window;
-  a.c = std::fabs(scale) * kLog2eHost;
-  a.negate = scale < 0.f;
+  set_scale(scale, a.c, a.qmode);
   const int bq = prefill_block_q(f32);
   a.n_qt = (Lq + bq - 1) / bq;
   a.heads_per_xcd = prefill_heads_per_xcd(B, Hq);
@@ -123,8 +134,7 @@ int attn_decode(const void* q, const void* k_pool, const void* v_pool, const int
   a.max_len = max_len;
   a.window = window;
   a.n_chunks = decode_num_chunks(max_len);
-  a.c = std::fabs(scale) * kLog2eHost;
-  a.negate = scale < 0.f;
+  set_scale(scale, a.c, a.qmode);
   const hipError_t e = launch_decode(a, d, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }

@@ -81,4 +81,92 @@ struct RowState {
   float l;   // this lane's partial sum of probabilities, relative to m
 };
 
+// The online softmax of one tile ("003-注意力机制详解…", §二: new row max, running sum and
+// accumulator rescaled by exp(old max - new max), exponentials of the tile, row sums), split so
+// that the rarely taken rescale branch comes first and the exponentials form straight-line code
+// that the scheduler can interleave with MFMA work of the next tile.
+//
+// A tile is NB 32-key blocks in the S^T accumulator layout: lane value i of block kb is key
+// kbase + 32*kb + 8*(i/4) + (i%4), where kbase = tile start + 4*(lane/32).  Scores are scaled
+// here, in fp32, by c = |scale| * log2(e).
+
+// Edge tiles: keys outside [kbase + lo, kbase + hi] become -inf.
+template <int NB>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[NB], int lo, int hi) {
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int ci = kb * 32 + (i >> 2) * 8 + (i & 3);
+      const bool vis = (ci >= lo) & (ci <= hi);
+      s[kb][i] = vis ? s[kb][i] : -INFINITY;
+    }
+}
+
+// Row maximum of the tile; raises the reference maximum (rescaling the running sum and the
+// accumulator) only when the tile's maximum exceeds it by more than kRescaleSlack.  Returns
+// the reference to subtract, with the -inf guard of a row that has seen no key yet.
+template <int NB, int ND>
+__device__ __forceinline__ float update_max(const f32x16 (&s)[NB], RowState& st, f32x16 (&o)[ND], float c) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+  mx = pair_max(mx);
+  const float tmax = (mx == -INFINITY) ? -INFINITY : mx * c;
+  const bool need = tmax > st.m + kRescaleSlack;
+  if (wave_any(need)) {
+    const float m_new = need ? tmax : st.m;
+    const float alpha = need ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.f;
+    st.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) o[dt] *= alpha;
+    st.m = m_new;
+  }
+  return (st.m == -INFINITY) ? 0.f : st.m;
+}
+
+// Probabilities p = exp2(s * c - mb) of a 32-key block, added to the running sum in fp32 and
+// returned packed as bf16 pairs (round to nearest even) in the order of the P.V B operand.
+// Masked keys hold s = -inf and c > 0, so they give exp2(-inf) = 0 without a select (a zero
+// scale is run as Q = 0 with c = 1, which yields the same all-zero scores).
+__device__ __forceinline__ void exp_block(const f32x16& s, float c, float mb, RowState& st, unsigned (&pk)[8]) {
+  float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    const float e0 = __builtin_amdgcn_exp2f(fmaf(s[i], c, -mb));
+    const float e1 = __builtin_amdgcn_exp2f(fmaf(s[i + 1], c, -mb));
+    l0 += e0;
+    l1 += e1;
+    pk[i >> 1] = pack_bf16x2(e0, e1);
+  }
+  st.l += l0 + l1;
+}
+
+// fp32 variant for the fp32 path (P stays fp32).
+__device__ __forceinline__ void exp_block_f32(const f32x16& s, float c, float mb, RowState& st, float (&p)[16]) {
+  float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    const float e0 = __builtin_amdgcn_exp2f(fmaf(s[i], c, -mb));
+    const float e1 = __builtin_amdgcn_exp2f(fmaf(s[i + 1], c, -mb));
+    l0 += e0;
+    l1 += e1;
+    p[i] = e0;
+    p[i + 1] = e1;
+  }
+  st.l += l0 + l1;
+}
+
+// How Q enters the kernels: as given, with its sign flipped (negative scale, run as |scale|), or
+// as zeros (scale = 0, run with c = 1).  All three are exact.
+enum QMode : int { kQAsIs = 0, kQNegate = 1, kQZero = 2 };
+
+// Q fragment word with the mode applied.
+__device__ __forceinline__ u32x4 q_word(u32x4 w, int qmode) {
+  if (qmode == kQZero) return u32x4{0u, 0u, 0u, 0u};
+  return qmode == kQNegate ? (w ^ 0x80008000u) : w;
+}
+
 }  // namespace attnfwd

@@ -50,12 +50,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecArgs a) {
   bf16x8 qf[D / 16];
   {
     const unsigned short* Qg = (const unsigned short*)a.q + ((size_t)s * a.Hq + h0 + col) * D;
-    const unsigned flip = a.negate ? 0x80008000u : 0u;
     for (int ks = 0; ks < D / 16; ++ks) {
       u32x4 w = {0u, 0u, 0u, 0u};
       if (col < nh) w = *(const u32x4*)(Qg + ks * 16 + h * 8);
-      w ^= flip;
-      qf[ks] = __builtin_bit_cast(bf16x8, w);
+      qf[ks] = __builtin_bit_cast(bf16x8, q_word(w, a.qmode));
     }
   }
 
@@ -117,40 +115,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecArgs a) {
     for (int i = 0; i < 16; ++i) sv[i] = 0.f;
     for (int ks = 0; ks < D / 16; ++ks) sv = mfma_32x32x16(__builtin_bit_cast(bf16x8, kc[ks]), qf[ks], sv);
 
-    const bool edge = kb0 + BKD > end;
-    if (edge) {
-      for (int i = 0; i < 16; ++i) {
-        const int key = kb0 + (i >> 2) * 8 + h * 4 + (i & 3);
-        if (key >= end) sv[i] = -INFINITY;
-      }
-    }
-    float mx = -INFINITY;
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[i]);
-    mx = pair_max(mx);
-    const float tmax = (mx == -INFINITY) ? -INFINITY : mx * c;
-    const bool need = tmax > st.m + kRescaleSlack;
-    if (wave_any(need)) {
-      const float m_new = need ? tmax : st.m;
-      const float alpha = need ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.f;
-      st.l *= alpha;
-      for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-      st.m = m_new;
-    }
-    const float mb = (st.m == -INFINITY) ? 0.f : st.m;
+    f32x16 sa[1] = {sv};
+    const bool full = kb0 + BKD <= end;
+    if (!full) mask_tile(sa, -(1 << 30), end - 1 - (kb0 + 4 * h));  // keys at or past `end`
+    const float mb = update_max(sa, st, o, c);
     unsigned pk[8];
-    float lsum = 0.f;
-    for (int pi = 0; pi < 8; ++pi) {
-      const float s0 = sv[2 * pi], s1 = sv[2 * pi + 1];
-      float p0 = __builtin_amdgcn_exp2f(fmaf(s0, c, -mb));
-      float p1 = __builtin_amdgcn_exp2f(fmaf(s1, c, -mb));
-      if (edge) {
-        p0 = (s0 == -INFINITY) ? 0.f : p0;
-        p1 = (s1 == -INFINITY) ? 0.f : p1;
-      }
-      pk[pi] = pack_bf16x2(p0, p1);
-      lsum += p0 + p1;
-    }
-    st.l += lsum;
+    exp_block(sa[0], c, mb, st, pk);
     for (int j = 0; j < 2; ++j) {
       const u32x4 pw = {pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]};
       const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);

@@ -14,8 +14,8 @@ struct FwdArgs {
   int B, Hq, Hkv, Lq, Lk;
   int group;          // Hq / Hkv
   int causal, window;
-  float c;            // |scale| * log2(e)
-  int negate;         // scale < 0: Q's sign is flipped in registers so that c stays >= 0
+  float c;            // |scale| * log2(e), or 1 when scale = 0
+  int qmode;          // kQAsIs, kQNegate (scale < 0) or kQZero (scale = 0): c is always > 0
   int n_qt;           // query tiles per head
   int heads_per_xcd;  // > 0: XCD-banded block order (see plan.hpp)
 };
@@ -32,7 +32,7 @@ struct DecArgs {
   int64_t pool_rows;
   int n_seq, Hq, Hkv, group, hblocks, max_len, window, n_chunks;
   float c;
-  int negate;
+  int qmode;
 };
 
 int prefill_block_q(bool f32);

@@ -23,6 +23,8 @@
 //     straddle a boundary are masked.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "attn_device.hpp"
 #include "kernels.hpp"
 #include "plan.hpp"
@@ -31,21 +33,59 @@ namespace attnfwd {
 
 template <int D, int BK>
 struct Bf16Cfg {
-  static constexpr int THREADS = 256, BQ = 128, NB = BK / 32;
-  static constexpr int KP = D + 8;    // K row pitch (elements): rows land 16 bytes apart mod 256
-  static constexpr int VP = D + 32;   // V row pitch (elements): rows land 64 bytes apart mod 256
-  static constexpr int K_ELEMS = BK * KP, V_ELEMS = BK * VP, STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int CHUNKS = D / 8;                   // 16-byte pieces per row
-  static constexpr int LOADS = BK * CHUNKS / THREADS;    // pieces per thread per tensor
-  static_assert(BK * CHUNKS % THREADS == 0, "tile must split evenly over the threads");
+  static constexpr int THREADS = 256, WAVES = 4, BQ = 128, NB = BK / 32;
+  static constexpr int ROWB = D * 2;    // bytes of one K/V row in memory
+  static constexpr int CH = D / 8;      // 16-byte chunks per row
+  // LDS row pitches.  K rows sit 16 bytes apart modulo the 256-byte bank space, so the A-operand
+  // reads (16 consecutive rows, one chunk each) hit 16 distinct slots; V rows sit 64 bytes apart,
+  // so a transposed read (4 consecutive rows x 64 bytes per half-wave) covers the bank space once.
+  static constexpr int KPB = ROWB + 16, VPB = ROWB + 64;
+  static constexpr int K_TILE = BK * KPB, V_TILE = BK * VPB;  // LDS bytes per stage
+  static constexpr int K_LOADS = (K_TILE + 1023) / 1024;      // wave-wide 16-byte loads per tile
+  static constexpr int V_LOADS = (V_TILE + 1023) / 1024;
+  static constexpr int KL_PER_WAVE = (K_LOADS + WAVES - 1) / WAVES;
+  static constexpr int VL_PER_WAVE = (V_LOADS + WAVES - 1) / WAVES;
+  static constexpr int LDS_BYTES = 2 * K_TILE + 2 * V_TILE + 1024;  // + slack for the last partial load
 };
+
+// Per-lane key window of an edge tile, relative to kbase = k0 + 4*(lane/32): key kbase + ci is
+// visible iff lo <= ci <= hi.
+__device__ __forceinline__ void edge_limits(int k0, int h, int q, const FwdArgs& a, int& lo, int& hi) {
+  const int pos = q + (a.Lk - a.Lq);
+  int hk = a.Lk - 1;
+  if (a.causal && pos < hk) hk = pos;
+  int lk = 0;
+  if (a.window > 0 && pos - a.window + 1 > lk) lk = pos - a.window + 1;
+  const int kbase = k0 + 4 * h;
+  lo = lk - kbase;
+  hi = hk - kbase;
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// N wave-wide global->LDS loads of one tile: load i writes LDS bytes [j*1024, +1024) of `stage`,
+// j = wave + waves*i, from byte offset voff[i] + gbase of the buffer; lanes with ok[i] = false
+// (pad slots, slots past the tile) are skipped.
+template <int N>
+__device__ __forceinline__ void issue_loads(__amdgpu_buffer_rsrc_t rs, unsigned char* stage, int wave, int waves,
+                                            const unsigned (&voff)[N], const bool (&ok)[N], unsigned gbase) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int j = wave + waves * i;
+    if (ok[i]) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(stage + j * 1024), 16, voff[i], gbase, 0, 0);
+  }
+}
 
 template <int D, int BK>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   using C = Bf16Cfg<D, BK>;
-  __shared__ __attribute__((aligned(16))) unsigned short smem[2 * C::STAGE];
+  constexpr int NB = C::NB;
+  // Two K stages and two V stages, filled straight from global memory by buffer loads while the
+  // other stage is being computed on.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: kept in an SGPR
   const int h = lane >> 5, col = lane & 31;
   const PrefillTile t = prefill_tile(blockIdx.x, a.B, a.Hq, a.group, a.n_qt, a.causal, a.heads_per_xcd);
   const int q_start = t.qt * C::BQ;
@@ -53,148 +93,132 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const KeyRange kr = key_range(q_start, C::BQ, a.Lq, a.Lk, BK, a.causal, a.window);
 
   const unsigned short* Qg = (const unsigned short*)a.q + ((size_t)(t.b * a.Hq + t.hq) * a.Lq) * D;
-  const unsigned short* Kg = (const unsigned short*)a.k + ((size_t)(t.b * a.Hkv + t.hkv) * a.Lk) * D;
-  const unsigned short* Vg = (const unsigned short*)a.v + ((size_t)(t.b * a.Hkv + t.hkv) * a.Lk) * D;
+  const size_t kv_off = ((size_t)(t.b * a.Hkv + t.hkv) * a.Lk) * D;
+  // Buffer descriptors over this head's K and V: rows at or past Lk read as zeros.
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned short*)a.k + kv_off), 0, a.Lk * C::ROWB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned short*)a.v + kv_off), 0, a.Lk * C::ROWB, 0x00020000);
 
   // Q rows as the B operand: lane holds Q[q][16*ks + 8*h .. +7] for every ks.
   bf16x8 qf[D / 16];
   {
-    const unsigned flip = a.negate ? 0x80008000u : 0u;  // negative scale: flip the sign of Q exactly
+#pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       u32x4 w = {0u, 0u, 0u, 0u};
       if (q < a.Lq) w = *(const u32x4*)(Qg + (size_t)q * D + ks * 16 + h * 8);
-      w ^= flip;
-      qf[ks] = __builtin_bit_cast(bf16x8, w);
+      qf[ks] = __builtin_bit_cast(bf16x8, q_word(w, a.qmode));
     }
   }
 
   f32x16 o[D / 32];
+#pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
   RowState st = {-INFINITY, 0.f};
-
-  u32x4 kreg[C::LOADS], vreg[C::LOADS];
-  auto load_tile = [&](int kt) {
-    const int k0 = kt * BK;
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int idx = tid + i * C::THREADS;
-      const int row = idx / C::CHUNKS, ch = idx % C::CHUNKS;
-      const int key = k0 + row;
-      if (key < a.Lk) {
-        kreg[i] = *(const u32x4*)(Kg + (size_t)key * D + ch * 8);
-        vreg[i] = *(const u32x4*)(Vg + (size_t)key * D + ch * 8);
-      } else {
-        kreg[i] = u32x4{0u, 0u, 0u, 0u};
-        vreg[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto store_tile = [&](int stage) {
-    unsigned short* Ks = smem + stage * C::STAGE;
-    unsigned short* Vs = Ks + C::K_ELEMS;
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int idx = tid + i * C::THREADS;
-      const int row = idx / C::CHUNKS, ch = idx % C::CHUNKS;
-      *(u32x4*)(Ks + row * C::KP + ch * 8) = kreg[i];
-      *(u32x4*)(Vs + row * C::VP + ch * 8) = vreg[i];
-    }
-  };
-
-  if (kr.kt_lo <= kr.kt_hi) {
-    load_tile(kr.kt_lo);
-    store_tile(0);
-    __syncthreads();
-  }
   const float c = a.c;
-  // ds_read_b64_tr_b16 addressing for the V^T operand (see attn_device.hpp): 16-lane group G
-  // covers columns 16*(G%2) .. +15 of a 32-column block, half-wave h covers keys 4h.. of each
-  // 8-key group.
-  const int trG = lane >> 4, tri = lane & 15;
-  const int tr_row = 4 * h + (tri >> 2);
-  const int tr_col = (trG & 1) * 16 + (tri & 3) * 4;
 
-  for (int kt = kr.kt_lo; kt <= kr.kt_hi; ++kt) {
-    const int stage = (kt - kr.kt_lo) & 1;
-    const bool more = kt < kr.kt_hi;
-    if (more) load_tile(kt + 1);
+  // Global -> LDS.  Wave-wide load j of a tile writes 16 bytes per lane at LDS offset
+  // j*1024 + 16*lane of the stage; that slot is row o / pitch, chunk (o % pitch) / 16 of the padded
+  // layout.  Pad slots and slots past the tile are skipped; rows past Lk read as zeros.
+  unsigned k_voff[C::KL_PER_WAVE], v_voff[C::VL_PER_WAVE];
+  bool k_ok[C::KL_PER_WAVE], v_ok[C::VL_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < C::KL_PER_WAVE; ++i) {
+    const int j = wave + C::WAVES * i, o = j * 1024 + 16 * lane;
+    const int row = o / C::KPB, chunk = (o % C::KPB) / 16;
+    k_ok[i] = j < C::K_LOADS && row < BK && chunk < C::CH;
+    k_voff[i] = (unsigned)(row * C::ROWB + chunk * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < C::VL_PER_WAVE; ++i) {
+    const int j = wave + C::WAVES * i, o = j * 1024 + 16 * lane;
+    const int row = o / C::VPB, chunk = (o % C::VPB) / 16;
+    v_ok[i] = j < C::V_LOADS && row < BK && chunk < C::CH;
+    v_voff[i] = (unsigned)(row * C::ROWB + chunk * 16);
+  }
+  auto issue_k = [&](int stage, int kt) {
+    issue_loads(krs, smem + stage * C::K_TILE, wave, C::WAVES, k_voff, k_ok, (unsigned)(kt * BK * C::ROWB));
+  };
+  auto issue_v = [&](int stage, int kt) {
+    issue_loads(vrs, smem + 2 * C::K_TILE + stage * C::V_TILE, wave, C::WAVES, v_voff, v_ok,
+                (unsigned)(kt * BK * C::ROWB));
+  };
 
-    const unsigned short* Ks = smem + stage * C::STAGE;
-    const unsigned short* Vs = Ks + C::K_ELEMS;
-    const int k0 = kt * BK;
-
-    // ---- S^T = K Q^T (fp32 accumulate); scale is applied later, in fp32 ----
-    f32x16 s[C::NB];
-    for (int kb = 0; kb < C::NB; ++kb)
+  // K reads for S^T = K Q^T: lane reads row 32*kb + col, elements 16*ks + 8*h .. +7.
+  const int k_lane = col * C::KPB + h * 16;
+  auto qk = [&](int stage, f32x16 (&s)[NB]) {
+    const unsigned char* Ks = smem + stage * C::K_TILE + k_lane;
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-    for (int ks = 0; ks < D / 16; ++ks) {
-      for (int kb = 0; kb < C::NB; ++kb) {
-        const bf16x8 kf = *(const bf16x8*)(Ks + (kb * 32 + col) * C::KP + ks * 16 + h * 8);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) {
+        const bf16x8 kf = *(const bf16x8*)(Ks + kb * 32 * C::KPB + ks * 32);
         s[kb] = mfma_32x32x16(kf, qf[ks], s[kb]);
       }
-    }
-
-    // ---- mask (only tiles that straddle a boundary) ----
-    const bool edge = !tile_full(k0, q_start, C::BQ, a.Lq, a.Lk, BK, a.causal, a.window);
-    if (edge) {
-      for (int kb = 0; kb < C::NB; ++kb)
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + kb * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
-          if (!visible(key, q, a.Lq, a.Lk, a.causal, a.window)) s[kb][i] = -INFINITY;
-        }
-    }
-
-    // ---- online softmax ([DS-Attn §二]) with a lazily raised reference maximum ----
-    float mx = -INFINITY;
-    for (int kb = 0; kb < C::NB; ++kb)
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = pair_max(mx);
-    const float tmax = (mx == -INFINITY) ? -INFINITY : mx * c;
-    const bool need = tmax > st.m + kRescaleSlack;
-    if (wave_any(need)) {
-      const float m_new = need ? tmax : st.m;
-      const float alpha = need ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.f;
-      st.l *= alpha;
-      for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-      st.m = m_new;
-    }
-    const float mb = (st.m == -INFINITY) ? 0.f : st.m;
-
-    // P = exp2(S * c - m), rounded to bf16 for the MFMA; the row sum takes the fp32 values so
-    // that the LSE keeps fp32 accuracy.
-    unsigned pk[C::NB * 8];
-    float lsum = 0.f;
-    for (int kb = 0; kb < C::NB; ++kb) {
-      for (int pi = 0; pi < 8; ++pi) {
-        const float s0 = s[kb][2 * pi], s1 = s[kb][2 * pi + 1];
-        float p0 = __builtin_amdgcn_exp2f(fmaf(s0, c, -mb));
-        float p1 = __builtin_amdgcn_exp2f(fmaf(s1, c, -mb));
-        if (edge) {
-          p0 = (s0 == -INFINITY) ? 0.f : p0;
-          p1 = (s1 == -INFINITY) ? 0.f : p1;
-        }
-        pk[kb * 8 + pi] = pack_bf16x2(p0, p1);
-        lsum += p0 + p1;
-      }
-    }
-    st.l += lsum;
-
-    // ---- O^T += V^T P^T ----
-    for (int j = 0; j < BK / 16; ++j) {
-      const int kb = j >> 1, half = j & 1;
-      const u32x4 pw = {pk[kb * 8 + half * 4 + 0], pk[kb * 8 + half * 4 + 1], pk[kb * 8 + half * 4 + 2],
-                        pk[kb * 8 + half * 4 + 3]};
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-      const unsigned short* vrow = Vs + (16 * j + tr_row) * C::VP + tr_col;
+  };
+  // V^T operand through ds_read_b64_tr_b16 (see attn_device.hpp): lane reads 8 bytes at row
+  // 16*j + 8*rr + 4*h + (lane&15)/4, columns 32*dt + 16*((lane>>4)&1) + 4*(lane&3) .. +3.
+  const int v_lane = (4 * h + ((lane & 15) >> 2)) * C::VPB + ((lane >> 4) & 1) * 32 + (lane & 3) * 8;
+  auto pv = [&](int stage, int kb, const u32x4 (&pw)[2]) {
+    const unsigned char* Vs = smem + 2 * C::K_TILE + stage * C::V_TILE + v_lane;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int j = 2 * kb + half;
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[half]);
+#pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const u32x2 r0 = lds_read_tr16(vrow + dt * 32);
-        const u32x2 r1 = lds_read_tr16(vrow + 8 * C::VP + dt * 32);
-        const u32x4 vw = {r0[0], r0[1], r1[0], r1[1]};
+        const u32x2 r0 = lds_read_tr16(Vs + 16 * j * C::VPB + dt * 64);
+        const u32x2 r1 = lds_read_tr16(Vs + (16 * j + 8) * C::VPB + dt * 64);
+        const u32x4 vw = __builtin_shufflevector(r0, r1, 0, 1, 2, 3);
         o[dt] = mfma_32x32x16(__builtin_bit_cast(bf16x8, vw), pb, o[dt]);
       }
     }
-
-    if (more) store_tile(stage ^ 1);
+  };
+  const int lo = kr.kt_lo, hi = kr.kt_hi;
+  // One tile on stage `stage` (a compile-time constant after the unroll below): start the loads of
+  // tile kt+1 into the other stage, S = K Q^T, mask (edge tiles only), the online softmax of S,
+  // O += P V, then wait for the loads and synchronise.
+  auto step = [&](int kt, auto stage_c) {
+    constexpr int STAGE = decltype(stage_c)::value;
+    if (kt + 1 <= hi) {
+      issue_k(STAGE ^ 1, kt + 1);
+      issue_v(STAGE ^ 1, kt + 1);
+    }
+    f32x16 sc[NB];
+    qk(STAGE, sc);
+    const int k0 = kt * BK;
+    if (!tile_full(k0, q_start, C::BQ, a.Lq, a.Lk, BK, a.causal, a.window)) {
+      int elo, ehi;
+      edge_limits(k0, h, q, a, elo, ehi);
+      mask_tile(sc, elo, ehi);
+    }
+    const float mb = update_max(sc, st, o, c);
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+      unsigned pk[8];
+      exp_block(sc[kb], c, mb, st, pk);
+      const u32x4 pw[2] = {u32x4{pk[0], pk[1], pk[2], pk[3]}, u32x4{pk[4], pk[5], pk[6], pk[7]}};
+      pv(STAGE, kb, pw);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's global->LDS loads have landed
     __syncthreads();
+  };
+
+  if (lo <= hi) {
+    issue_k(0, lo);
+    issue_v(0, lo);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = lo; kt <= hi; kt += 2) {
+      step(kt, std::integral_constant<int, 0>{});
+      if (kt + 1 <= hi) step(kt + 1, std::integral_constant<int, 1>{});
+    }
   }
 
   // ---- epilogue: O = acc / l (bf16, round to nearest even), LSE in natural log ----
@@ -202,7 +226,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (q < a.Lq) {
     unsigned short* Og = (unsigned short*)a.o + ((size_t)(t.b * a.Hq + t.hq) * a.Lq + q) * D;
+#pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
       for (int g = 0; g < 4; ++g) {
         const u32x2 w = {pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv),
                          pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv)};
@@ -247,12 +273,12 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
   // Contraction index of MFMA step (ks2, e) in half-wave h is d = 4*ks2 + 2*h + e.
   float qf[D / 2];
   {
-    const float sgn = a.negate ? -1.f : 1.f;
+    const float sgn = a.qmode == kQNegate ? -1.f : (a.qmode == kQZero ? 0.f : 1.f);
     for (int ks2 = 0; ks2 < D / 4; ++ks2) {
       float2 w = make_float2(0.f, 0.f);
       if (q < a.Lq) w = *(const float2*)(Qg + (size_t)q * D + 4 * ks2 + 2 * h);
-      qf[2 * ks2] = w.x * sgn;
-      qf[2 * ks2 + 1] = w.y * sgn;
+      qf[2 * ks2] = a.qmode == kQZero ? 0.f : w.x * sgn;
+      qf[2 * ks2 + 1] = a.qmode == kQZero ? 0.f : w.y * sgn;
     }
   }
 
@@ -303,41 +329,22 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
     const float* Vs = Ks + C::K_ELEMS;
     const int k0 = kt * BK;
 
-    f32x16 s;
-    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+    f32x16 s[1];
+    for (int i = 0; i < 16; ++i) s[0][i] = 0.f;
     for (int ks2 = 0; ks2 < D / 4; ++ks2) {
       const float2 kf = *(const float2*)(Ks + col * C::KP + 4 * ks2 + 2 * h);
-      s = mfma_32x32x2(kf.x, qf[2 * ks2], s);
-      s = mfma_32x32x2(kf.y, qf[2 * ks2 + 1], s);
+      s[0] = mfma_32x32x2(kf.x, qf[2 * ks2], s[0]);
+      s[0] = mfma_32x32x2(kf.y, qf[2 * ks2 + 1], s[0]);
     }
-
-    const bool edge = !tile_full(k0, q_start, C::BQ, a.Lq, a.Lk, BK, a.causal, a.window);
-    if (edge) {
-      for (int i = 0; i < 16; ++i) {
-        const int key = k0 + (i >> 2) * 8 + h * 4 + (i & 3);
-        if (!visible(key, q, a.Lq, a.Lk, a.causal, a.window)) s[i] = -INFINITY;
-      }
-    }
-    float mx = -INFINITY;
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
-    mx = pair_max(mx);
-    const float tmax = (mx == -INFINITY) ? -INFINITY : mx * c;
-    const bool need = tmax > st.m + kRescaleSlack;
-    if (wave_any(need)) {
-      const float m_new = need ? tmax : st.m;
-      const float alpha = need ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.f;
-      st.l *= alpha;
-      for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-      st.m = m_new;
-    }
-    const float mb = (st.m == -INFINITY) ? 0.f : st.m;
     float p[16];
-    for (int i = 0; i < 16; ++i) {
-      float pi = __builtin_amdgcn_exp2f(fmaf(s[i], c, -mb));
-      if (edge) pi = (s[i] == -INFINITY) ? 0.f : pi;
-      p[i] = pi;
-      st.l += pi;
+    const bool full = tile_full(k0, q_start, C::BQ, a.Lq, a.Lk, BK, a.causal, a.window);
+    if (!full) {
+      int elo, ehi;
+      edge_limits(k0, h, q, a, elo, ehi);
+      mask_tile(s, elo, ehi);
     }
+    const float mb = update_max(s, st, o, c);
+    exp_block_f32(s[0], c, mb, st, p);
     // O^T += V^T P^T: MFMA i pairs key (8*(i/4) + i%4) of half-wave 0 with key +4 of half 1.
     for (int i = 0; i < 16; ++i) {
       const int key = (i >> 2) * 8 + h * 4 + (i & 3);
@@ -366,12 +373,18 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
 
 // ---------------------------------------------------------------------------------------------
 
+// Explicit instantiations: the host pass must emit a launch stub for every variant.
+template __global__ void fwd_bf16_kernel<64, 64>(FwdArgs);
+template __global__ void fwd_bf16_kernel<128, 64>(FwdArgs);
+template __global__ void fwd_f32_kernel<64>(FwdArgs);
+template __global__ void fwd_f32_kernel<128>(FwdArgs);
+
 int prefill_block_q(bool f32) { return f32 ? F32Cfg<64>::BQ : Bf16Cfg<128, 64>::BQ; }
 int prefill_block_k(bool f32) { return f32 ? F32Cfg<64>::BK : 64; }
 int prefill_threads(bool) { return 256; }
 int prefill_lds_bytes(bool f32, int d) {
   if (f32) return d == 64 ? 2 * F32Cfg<64>::STAGE * 4 : 2 * F32Cfg<128>::STAGE * 4;
-  return d == 64 ? 2 * Bf16Cfg<64, 64>::STAGE * 2 : 2 * Bf16Cfg<128, 64>::STAGE * 2;
+  return d == 64 ? Bf16Cfg<64, 64>::LDS_BYTES : Bf16Cfg<128, 64>::LDS_BYTES;
 }
 
 hipError_t launch_prefill(const FwdArgs& a, bool f32, int d, hipStream_t stream) {
