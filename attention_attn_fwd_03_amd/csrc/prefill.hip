@@ -23,6 +23,7 @@
 //     straddle a boundary are masked.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <type_traits>
 
 #include "attn_device.hpp"
@@ -45,7 +46,8 @@ struct Bf16Cfg {
   static constexpr int V_LOADS = (V_TILE + 1023) / 1024;
   static constexpr int KL_PER_WAVE = (K_LOADS + WAVES - 1) / WAVES;
   static constexpr int VL_PER_WAVE = (V_LOADS + WAVES - 1) / WAVES;
-  static constexpr int LDS_BYTES = 2 * K_TILE + 2 * V_TILE + 1024;  // + slack for the last partial load
+  static constexpr int LDS_BYTES = 2 * K_TILE + 2 * V_TILE;
+  static_assert(K_TILE % 1024 == 0 && V_TILE % 1024 == 0, "stages must be whole wave-wide loads");
 };
 
 // Per-lane key window of an edge tile, relative to kbase = k0 + 4*(lane/32): key kbase + ci is
@@ -64,19 +66,20 @@ __device__ __forceinline__ void edge_limits(int k0, int h, int q, const FwdArgs&
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // N wave-wide global->LDS loads of one tile: load i writes LDS bytes [j*1024, +1024) of `stage`,
-// j = wave + waves*i, from byte offset voff[i] + gbase of the buffer; lanes with ok[i] = false
-// (pad slots, slots past the tile) are skipped.
+// j = wave + waves*i (loads with j >= total are skipped; j is uniform), from byte offset
+// voff[i] + gbase of the buffer.  Lanes that land on pad slots carry an offset past the buffer
+// and write zeros there, which nothing reads; so no lane needs its own branch.
 template <int N>
 __device__ __forceinline__ void issue_loads(__amdgpu_buffer_rsrc_t rs, unsigned char* stage, int wave, int waves,
-                                            const unsigned (&voff)[N], const bool (&ok)[N], unsigned gbase) {
+                                            int total, const unsigned (&voff)[N], unsigned gbase) {
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const int j = wave + waves * i;
-    if (ok[i]) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(stage + j * 1024), 16, voff[i], gbase, 0, 0);
+    if (j < total) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(stage + j * 1024), 16, voff[i], gbase, 0, 0);
   }
 }
 
-template <int D, int BK>
+template <int D, int BK, int PIPE>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   using C = Bf16Cfg<D, BK>;
   constexpr int NB = C::NB;
@@ -122,27 +125,26 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   // Global -> LDS.  Wave-wide load j of a tile writes 16 bytes per lane at LDS offset
   // j*1024 + 16*lane of the stage; that slot is row o / pitch, chunk (o % pitch) / 16 of the padded
   // layout.  Pad slots and slots past the tile are skipped; rows past Lk read as zeros.
+  // An offset past any buffer (and past any gbase it is added to) for pad slots.
+  constexpr unsigned kPastEnd = 0x80000000u;
   unsigned k_voff[C::KL_PER_WAVE], v_voff[C::VL_PER_WAVE];
-  bool k_ok[C::KL_PER_WAVE], v_ok[C::VL_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::KL_PER_WAVE; ++i) {
-    const int j = wave + C::WAVES * i, o = j * 1024 + 16 * lane;
+    const int o = (wave + C::WAVES * i) * 1024 + 16 * lane;
     const int row = o / C::KPB, chunk = (o % C::KPB) / 16;
-    k_ok[i] = j < C::K_LOADS && row < BK && chunk < C::CH;
-    k_voff[i] = (unsigned)(row * C::ROWB + chunk * 16);
+    k_voff[i] = (row < BK && chunk < C::CH) ? (unsigned)(row * C::ROWB + chunk * 16) : kPastEnd;
   }
 #pragma unroll
   for (int i = 0; i < C::VL_PER_WAVE; ++i) {
-    const int j = wave + C::WAVES * i, o = j * 1024 + 16 * lane;
+    const int o = (wave + C::WAVES * i) * 1024 + 16 * lane;
     const int row = o / C::VPB, chunk = (o % C::VPB) / 16;
-    v_ok[i] = j < C::V_LOADS && row < BK && chunk < C::CH;
-    v_voff[i] = (unsigned)(row * C::ROWB + chunk * 16);
+    v_voff[i] = (row < BK && chunk < C::CH) ? (unsigned)(row * C::ROWB + chunk * 16) : kPastEnd;
   }
   auto issue_k = [&](int stage, int kt) {
-    issue_loads(krs, smem + stage * C::K_TILE, wave, C::WAVES, k_voff, k_ok, (unsigned)(kt * BK * C::ROWB));
+    issue_loads(krs, smem + stage * C::K_TILE, wave, C::WAVES, C::K_LOADS, k_voff, (unsigned)(kt * BK * C::ROWB));
   };
   auto issue_v = [&](int stage, int kt) {
-    issue_loads(vrs, smem + 2 * C::K_TILE + stage * C::V_TILE, wave, C::WAVES, v_voff, v_ok,
+    issue_loads(vrs, smem + 2 * C::K_TILE + stage * C::V_TILE, wave, C::WAVES, C::V_LOADS, v_voff,
                 (unsigned)(kt * BK * C::ROWB));
   };
 
@@ -210,7 +212,65 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     __syncthreads();
   };
 
-  if (lo <= hi) {
+  // S-ahead schedule: K runs one tile ahead of V.  In the tile on stage STAGE, S(kt+1) is computed
+  // from the other K stage while the exponentials of S(kt) are formed, so the MFMA pipe has
+  // independent work during the softmax.  K(kt+2) and V(kt+1) load meanwhile.  (On the last tile
+  // the extra S is computed from a stale stage and discarded, which keeps the block branch-free.)
+  auto step_ahead = [&](int kt, auto stage_c, f32x16 (&s_cur)[NB], f32x16 (&s_next)[NB]) {
+    constexpr int STAGE = decltype(stage_c)::value;
+    if (kt + 2 <= hi) issue_k(STAGE, kt + 2);
+    if (kt + 1 <= hi) issue_v(STAGE ^ 1, kt + 1);
+    const int k0 = kt * BK;
+    if (!tile_full(k0, q_start, C::BQ, a.Lq, a.Lk, BK, a.causal, a.window)) {
+      int elo, ehi;
+      edge_limits(k0, h, q, a, elo, ehi);
+      mask_tile(s_cur, elo, ehi);
+    }
+    const float mb = update_max(s_cur, st, o, c);
+    qk(STAGE ^ 1, s_next);
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+      unsigned pk[8];
+      exp_block(s_cur[kb], c, mb, st, pk);
+      const u32x4 pw[2] = {u32x4{pk[0], pk[1], pk[2], pk[3]}, u32x4{pk[4], pk[5], pk[6], pk[7]}};
+      pv(STAGE, kb, pw);
+    }
+    if constexpr (PIPE == 2) {
+      // Issue order: each S(kt+1) MFMA with its K read and a slice of the exponentials, so the
+      // VALU work sits between MFMAs of this wave; then the P.V MFMAs with their V reads.
+#pragma unroll
+      for (int g = 0; g < NB * (D / 16); ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+      }
+#pragma unroll
+      for (int g = 0; g < (BK / 16) * (D / 32); ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  if constexpr (PIPE != 0) {
+    if (lo <= hi) {
+      issue_k(0, lo);
+      issue_v(0, lo);
+      if (lo + 1 <= hi) issue_k(1, lo + 1);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      f32x16 sa[NB], sb[NB];
+      qk(0, sa);
+      __syncthreads();  // every wave is done with K(lo) before its stage is refilled
+      for (int kt = lo; kt <= hi; kt += 2) {
+        step_ahead(kt, std::integral_constant<int, 0>{}, sa, sb);
+        if (kt + 1 <= hi) step_ahead(kt + 1, std::integral_constant<int, 1>{}, sb, sa);
+      }
+    }
+  } else if (lo <= hi) {
     issue_k(0, lo);
     issue_v(0, lo);
     __builtin_amdgcn_s_waitcnt(0);
@@ -374,8 +434,12 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------------------------
 
 // Explicit instantiations: the host pass must emit a launch stub for every variant.
-template __global__ void fwd_bf16_kernel<64, 64>(FwdArgs);
-template __global__ void fwd_bf16_kernel<128, 64>(FwdArgs);
+template __global__ void fwd_bf16_kernel<64, 64, 0>(FwdArgs);
+template __global__ void fwd_bf16_kernel<128, 64, 0>(FwdArgs);
+template __global__ void fwd_bf16_kernel<64, 64, 1>(FwdArgs);
+template __global__ void fwd_bf16_kernel<128, 64, 1>(FwdArgs);
+template __global__ void fwd_bf16_kernel<64, 64, 2>(FwdArgs);
+template __global__ void fwd_bf16_kernel<128, 64, 2>(FwdArgs);
 template __global__ void fwd_f32_kernel<64>(FwdArgs);
 template __global__ void fwd_f32_kernel<128>(FwdArgs);
 
@@ -387,6 +451,15 @@ int prefill_lds_bytes(bool f32, int d) {
   return d == 64 ? Bf16Cfg<64, 64>::LDS_BYTES : Bf16Cfg<128, 64>::LDS_BYTES;
 }
 
+// Schedule choice for tuning (ATTNFWD_PREFILL_PIPE=0/1/2), read once.
+static int prefill_schedule() {
+  static const int v = [] {
+    const char* e = getenv("ATTNFWD_PREFILL_PIPE");
+    return e != nullptr ? atoi(e) : 0;
+  }();
+  return v;
+}
+
 hipError_t launch_prefill(const FwdArgs& a, bool f32, int d, hipStream_t stream) {
   const int64_t grid = (int64_t)a.n_qt * a.B * a.Hq;
   const dim3 g((unsigned)grid), b(256);
@@ -394,8 +467,19 @@ hipError_t launch_prefill(const FwdArgs& a, bool f32, int d, hipStream_t stream)
     if (d == 64) hipLaunchKernelGGL(fwd_f32_kernel<64>, g, b, 0, stream, a);
     else hipLaunchKernelGGL(fwd_f32_kernel<128>, g, b, 0, stream, a);
   } else {
-    if (d == 64) hipLaunchKernelGGL((fwd_bf16_kernel<64, 64>), g, b, 0, stream, a);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<128, 64>), g, b, 0, stream, a);
+    switch (prefill_schedule()) {
+      case 1:
+        if (d == 64) hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, 1>), g, b, 0, stream, a);
+        else hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, 1>), g, b, 0, stream, a);
+        break;
+      case 2:
+        if (d == 64) hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, 2>), g, b, 0, stream, a);
+        else hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, 2>), g, b, 0, stream, a);
+        break;
+      default:
+        if (d == 64) hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, 0>), g, b, 0, stream, a);
+        else hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, 0>), g, b, 0, stream, a);
+    }
   }
   return hipGetLastError();
 }
