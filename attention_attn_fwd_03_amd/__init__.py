@@ -44,7 +44,7 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd.restype = i32
     L.attn_fwd_f32.argtypes = L.attn_fwd.argtypes
     L.attn_fwd_f32.restype = i32
-    L.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32]
+    L.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     L.attn_decode_workspace_size.restype = sz
     L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, i32, f32, vp, sz, vp]
     L.attn_decode.restype = i32
@@ -54,7 +54,7 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_plan.restype = i32
     L.attn_fwd_schedule.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, i64]
     L.attn_fwd_schedule.restype = i32
-    L.attn_decode_plan.argtypes = [i32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    L.attn_decode_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
     L.attn_decode_plan.restype = i32
     _lib = L
     return L
@@ -112,8 +112,8 @@ def attn_fwd(q, k, v, *, causal: bool = False, window: int = 0, scale: float | N
     return (o, lse) if return_lse else o
 
 
-def decode_workspace_size(n_seq: int, Hq: int, d: int, max_len: int) -> int:
-    return int(lib().attn_decode_workspace_size(n_seq, Hq, d, max_len))
+def decode_workspace_size(n_seq: int, Hq: int, Hkv: int, d: int, max_len: int) -> int:
+    return int(lib().attn_decode_workspace_size(n_seq, Hq, Hkv, d, max_len))
 
 
 def attn_decode(q, k_pool, v_pool, offsets, lens, *, max_len: int, window: int = 0, scale: float | None = None,
@@ -135,7 +135,7 @@ def attn_decode(q, k_pool, v_pool, offsets, lens, *, max_len: int, window: int =
         raise ValueError("shape mismatch between q, pools, offsets and lens")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    need = decode_workspace_size(N, Hq, d, max_len)
+    need = decode_workspace_size(N, Hq, Hkv, d, max_len)
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
     o = torch.empty_like(q) if out is None else out
@@ -165,7 +165,8 @@ def fwd_schedule(B, Hq, Hkv, Lq, Lk, d, causal=False, window=0, f32=False) -> np
     return out
 
 
-def decode_plan(max_len: int) -> tuple[int, int]:
+def decode_plan(n_seq: int, Hq: int, Hkv: int, max_len: int) -> tuple[int, int]:
+    """(keys per chunk, number of chunks) the decode pass uses for these sizes."""
     c, n = ctypes.c_int32(), ctypes.c_int32()
-    _check(lib().attn_decode_plan(int(max_len), ctypes.byref(c), ctypes.byref(n)))
+    _check(lib().attn_decode_plan(int(n_seq), int(Hq), int(Hkv), int(max_len), ctypes.byref(c), ctypes.byref(n)))
     return c.value, n.value

@@ -40,9 +40,11 @@ int check_fwd(const void* q, const void* k, const void* v, const void* o, const 
   if (!std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
   (void)lse;
-  // Element offsets are computed in size_t on the device, block indices in 32 bits.
+  // Element offsets are computed in size_t on the device, block indices and per-head buffer
+  // byte ranges in 32 bits.
   const int64_t n_qt = (Lq + 127) / 128;
   if ((int64_t)B * Hq * n_qt >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
+  if ((int64_t)Lk * d * 4 >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }
 
@@ -93,9 +95,9 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
   return fwd_common(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d, causal, window, scale, stream, true);
 }
 
-size_t attn_decode_workspace_size(int n_seq, int Hq, int d, int max_len) {
-  if (n_seq <= 0 || Hq <= 0 || max_len < 1 || (d != 64 && d != 128)) return 0;
-  return decode_workspace_bytes(n_seq, Hq, d, max_len);
+size_t attn_decode_workspace_size(int n_seq, int Hq, int Hkv, int d, int max_len) {
+  if (n_seq <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_len < 1 || (d != 64 && d != 128)) return 0;
+  return decode_workspace_bytes(n_seq, Hq, Hkv, d, max_len);
 }
 
 int attn_decode(const void* q, const void* k_pool, const void* v_pool, const int64_t* offsets,
@@ -110,9 +112,11 @@ int attn_decode(const void* q, const void* k_pool, const void* v_pool, const int
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
   if (n_seq > 65535) return ATTN_ERR_SHAPE;
   const int group = Hq / Hkv;
-  const int hblocks = (group + 31) / 32;
+  const int hblocks = decode_head_blocks(group);
   if ((int64_t)Hkv * hblocks > 65535) return ATTN_ERR_SHAPE;
-  const size_t need = decode_workspace_bytes(n_seq, Hq, d, max_len);
+  // one sequence's rows of one head are addressed with 32-bit byte offsets
+  if ((int64_t)max_len * Hkv * d * 2 >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
+  const size_t need = decode_workspace_bytes(n_seq, Hq, Hkv, d, max_len);
   if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_UNSUPPORTED;
 
@@ -133,7 +137,8 @@ int attn_decode(const void* q, const void* k_pool, const void* v_pool, const int
   a.hblocks = hblocks;
   a.max_len = max_len;
   a.window = window;
-  a.n_chunks = decode_num_chunks(max_len);
+  a.chunk_keys = decode_chunk_keys(n_seq, Hkv * hblocks, max_len);
+  a.n_chunks = decode_num_chunks(max_len, a.chunk_keys);
   set_scale(scale, a.c, a.qmode);
   const hipError_t e = launch_decode(a, d, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -199,11 +204,11 @@ int attn_fwd_schedule(int B, int Hq, int Hkv, int Lq, int Lk, int d, int causal,
   return ATTN_OK;
 }
 
-int attn_decode_plan(int max_len, int32_t* chunk_keys, int32_t* num_chunks) {
+int attn_decode_plan(int n_seq, int Hq, int Hkv, int max_len, int32_t* chunk_keys, int32_t* num_chunks) {
   if (!chunk_keys || !num_chunks) return ATTN_ERR_NULL;
-  if (max_len < 1) return ATTN_ERR_SHAPE;
-  *chunk_keys = kDecodeChunk;
-  *num_chunks = decode_num_chunks(max_len);
+  if (n_seq <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_len < 1) return ATTN_ERR_SHAPE;
+  *chunk_keys = decode_chunk_keys(n_seq, Hkv * decode_head_blocks(Hq / Hkv), max_len);
+  *num_chunks = decode_num_chunks(max_len, *chunk_keys);
   return ATTN_OK;
 }
 

@@ -30,7 +30,7 @@ struct DecArgs {
   float* lse;
   float* ws;  // per-chunk partials: O [n_seq][Hq][n_chunks][d], then (m, l) [n_seq][Hq][n_chunks][2]
   int64_t pool_rows;
-  int n_seq, Hq, Hkv, group, hblocks, max_len, window, n_chunks;
+  int n_seq, Hq, Hkv, group, hblocks, max_len, window, n_chunks, chunk_keys;
   float c;
   int qmode;
 };
@@ -41,7 +41,7 @@ int prefill_threads(bool f32);
 int prefill_lds_bytes(bool f32, int d);
 hipError_t launch_prefill(const FwdArgs& a, bool f32, int d, hipStream_t stream);
 
-size_t decode_workspace_bytes(int n_seq, int Hq, int d, int max_len);
+size_t decode_workspace_bytes(int n_seq, int Hq, int Hkv, int d, int max_len);
 hipError_t launch_decode(const DecArgs& a, int d, hipStream_t stream);
 
 }  // namespace attnfwd

@@ -101,10 +101,19 @@ ATTN_HD PrefillTile prefill_tile(int bid, int B, int Hq, int group, int n_qt, in
 
 ATTN_HD int prefill_heads_per_xcd(int B, int Hq) { return (B * Hq) % 8 == 0 ? (B * Hq) / 8 : 0; }
 
-// Decode: each workgroup handles one chunk of kDecodeChunk keys of one (sequence, KV head,
-// block of up to 32 query heads); a second pass merges the chunks.
-constexpr int kDecodeChunk = 512;
+// Decode: each workgroup handles one chunk of keys of one (sequence, KV head, block of up to 32
+// query heads); a second pass merges the chunks.
+ATTN_HD int decode_head_blocks(int group) { return (group + 31) / 32; }
 
-ATTN_HD int decode_num_chunks(int max_len) { return (max_len + kDecodeChunk - 1) / kDecodeChunk; }
+// Keys per chunk: the largest power of two in [128, 1024] that still gives about 8192 work units
+// at the longest sequence (units = n_seq * KV heads * head blocks * chunks), so that every CU
+// has work, while long chunks keep the number of partials small.
+ATTN_HD int decode_chunk_keys(int n_seq, int units_per_chunk_row, int max_len) {
+  int ck = 1024;
+  while (ck > 128 && (long long)n_seq * units_per_chunk_row * ((max_len + ck - 1) / ck) < 8192) ck /= 2;
+  return ck;
+}
+
+ATTN_HD int decode_num_chunks(int max_len, int chunk_keys) { return (max_len + chunk_keys - 1) / chunk_keys; }
 
 }  // namespace attnfwd

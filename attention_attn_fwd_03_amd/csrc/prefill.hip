@@ -66,17 +66,27 @@ __device__ __forceinline__ void edge_limits(int k0, int h, int q, const FwdArgs&
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // N wave-wide global->LDS loads of one tile: load i writes LDS bytes [j*1024, +1024) of `stage`,
-// j = wave + waves*i (loads with j >= total are skipped; j is uniform), from byte offset
-// voff[i] + gbase of the buffer.  Lanes that land on pad slots carry an offset past the buffer
-// and write zeros there, which nothing reads; so no lane needs its own branch.
+// j = wave + waves*i (loads with j >= total are skipped; j is uniform), from byte offset voff[i]
+// of the buffer `rs`.  The buffer covers exactly the tile's valid rows, so rows past the end of
+// the sequence read as zeros; lanes that land on pad slots carry an offset past any buffer and
+// write zeros there, which nothing reads.  No lane needs its own branch.  (The scalar offset
+// is kept 0: only the per-lane offset is range-checked.)
 template <int N>
 __device__ __forceinline__ void issue_loads(__amdgpu_buffer_rsrc_t rs, unsigned char* stage, int wave, int waves,
-                                            int total, const unsigned (&voff)[N], unsigned gbase) {
+                                            int total, const unsigned (&voff)[N]) {
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const int j = wave + waves * i;
-    if (j < total) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(stage + j * 1024), 16, voff[i], gbase, 0, 0);
+    if (j < total) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(stage + j * 1024), 16, voff[i], 0, 0, 0);
   }
+}
+
+// Buffer descriptor over rows [row0, nrows) of a row-major [nrows, D] bf16 matrix at `base`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const unsigned short* base, int row0, int nrows,
+                                                            int row_bytes) {
+  const int left = nrows - row0 > 0 ? nrows - row0 : 0;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned char*)base + (size_t)row0 * row_bytes), 0,
+                                           left * row_bytes, 0x00020000);
 }
 
 template <int D, int BK, int PIPE>
@@ -84,8 +94,23 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   using C = Bf16Cfg<D, BK>;
   constexpr int NB = C::NB;
   // Two K stages and two V stages, filled straight from global memory by buffer loads while the
-  // other stage is being computed on.
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
+  // other stage is being computed on.  Each stage is its own LDS object, so the compiler can see
+  // that reads of one stage do not depend on the loads still landing in the other and does not
+  // wait for them.
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[C::K_TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[C::K_TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[C::V_TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[C::V_TILE];
+  auto k_stage = [&](auto st_c) -> unsigned char* {
+    if constexpr (decltype(st_c)::value == 0) return k_lds0;
+    else return k_lds1;
+  };
+  auto v_stage = [&](auto st_c) -> unsigned char* {
+    if constexpr (decltype(st_c)::value == 0) return v_lds0;
+    else return v_lds1;
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: kept in an SGPR
@@ -97,11 +122,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
 
   const unsigned short* Qg = (const unsigned short*)a.q + ((size_t)(t.b * a.Hq + t.hq) * a.Lq) * D;
   const size_t kv_off = ((size_t)(t.b * a.Hkv + t.hkv) * a.Lk) * D;
-  // Buffer descriptors over this head's K and V: rows at or past Lk read as zeros.
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned short*)a.k + kv_off), 0, a.Lk * C::ROWB, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned short*)a.v + kv_off), 0, a.Lk * C::ROWB, 0x00020000);
+  const unsigned short* Kh = (const unsigned short*)a.k + kv_off;  // this head's K and V rows
+  const unsigned short* Vh = (const unsigned short*)a.v + kv_off;
 
   // Q rows as the B operand: lane holds Q[q][16*ks + 8*h .. +7] for every ks.
   bf16x8 qf[D / 16];
@@ -124,7 +146,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
 
   // Global -> LDS.  Wave-wide load j of a tile writes 16 bytes per lane at LDS offset
   // j*1024 + 16*lane of the stage; that slot is row o / pitch, chunk (o % pitch) / 16 of the padded
-  // layout.  Pad slots and slots past the tile are skipped; rows past Lk read as zeros.
+  // layout.  The per-lane byte offsets inside a tile are the same for every tile.
   // An offset past any buffer (and past any gbase it is added to) for pad slots.
   constexpr unsigned kPastEnd = 0x80000000u;
   unsigned k_voff[C::KL_PER_WAVE], v_voff[C::VL_PER_WAVE];
@@ -140,18 +162,17 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     const int row = o / C::VPB, chunk = (o % C::VPB) / 16;
     v_voff[i] = (row < BK && chunk < C::CH) ? (unsigned)(row * C::ROWB + chunk * 16) : kPastEnd;
   }
-  auto issue_k = [&](int stage, int kt) {
-    issue_loads(krs, smem + stage * C::K_TILE, wave, C::WAVES, C::K_LOADS, k_voff, (unsigned)(kt * BK * C::ROWB));
+  auto issue_k = [&](auto st_c, int kt) {
+    issue_loads(rows_rsrc(Kh, kt * BK, a.Lk, C::ROWB), k_stage(st_c), wave, C::WAVES, C::K_LOADS, k_voff);
   };
-  auto issue_v = [&](int stage, int kt) {
-    issue_loads(vrs, smem + 2 * C::K_TILE + stage * C::V_TILE, wave, C::WAVES, C::V_LOADS, v_voff,
-                (unsigned)(kt * BK * C::ROWB));
+  auto issue_v = [&](auto st_c, int kt) {
+    issue_loads(rows_rsrc(Vh, kt * BK, a.Lk, C::ROWB), v_stage(st_c), wave, C::WAVES, C::V_LOADS, v_voff);
   };
 
   // K reads for S^T = K Q^T: lane reads row 32*kb + col, elements 16*ks + 8*h .. +7.
   const int k_lane = col * C::KPB + h * 16;
-  auto qk = [&](int stage, f32x16 (&s)[NB]) {
-    const unsigned char* Ks = smem + stage * C::K_TILE + k_lane;
+  auto qk = [&](auto st_c, f32x16 (&s)[NB]) {
+    const unsigned char* Ks = k_stage(st_c) + k_lane;
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
@@ -167,8 +188,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   // V^T operand through ds_read_b64_tr_b16 (see attn_device.hpp): lane reads 8 bytes at row
   // 16*j + 8*rr + 4*h + (lane&15)/4, columns 32*dt + 16*((lane>>4)&1) + 4*(lane&3) .. +3.
   const int v_lane = (4 * h + ((lane & 15) >> 2)) * C::VPB + ((lane >> 4) & 1) * 32 + (lane & 3) * 8;
-  auto pv = [&](int stage, int kb, const u32x4 (&pw)[2]) {
-    const unsigned char* Vs = smem + 2 * C::K_TILE + stage * C::V_TILE + v_lane;
+  auto pv = [&](auto st_c, int kb, const u32x4 (&pw)[2]) {
+    const unsigned char* Vs = v_stage(st_c) + v_lane;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int j = 2 * kb + half;
@@ -188,12 +209,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   // O += P V, then wait for the loads and synchronise.
   auto step = [&](int kt, auto stage_c) {
     constexpr int STAGE = decltype(stage_c)::value;
+    using Cur = std::integral_constant<int, STAGE>;
+    using Oth = std::integral_constant<int, STAGE ^ 1>;
     if (kt + 1 <= hi) {
-      issue_k(STAGE ^ 1, kt + 1);
-      issue_v(STAGE ^ 1, kt + 1);
+      issue_k(Oth{}, kt + 1);
+      issue_v(Oth{}, kt + 1);
     }
     f32x16 sc[NB];
-    qk(STAGE, sc);
+    qk(Cur{}, sc);
     const int k0 = kt * BK;
     if (!tile_full(k0, q_start, C::BQ, a.Lq, a.Lk, BK, a.causal, a.window)) {
       int elo, ehi;
@@ -206,7 +229,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
       unsigned pk[8];
       exp_block(sc[kb], c, mb, st, pk);
       const u32x4 pw[2] = {u32x4{pk[0], pk[1], pk[2], pk[3]}, u32x4{pk[4], pk[5], pk[6], pk[7]}};
-      pv(STAGE, kb, pw);
+      pv(Cur{}, kb, pw);
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's global->LDS loads have landed
     __syncthreads();
@@ -218,8 +241,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   // the extra S is computed from a stale stage and discarded, which keeps the block branch-free.)
   auto step_ahead = [&](int kt, auto stage_c, f32x16 (&s_cur)[NB], f32x16 (&s_next)[NB]) {
     constexpr int STAGE = decltype(stage_c)::value;
-    if (kt + 2 <= hi) issue_k(STAGE, kt + 2);
-    if (kt + 1 <= hi) issue_v(STAGE ^ 1, kt + 1);
+    using Cur = std::integral_constant<int, STAGE>;
+    using Oth = std::integral_constant<int, STAGE ^ 1>;
+    if (kt + 2 <= hi) issue_k(Cur{}, kt + 2);
+    if (kt + 1 <= hi) issue_v(Oth{}, kt + 1);
     const int k0 = kt * BK;
     if (!tile_full(k0, q_start, C::BQ, a.Lq, a.Lk, BK, a.causal, a.window)) {
       int elo, ehi;
@@ -227,13 +252,13 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
       mask_tile(s_cur, elo, ehi);
     }
     const float mb = update_max(s_cur, st, o, c);
-    qk(STAGE ^ 1, s_next);
+    qk(Oth{}, s_next);
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) {
       unsigned pk[8];
       exp_block(s_cur[kb], c, mb, st, pk);
       const u32x4 pw[2] = {u32x4{pk[0], pk[1], pk[2], pk[3]}, u32x4{pk[4], pk[5], pk[6], pk[7]}};
-      pv(STAGE, kb, pw);
+      pv(Cur{}, kb, pw);
     }
     if constexpr (PIPE == 2) {
       // Issue order: each S(kt+1) MFMA with its K read and a slice of the exponentials, so the
@@ -257,27 +282,27 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
 
   if constexpr (PIPE != 0) {
     if (lo <= hi) {
-      issue_k(0, lo);
-      issue_v(0, lo);
-      if (lo + 1 <= hi) issue_k(1, lo + 1);
+      issue_k(S0{}, lo);
+      issue_v(S0{}, lo);
+      if (lo + 1 <= hi) issue_k(S1{}, lo + 1);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       f32x16 sa[NB], sb[NB];
-      qk(0, sa);
+      qk(S0{}, sa);
       __syncthreads();  // every wave is done with K(lo) before its stage is refilled
       for (int kt = lo; kt <= hi; kt += 2) {
-        step_ahead(kt, std::integral_constant<int, 0>{}, sa, sb);
-        if (kt + 1 <= hi) step_ahead(kt + 1, std::integral_constant<int, 1>{}, sb, sa);
+        step_ahead(kt, S0{}, sa, sb);
+        if (kt + 1 <= hi) step_ahead(kt + 1, S1{}, sb, sa);
       }
     }
   } else if (lo <= hi) {
-    issue_k(0, lo);
-    issue_v(0, lo);
+    issue_k(S0{}, lo);
+    issue_v(S0{}, lo);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int kt = lo; kt <= hi; kt += 2) {
-      step(kt, std::integral_constant<int, 0>{});
-      if (kt + 1 <= hi) step(kt + 1, std::integral_constant<int, 1>{});
+      step(kt, S0{});
+      if (kt + 1 <= hi) step(kt + 1, S1{});
     }
   }
 

@@ -146,7 +146,7 @@ def main():
     max_len = int(lens.max())
     od = torch.empty_like(qd)
     lsed = torch.empty((cd.n_seq, cd.Hq), device=dev, dtype=torch.float32)
-    ws = torch.empty(af.decode_workspace_size(cd.n_seq, cd.Hq, cd.d, max_len), device=dev, dtype=torch.uint8)
+    ws = torch.empty(af.decode_workspace_size(cd.n_seq, cd.Hq, cd.Hkv, cd.d, max_len), device=dev, dtype=torch.uint8)
     torch.cuda.synchronize()
 
     do_pre = args.only in (None, "prefill")
@@ -279,7 +279,7 @@ def run_suite(args):
             reps_data.append((qd, kp, vp, offs, lens_t))
         od = torch.empty_like(reps_data[0][0])
         lsed = torch.empty((c.n_seq, c.Hq), device=dev, dtype=torch.float32)
-        ws = torch.empty(af.decode_workspace_size(c.n_seq, c.Hq, c.d, max_len), device=dev, dtype=torch.uint8)
+        ws = torch.empty(af.decode_workspace_size(c.n_seq, c.Hq, c.Hkv, c.d, max_len), device=dev, dtype=torch.uint8)
         it = [0]
 
         def call():

@@ -40,7 +40,8 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
   ATTN_ERR_SHAPE = 2,       /* a size <= 0 (n_seq may not be 0 either), Hq % Hkv != 0, window < 0,
-                               max_len < 1, pool_rows < 0, or a size too large to index */
+                               max_len < 1, pool_rows < 0, or a size too large to index (per head,
+                               Lk*d*4 and max_len*Hkv*d*2 must stay below 2^31 bytes) */
   ATTN_ERR_UNSUPPORTED = 3, /* d not in {64, 128}; window > 0 without causal; scale not finite;
                                a pointer not 16-byte aligned */
   ATTN_ERR_WORKSPACE = 4,   /* decode workspace NULL or smaller than attn_decode_workspace_size */
@@ -63,7 +64,7 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
                  int causal, int window, float scale, void* stream);
 
 /* Bytes of device workspace attn_decode needs for these sizes (0 if a size is invalid). */
-size_t attn_decode_workspace_size(int n_seq, int Hq, int d, int max_len);
+size_t attn_decode_workspace_size(int n_seq, int Hq, int Hkv, int d, int max_len);
 
 /* Decode: one new query token per sequence against its cached keys and values.
  *   q, o [n_seq, Hq, d] bf16;  k_pool, v_pool [pool_rows, Hkv, d] bf16.
@@ -109,8 +110,9 @@ int attn_fwd_plan(int B, int Hq, int Hkv, int Lq, int Lk, int d, int causal, int
 int attn_fwd_schedule(int B, int Hq, int Hkv, int Lq, int Lk, int d, int causal, int window,
                       int dtype_f32, int32_t* out, int64_t out_len);
 
-/* Keys per decode chunk and number of chunks for max_len. */
-int attn_decode_plan(int max_len, int32_t* chunk_keys, int32_t* num_chunks);
+/* Keys per decode chunk (a power of two in [128, 1024], chosen so that the batch splits into
+ * enough work units) and the number of chunks at max_len. */
+int attn_decode_plan(int n_seq, int Hq, int Hkv, int max_len, int32_t* chunk_keys, int32_t* num_chunks);
 
 #ifdef __cplusplus
 }

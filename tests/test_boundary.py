@@ -54,6 +54,7 @@ def fwd(**kw):
     (dict(B=0), af.ATTN_ERR_SHAPE), (dict(Hq=-1), af.ATTN_ERR_SHAPE), (dict(Lq=0), af.ATTN_ERR_SHAPE),
     (dict(Lk=0), af.ATTN_ERR_SHAPE), (dict(Hq=6, Hkv=4), af.ATTN_ERR_SHAPE), (dict(window=-1), af.ATTN_ERR_SHAPE),
     (dict(causal=2), af.ATTN_ERR_SHAPE), (dict(B=1 << 20, Hq=1 << 10, Hkv=1 << 10, Lq=1 << 10), af.ATTN_ERR_SHAPE),
+    (dict(Lk=1 << 23), af.ATTN_ERR_SHAPE),
     (dict(d=96), af.ATTN_ERR_UNSUPPORTED), (dict(d=256), af.ATTN_ERR_UNSUPPORTED),
     (dict(causal=0, window=16), af.ATTN_ERR_UNSUPPORTED),
     (dict(scale=math.inf), af.ATTN_ERR_UNSUPPORTED), (dict(scale=math.nan), af.ATTN_ERR_UNSUPPORTED),
@@ -86,20 +87,37 @@ def dec(**kw):
     (dict(d=32), af.ATTN_ERR_UNSUPPORTED), (dict(scale=-math.inf), af.ATTN_ERR_UNSUPPORTED),
     (dict(kp=MISALIGNED), af.ATTN_ERR_UNSUPPORTED),
     (dict(ws=None), af.ATTN_ERR_WORKSPACE), (dict(ws_bytes=16), af.ATTN_ERR_WORKSPACE),
+    (dict(max_len=1 << 22, Hkv=8, Hq=8), af.ATTN_ERR_SHAPE),
 ])
 def test_decode_rejects_bad_arguments(kw, status):
     assert dec(**kw) == status
 
 
 def test_decode_workspace_size():
-    chunk, n = af.decode_plan(32768)
+    chunk, n = af.decode_plan(64, 32, 8, 32768)
     assert n == math.ceil(32768 / chunk)
-    assert af.decode_workspace_size(64, 32, 128, 32768) == 64 * 32 * n * (128 + 2) * 4
-    assert af.decode_workspace_size(3, 5, 64, 1) == 3 * 5 * 1 * 66 * 4
-    assert af.decode_workspace_size(0, 32, 128, 10) == 0
-    assert af.decode_workspace_size(4, 32, 96, 10) == 0
+    assert af.decode_workspace_size(64, 32, 8, 128, 32768) == 64 * 32 * n * (128 + 2) * 4
+    chunk, n = af.decode_plan(3, 5, 5, 1)
+    assert (chunk, n) == (128, 1)
+    assert af.decode_workspace_size(3, 5, 5, 64, 1) == 3 * 5 * 1 * 66 * 4
+    assert af.decode_workspace_size(0, 32, 8, 128, 10) == 0
+    assert af.decode_workspace_size(4, 32, 8, 96, 10) == 0
+    assert af.decode_workspace_size(4, 32, 7, 128, 10) == 0
     with pytest.raises(RuntimeError):
-        af.decode_plan(0)
+        af.decode_plan(4, 32, 8, 0)
+
+
+@pytest.mark.parametrize("n_seq,Hq,Hkv,max_len", [(64, 32, 8, 32768), (64, 32, 1, 32768), (1, 8, 8, 100),
+                                                  (4, 64, 1, 5000), (512, 32, 8, 4096)])
+def test_decode_chunk_choice(n_seq, Hq, Hkv, max_len):
+    """Chunks are a power of two in [128, 1024]; the batch splits into at least 8192 work units
+    unless the chunk is already at its floor, and a chunk twice as long would not."""
+    chunk, n = af.decode_plan(n_seq, Hq, Hkv, max_len)
+    assert chunk in (128, 256, 512, 1024) and n == math.ceil(max_len / chunk)
+    units = lambda c: n_seq * Hkv * math.ceil(Hq // Hkv / 32) * math.ceil(max_len / c)
+    assert units(chunk) >= 8192 or chunk == 128
+    if chunk < 1024:
+        assert units(2 * chunk) < 8192
 
 
 # --------------------------------------------------------------------------------------------

@@ -224,14 +224,14 @@ def test_named_decode(name):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("Hkv", [8, 2, 1])
 def test_decode_chunk_edges(Hkv, d):
-    chunk, _ = af.decode_plan(10)
+    chunk, _ = af.decode_plan(10, 8, Hkv, 2 * 1024 + 3)
     lens = [1, chunk - 1, chunk, chunk + 1, 0, 2 * chunk + 3, 5, 33, 31, 32]
     decode_case(lens, 8, Hkv, d, seed=1000 + Hkv + d)
 
 
 @pytest.mark.parametrize("W", [1, 31, 100, 600, 5000])
 def test_decode_window(W):
-    chunk, _ = af.decode_plan(10)
+    chunk, _ = af.decode_plan(5, 8, 2, 3 * 1024 + 1)
     lens = [1, 50, chunk + 7, 3 * chunk + 1, 2000]
     decode_case(lens, 8, 2, 128, window=W, seed=1100 + W)
 
@@ -284,3 +284,25 @@ def test_decode_matches_prefill_last_row():
     torch.cuda.synchronize()
     diff = (o_dec[0].float() - o_pref[0, :, L - 1].float()).abs().max().item()
     assert diff <= 2e-2
+
+
+@pytest.mark.parametrize("Lk", [65, 129, 1000, 4097])
+@pytest.mark.parametrize("d", [64, 128])
+def test_reads_stay_inside_k_and_v(Lk, d):
+    """K and V sit directly in front of NaN-filled memory; a kernel reading rows past Lk (for
+    the last head, whose rows end the tensor) would turn O into NaN through 0 * NaN."""
+    B, Hq, Hkv, Lq = 1, 4, 2, 77
+    say(f"tail reads Lk{Lk} d{d}")
+    q, k, v = wl.prefill_inputs(B, Hq, Hkv, Lq, Lk, d, seed=1700 + Lk, device="cpu")
+
+    def fenced(t):
+        store = torch.full((t.numel() + 128 * d,), float("nan"), dtype=t.dtype, device=DEV)
+        view = store[: t.numel()].view(t.shape)
+        view.copy_(t.to(DEV))
+        return view
+
+    kk, vv = fenced(k), fenced(v)
+    for causal in (False, True):
+        o, lse = run_fwd(q.to(DEV), kk, vv, causal, 0, 1.0 / math.sqrt(d))
+        O_ref, L_ref = oracle.attention(to64(q), to64(k), to64(v), scale=1.0 / math.sqrt(d), causal=causal)
+        check(to64(o), O_ref, lse.cpu().numpy(), L_ref, "bf16", f"fenced Lk{Lk} d{d} causal{causal}")
