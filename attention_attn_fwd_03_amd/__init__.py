@@ -165,8 +165,32 @@ def fwd_schedule(B, Hq, Hkv, Lq, Lk, d, causal=False, window=0, f32=False) -> np
     return out
 
 
-def decode_plan(n_seq: int, Hq: int, Hkv: int, max_len: int) -> tuple[int, int]:
-    """(keys per chunk, number of chunks) the decode pass uses for these sizes."""
-    c, n = ctypes.c_int32(), ctypes.c_int32()
-    _check(lib().attn_decode_plan(int(n_seq), int(Hq), int(Hkv), int(max_len), ctypes.byref(c), ctypes.byref(n)))
-    return c.value, n.value
+def decode_plan(n_seq: int, Hq: int, Hkv: int, d: int) -> tuple[int, int]:
+    """(teams, rows per sequence) of the decode split on the current device."""
+    t, r = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().attn_decode_plan(int(n_seq), int(Hq), int(Hkv), int(d), ctypes.byref(t), ctypes.byref(r)))
+    return t.value, r.value
+
+
+def decode_pieces(lens, teams: int, window: int = 0, max_len: int | None = None, pool_rows: int | None = None,
+                  offsets=None) -> list[tuple[int, int, int, int]]:
+    """The (team, sequence, first block, blocks) pieces of one row of the decode split, in the
+    order the split computes them (host-side restatement of the plan for tests and tools)."""
+    nb = []
+    for s, n in enumerate(lens):
+        n = int(n)
+        ok = n >= 0 and (max_len is None or n <= max_len)
+        if offsets is not None:
+            ok = ok and int(offsets[s]) >= 0 and (pool_rows is None or int(offsets[s]) + n <= pool_rows)
+        vis = min(n, window) if (window > 0 and n > window) else n
+        nb.append((vis + 31) // 32 if ok else 0)
+    total = sum(nb)
+    share = -(-total // teams) if total else 0
+    out, p = [], 0
+    for s, b in enumerate(nb):
+        if b:
+            for t in range(p // share, (p + b - 1) // share + 1):
+                lo, hi = max(p, t * share), min(p + b, (t + 1) * share)
+                out.append((t, s, lo - p, hi - lo))
+        p += b
+    return out

@@ -97,7 +97,7 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
 
 size_t attn_decode_workspace_size(int n_seq, int Hq, int Hkv, int d, int max_len) {
   if (n_seq <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_len < 1 || (d != 64 && d != 128)) return 0;
-  return decode_workspace_bytes(n_seq, Hq, Hkv, d, max_len);
+  return decode_workspace_layout(n_seq, Hq, Hkv, d).total;
 }
 
 int attn_decode(const void* q, const void* k_pool, const void* v_pool, const int64_t* offsets,
@@ -112,13 +112,18 @@ int attn_decode(const void* q, const void* k_pool, const void* v_pool, const int
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
   if (n_seq > 65535) return ATTN_ERR_SHAPE;
   const int group = Hq / Hkv;
-  const int hblocks = decode_head_blocks(group);
-  if ((int64_t)Hkv * hblocks > 65535) return ATTN_ERR_SHAPE;
+  const int rows = decode_rows_per_seq(Hkv, group);
+  if (rows > 65535) return ATTN_ERR_SHAPE;
   // one sequence's rows of one head are addressed with 32-bit byte offsets
   if ((int64_t)max_len * Hkv * d * 2 >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
-  const size_t need = decode_workspace_bytes(n_seq, Hq, Hkv, d, max_len);
-  if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  // block counts summed over the batch are kept in 32 bits
+  if ((int64_t)n_seq * ((max_len + kDecodeBlockKeys - 1) / kDecodeBlockKeys) >= (int64_t)1 << 30)
+    return ATTN_ERR_SHAPE;
+  const DecWorkspaceLayout lay = decode_workspace_layout(n_seq, Hq, Hkv, d);
+  if (workspace == nullptr || workspace_bytes < lay.total) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_UNSUPPORTED;
+  const int workers = decode_workers(d);
+  if (workers <= 0) return ATTN_ERR_HIP;
 
   DecArgs a;
   a.q = q;
@@ -128,17 +133,22 @@ int attn_decode(const void* q, const void* k_pool, const void* v_pool, const int
   a.lens = lens;
   a.o = o;
   a.lse = lse;
-  a.ws = static_cast<float*>(workspace);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  a.ws_share = reinterpret_cast<int*>(ws + lay.share);
+  a.ws_prefix = reinterpret_cast<int*>(ws + lay.prefix);
+  a.ws_ml = reinterpret_cast<float*>(ws + lay.ml);
+  a.ws_o = reinterpret_cast<float*>(ws + lay.o);
   a.pool_rows = pool_rows;
   a.n_seq = n_seq;
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.group = group;
-  a.hblocks = hblocks;
+  a.hblocks = decode_head_blocks(group);
   a.max_len = max_len;
   a.window = window;
-  a.chunk_keys = decode_chunk_keys(n_seq, Hkv * hblocks, max_len);
-  a.n_chunks = decode_num_chunks(max_len, a.chunk_keys);
+  a.rows = rows;
+  a.nh = decode_heads_per_block(group);
+  a.teams = decode_teams(workers, rows);
   set_scale(scale, a.c, a.qmode);
   const hipError_t e = launch_decode(a, d, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -204,11 +214,14 @@ int attn_fwd_schedule(int B, int Hq, int Hkv, int Lq, int Lk, int d, int causal,
   return ATTN_OK;
 }
 
-int attn_decode_plan(int n_seq, int Hq, int Hkv, int max_len, int32_t* chunk_keys, int32_t* num_chunks) {
-  if (!chunk_keys || !num_chunks) return ATTN_ERR_NULL;
-  if (n_seq <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_len < 1) return ATTN_ERR_SHAPE;
-  *chunk_keys = decode_chunk_keys(n_seq, Hkv * decode_head_blocks(Hq / Hkv), max_len);
-  *num_chunks = decode_num_chunks(max_len, *chunk_keys);
+int attn_decode_plan(int n_seq, int Hq, int Hkv, int d, int32_t* teams, int32_t* rows_per_seq) {
+  if (!teams || !rows_per_seq) return ATTN_ERR_NULL;
+  if (n_seq <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  const int workers = decode_workers(d);
+  if (workers <= 0) return ATTN_ERR_HIP;
+  *rows_per_seq = decode_rows_per_seq(Hkv, Hq / Hkv);
+  *teams = decode_teams(workers, *rows_per_seq);
   return ATTN_OK;
 }
 

@@ -28,12 +28,25 @@ struct DecArgs {
   const int32_t* lens;
   void* o;
   float* lse;
-  float* ws;  // per-chunk partials: O [n_seq][Hq][n_chunks][d], then (m, l) [n_seq][Hq][n_chunks][2]
+  // Workspace regions (see decode_workspace_layout): the blocks-per-team share, the exclusive
+  // prefix of per-sequence block counts, and the partials' (m, l) and unnormalised O.
+  int* ws_share;
+  int* ws_prefix;
+  float* ws_ml;
+  float* ws_o;
   int64_t pool_rows;
-  int n_seq, Hq, Hkv, group, hblocks, max_len, window, n_chunks, chunk_keys;
+  int n_seq, Hq, Hkv, group, hblocks, max_len, window;
+  int rows;   // rows per sequence: Hkv * hblocks
+  int nh;     // query heads per row slot: min(group, 32)
+  int teams;  // teams of `rows` workers in the split launch
   float c;
   int qmode;
 };
+
+struct DecWorkspaceLayout {
+  size_t share, prefix, ml, o, total;  // byte offsets of each region, and the size
+};
+DecWorkspaceLayout decode_workspace_layout(int n_seq, int Hq, int Hkv, int d);
 
 int prefill_block_q(bool f32);
 int prefill_block_k(bool f32);
@@ -41,7 +54,7 @@ int prefill_threads(bool f32);
 int prefill_lds_bytes(bool f32, int d);
 hipError_t launch_prefill(const FwdArgs& a, bool f32, int d, hipStream_t stream);
 
-size_t decode_workspace_bytes(int n_seq, int Hq, int Hkv, int d, int max_len);
+int decode_workers(int d);  // one resident round of split workers on the current device, or < 0
 hipError_t launch_decode(const DecArgs& a, int d, hipStream_t stream);
 
 }  // namespace attnfwd

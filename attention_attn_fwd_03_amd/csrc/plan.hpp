@@ -101,19 +101,31 @@ ATTN_HD PrefillTile prefill_tile(int bid, int B, int Hq, int group, int n_qt, in
 
 ATTN_HD int prefill_heads_per_xcd(int B, int Hq) { return (B * Hq) % 8 == 0 ? (B * Hq) / 8 : 0; }
 
-// Decode: each workgroup handles one chunk of keys of one (sequence, KV head, block of up to 32
-// query heads); a second pass merges the chunks.
+// Decode work decomposition.  A "row" is (sequence, KV head, block of up to 32 query heads that
+// share it); U = Hkv * head_blocks rows per sequence, all with the sequence's number of 32-key
+// blocks.  The launch holds `teams` teams of U single-wave workers.  The blocks of all sequences,
+// concatenated in sequence order, are cut into `teams` equal shares of q = ceil(T / teams)
+// blocks (T = total blocks of one row per sequence, summed); team t takes share t and its
+// member u runs row u of every sequence the share touches.  A (team, sequence) pair produces at
+// most one partial per row, stored in slot (t + s) * U + u: consecutive sequences' team ranges
+// overlap in at most one team, so slots never collide and at most U * (teams + n_seq) exist.
+constexpr int kDecodeBlockKeys = 32;
+constexpr int kDecodeMaxWorkers = 2048;  // workers per launch, at most (one resident round)
+
 ATTN_HD int decode_head_blocks(int group) { return (group + 31) / 32; }
-
-// Keys per chunk: the largest power of two in [128, 1024] that still gives about 8192 work units
-// at the longest sequence (units = n_seq * KV heads * head blocks * chunks), so that every CU
-// has work, while long chunks keep the number of partials small.
-ATTN_HD int decode_chunk_keys(int n_seq, int units_per_chunk_row, int max_len) {
-  int ck = 1024;
-  while (ck > 128 && (long long)n_seq * units_per_chunk_row * ((max_len + ck - 1) / ck) < 8192) ck /= 2;
-  return ck;
+ATTN_HD int decode_heads_per_block(int group) { return group < 32 ? group : 32; }
+ATTN_HD int decode_rows_per_seq(int Hkv, int group) { return Hkv * decode_head_blocks(group); }
+ATTN_HD int decode_teams(int workers, int rows_per_seq) {
+  const int t = workers / rows_per_seq;
+  return t > 0 ? t : 1;
 }
-
-ATTN_HD int decode_num_chunks(int max_len, int chunk_keys) { return (max_len + chunk_keys - 1) / chunk_keys; }
+// Keys the query of a sequence with n cached tokens sees: all of them, or the last `window`.
+ATTN_HD int decode_visible_keys(int n, int window) { return window > 0 && n > window ? window : n; }
+ATTN_HD int decode_key_blocks(int n, int window) {
+  return (decode_visible_keys(n, window) + kDecodeBlockKeys - 1) / kDecodeBlockKeys;
+}
+ATTN_HD long long decode_max_slots(int n_seq, int rows_per_seq) {
+  return (long long)rows_per_seq * (decode_teams(kDecodeMaxWorkers, rows_per_seq) + n_seq);
+}
 
 }  // namespace attnfwd

@@ -104,6 +104,7 @@ def main():
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="profile helper: run only one half of the step")
+    ap.add_argument("--workload", default=None, help="with --suite: run only this workload")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -250,7 +251,12 @@ def run_suite(args):
         ts = sorted(e[0].elapsed_time(e[1]) for e in ev)
         return ts[len(ts) // 2], ts[0]
 
+    def wanted(name):
+        return args.workload is None or args.workload == name
+
     for name, c in wl.PREFILL.items():
+        if not wanted(name):
+            continue
         q, k, v = wl.prefill_inputs_for(c, device=dev)
         o = torch.empty_like(q)
         lse = torch.empty(q.shape[:3], device=dev, dtype=torch.float32)
@@ -265,6 +271,8 @@ def run_suite(args):
                           "GB/s_algorithmic": round(prefill_bytes(c) / (med * 1e-3) / 1e9, 1)}), flush=True)
         del q, k, v, o, lse
     for name, c in wl.DECODE.items():
+        if not wanted(name):
+            continue
         lens = wl.decode_lens(c.n_seq, c.len_lo, c.len_hi, c.lens_seed)
         max_len = int(lens.max())
         # Several replicas of the pool are rotated so that the 256 MB last-level cache cannot hold the

@@ -88,36 +88,77 @@ def dec(**kw):
     (dict(kp=MISALIGNED), af.ATTN_ERR_UNSUPPORTED),
     (dict(ws=None), af.ATTN_ERR_WORKSPACE), (dict(ws_bytes=16), af.ATTN_ERR_WORKSPACE),
     (dict(max_len=1 << 22, Hkv=8, Hq=8), af.ATTN_ERR_SHAPE),
+    (dict(N=65535, Hq=1, Hkv=1, d=64, max_len=1 << 20), af.ATTN_ERR_SHAPE),
 ])
 def test_decode_rejects_bad_arguments(kw, status):
     assert dec(**kw) == status
 
 
-def test_decode_workspace_size():
-    chunk, n = af.decode_plan(64, 32, 8, 32768)
-    assert n == math.ceil(32768 / chunk)
-    assert af.decode_workspace_size(64, 32, 8, 128, 32768) == 64 * 32 * n * (128 + 2) * 4
-    chunk, n = af.decode_plan(3, 5, 5, 1)
-    assert (chunk, n) == (128, 1)
-    assert af.decode_workspace_size(3, 5, 5, 64, 1) == 3 * 5 * 1 * 66 * 4
+def expected_workspace(n_seq, Hq, Hkv, d):
+    """Partial slots for at most 2048 workers in teams of U = Hkv * ceil(g / 32), plus one team
+    boundary per sequence; each slot holds min(g, 32) heads of (m, l) and d floats of O."""
+    g = Hq // Hkv
+    U = Hkv * math.ceil(g / 32)
+    slots = U * (max(1, 2048 // U) + n_seq)
+    nh = min(g, 32)
+    up = lambda x: -(-x // 256) * 256
+    return 256 + up(4 * (n_seq + 1)) + up(slots * nh * 8) + slots * nh * d * 4
+
+
+@pytest.mark.parametrize("n_seq,Hq,Hkv,d", [(64, 32, 8, 128), (64, 32, 1, 128), (3, 5, 5, 64), (7, 64, 1, 128),
+                                            (1, 96, 2, 64)])
+def test_decode_workspace_size(n_seq, Hq, Hkv, d):
+    assert af.decode_workspace_size(n_seq, Hq, Hkv, d, 10) == expected_workspace(n_seq, Hq, Hkv, d)
+    # independent of max_len
+    assert af.decode_workspace_size(n_seq, Hq, Hkv, d, 1) == af.decode_workspace_size(n_seq, Hq, Hkv, d, 1 << 20)
+
+
+def test_decode_workspace_size_rejects():
     assert af.decode_workspace_size(0, 32, 8, 128, 10) == 0
     assert af.decode_workspace_size(4, 32, 8, 96, 10) == 0
     assert af.decode_workspace_size(4, 32, 7, 128, 10) == 0
-    with pytest.raises(RuntimeError):
-        af.decode_plan(4, 32, 8, 0)
+    assert af.decode_workspace_size(4, 32, 8, 128, 0) == 0
 
 
-@pytest.mark.parametrize("n_seq,Hq,Hkv,max_len", [(64, 32, 8, 32768), (64, 32, 1, 32768), (1, 8, 8, 100),
-                                                  (4, 64, 1, 5000), (512, 32, 8, 4096)])
-def test_decode_chunk_choice(n_seq, Hq, Hkv, max_len):
-    """Chunks are a power of two in [128, 1024]; the batch splits into at least 8192 work units
-    unless the chunk is already at its floor, and a chunk twice as long would not."""
-    chunk, n = af.decode_plan(n_seq, Hq, Hkv, max_len)
-    assert chunk in (128, 256, 512, 1024) and n == math.ceil(max_len / chunk)
-    units = lambda c: n_seq * Hkv * math.ceil(Hq // Hkv / 32) * math.ceil(max_len / c)
-    assert units(chunk) >= 8192 or chunk == 128
-    if chunk < 1024:
-        assert units(2 * chunk) < 8192
+@pytest.mark.parametrize("teams", [1, 3, 128, 1024])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_decode_pieces_partition_the_blocks(teams, seed):
+    """The split's pieces (restated on the host) cover every block of every sequence that is
+    read exactly once, give each team at most ceil(T / teams) blocks, and map each
+    (team, sequence) pair to a distinct slot (t + s) below teams + n_seq."""
+    rng = np.random.default_rng(seed)
+    n_seq = int(rng.integers(1, 80))
+    lens = rng.integers(0, 3000, n_seq)
+    lens[rng.random(n_seq) < 0.2] = 0
+    lens[rng.random(n_seq) < 0.1] = int(rng.integers(1, 33))
+    window = int(rng.choice([0, 0, 100, 1000]))
+    pieces = af.decode_pieces(lens, teams, window=window)
+    vis = [min(int(n), window) if (window and n > window) else int(n) for n in lens]
+    nb = [-(-v // 32) for v in vis]
+    total = sum(nb)
+    share = -(-total // teams)
+    covered = {}
+    per_team = {}
+    for t, s, b0, cnt in pieces:
+        assert 0 <= t < teams and cnt > 0 and 0 <= b0 and b0 + cnt <= nb[s]
+        for b in range(b0, b0 + cnt):
+            assert (s, b) not in covered
+            covered[(s, b)] = t
+        per_team[t] = per_team.get(t, 0) + cnt
+    assert len(covered) == total
+    assert all(v <= share for v in per_team.values())
+    slots = [t + s for t, s, _, _ in pieces]
+    assert len(set(slots)) == len(slots) and max(slots, default=0) < teams + n_seq
+    # a team's pieces follow the concatenated order: within a team, sequences increase
+    for t in per_team:
+        ss = [s for tt, s, _, _ in pieces if tt == t]
+        assert ss == sorted(ss)
+
+
+def test_decode_pieces_skip_sequences_not_read():
+    pieces = af.decode_pieces([64, 100, 32], teams=2, max_len=90)
+    assert {s for _, s, _, _ in pieces} == {0, 2}
+    assert sum(c for _, _, _, c in pieces) == 3
 
 
 # --------------------------------------------------------------------------------------------

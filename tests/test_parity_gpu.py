@@ -221,18 +221,51 @@ def test_named_decode(name):
     say(name, stats)
 
 
+def edge_lens(n_seq, share_blocks):
+    """Lengths that put team boundaries at, just before and just after sequence boundaries and
+    inside the last partial block, mixed with empty and one-token sequences."""
+    base = [1, 31, 32, 33, 0, 64, 5, 100]
+    lens = []
+    for i in range(n_seq):
+        if i % 3 == 0:
+            lens.append(share_blocks * 32 - (i % 5))  # a share's worth of keys, give or take a few
+        else:
+            lens.append(base[i % len(base)])
+    return lens
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("Hkv", [8, 2, 1])
-def test_decode_chunk_edges(Hkv, d):
-    chunk, _ = af.decode_plan(10, 8, Hkv, 2 * 1024 + 3)
-    lens = [1, chunk - 1, chunk, chunk + 1, 0, 2 * chunk + 3, 5, 33, 31, 32]
-    decode_case(lens, 8, Hkv, d, seed=1000 + Hkv + d)
+def test_decode_split_edges(Hkv, d):
+    """Lengths chosen against the actual split: the batch holds about `teams` shares, so pieces
+    start and end on every kind of boundary, including single-block pieces."""
+    Hq = 8
+    teams, rows = af.decode_plan(40, Hq, Hkv, d)
+    lens = edge_lens(40, 3)
+    total = sum(-(-n // 32) for n in lens)
+    # scale the long sequences so that the total is a few blocks per team
+    target = 3 * teams
+    k = max(1, target // max(total, 1))
+    lens = [n * k if n > 100 else n for n in lens]
+    say(f"split edges: teams {teams} rows {rows} total blocks {sum(-(-n // 32) for n in lens)}")
+    decode_case(lens, Hq, Hkv, d, seed=1000 + Hkv + d)
+
+
+def test_decode_one_long_sequence_over_all_teams():
+    """One sequence long enough that every team takes a share of it, next to tiny ones."""
+    teams, _ = af.decode_plan(3, 8, 2, 128)
+    lens = [5, teams * 32 * 2 + 17, 1]
+    decode_case(lens, 8, 2, 128, seed=1050)
+
+
+def test_decode_more_teams_than_blocks():
+    """Fewer blocks than teams: most teams get no work; every block is still computed."""
+    decode_case([1, 40, 3], 8, 8, 128, seed=1060)
 
 
 @pytest.mark.parametrize("W", [1, 31, 100, 600, 5000])
 def test_decode_window(W):
-    chunk, _ = af.decode_plan(5, 8, 2, 3 * 1024 + 1)
-    lens = [1, 50, chunk + 7, 3 * chunk + 1, 2000]
+    lens = [1, 50, 1031, 3 * 1024 + 1, 2000]
     decode_case(lens, 8, 2, 128, window=W, seed=1100 + W)
 
 
