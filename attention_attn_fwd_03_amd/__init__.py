@@ -54,7 +54,7 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_plan.restype = i32
     L.attn_fwd_schedule.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, i64]
     L.attn_fwd_schedule.restype = i32
-    L.attn_decode_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    L.attn_decode_plan.argtypes = [i32, i32, i32, i32] + [ctypes.POINTER(ctypes.c_int32)] * 3
     L.attn_decode_plan.restype = i32
     _lib = L
     return L
@@ -165,15 +165,16 @@ def fwd_schedule(B, Hq, Hkv, Lq, Lk, d, causal=False, window=0, f32=False) -> np
     return out
 
 
-def decode_plan(n_seq: int, Hq: int, Hkv: int, d: int) -> tuple[int, int]:
-    """(teams, rows per sequence) of the decode split on the current device."""
-    t, r = ctypes.c_int32(), ctypes.c_int32()
-    _check(lib().attn_decode_plan(int(n_seq), int(Hq), int(Hkv), int(d), ctypes.byref(t), ctypes.byref(r)))
-    return t.value, r.value
+def decode_plan(n_seq: int, Hq: int, Hkv: int, d: int) -> tuple[int, int, int]:
+    """(teams, rows per sequence, tokens per block) of the decode split on the current device."""
+    t, r, b = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().attn_decode_plan(int(n_seq), int(Hq), int(Hkv), int(d), ctypes.byref(t), ctypes.byref(r),
+                                  ctypes.byref(b)))
+    return t.value, r.value, b.value
 
 
-def decode_pieces(lens, teams: int, window: int = 0, max_len: int | None = None, pool_rows: int | None = None,
-                  offsets=None) -> list[tuple[int, int, int, int]]:
+def decode_pieces(lens, teams: int, tokens_per_block: int = 32, window: int = 0, max_len: int | None = None,
+                  pool_rows: int | None = None, offsets=None) -> list[tuple[int, int, int, int]]:
     """The (team, sequence, first block, blocks) pieces of one row of the decode split, in the
     order the split computes them (host-side restatement of the plan for tests and tools)."""
     nb = []
@@ -183,7 +184,7 @@ def decode_pieces(lens, teams: int, window: int = 0, max_len: int | None = None,
         if offsets is not None:
             ok = ok and int(offsets[s]) >= 0 and (pool_rows is None or int(offsets[s]) + n <= pool_rows)
         vis = min(n, window) if (window > 0 and n > window) else n
-        nb.append((vis + 31) // 32 if ok else 0)
+        nb.append(-(-vis // tokens_per_block) if ok else 0)
     total = sum(nb)
     share = -(-total // teams) if total else 0
     out, p = [], 0

@@ -112,12 +112,13 @@ int attn_decode(const void* q, const void* k_pool, const void* v_pool, const int
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
   if (n_seq > 65535) return ATTN_ERR_SHAPE;
   const int group = Hq / Hkv;
-  const int rows = decode_rows_per_seq(Hkv, group);
+  const int rows = decode_rows_per_seq(Hq, Hkv);
+  const int tpb = decode_tokens_per_block(Hq, Hkv);
   if (rows > 65535) return ATTN_ERR_SHAPE;
   // one sequence's rows of one head are addressed with 32-bit byte offsets
   if ((int64_t)max_len * Hkv * d * 2 >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
   // block counts summed over the batch are kept in 32 bits
-  if ((int64_t)n_seq * ((max_len + kDecodeBlockKeys - 1) / kDecodeBlockKeys) >= (int64_t)1 << 30)
+  if ((int64_t)n_seq * ((max_len + tpb - 1) / tpb) >= (int64_t)1 << 30)
     return ATTN_ERR_SHAPE;
   const DecWorkspaceLayout lay = decode_workspace_layout(n_seq, Hq, Hkv, d);
   if (workspace == nullptr || workspace_bytes < lay.total) return ATTN_ERR_WORKSPACE;
@@ -146,8 +147,10 @@ int attn_decode(const void* q, const void* k_pool, const void* v_pool, const int
   a.hblocks = decode_head_blocks(group);
   a.max_len = max_len;
   a.window = window;
+  a.pack = decode_pack(Hq, Hkv);
+  a.tpb = tpb;
   a.rows = rows;
-  a.nh = decode_heads_per_block(group);
+  a.nh = decode_heads_per_slot(Hq, Hkv);
   a.teams = decode_teams(workers, rows);
   set_scale(scale, a.c, a.qmode);
   const hipError_t e = launch_decode(a, d, reinterpret_cast<hipStream_t>(stream));
@@ -214,13 +217,15 @@ int attn_fwd_schedule(int B, int Hq, int Hkv, int Lq, int Lk, int d, int causal,
   return ATTN_OK;
 }
 
-int attn_decode_plan(int n_seq, int Hq, int Hkv, int d, int32_t* teams, int32_t* rows_per_seq) {
-  if (!teams || !rows_per_seq) return ATTN_ERR_NULL;
+int attn_decode_plan(int n_seq, int Hq, int Hkv, int d, int32_t* teams, int32_t* rows_per_seq,
+                     int32_t* tokens_per_block) {
+  if (!teams || !rows_per_seq || !tokens_per_block) return ATTN_ERR_NULL;
   if (n_seq <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   const int workers = decode_workers(d);
   if (workers <= 0) return ATTN_ERR_HIP;
-  *rows_per_seq = decode_rows_per_seq(Hkv, Hq / Hkv);
+  *rows_per_seq = decode_rows_per_seq(Hq, Hkv);
+  *tokens_per_block = decode_tokens_per_block(Hq, Hkv);
   *teams = decode_teams(workers, *rows_per_seq);
   return ATTN_OK;
 }

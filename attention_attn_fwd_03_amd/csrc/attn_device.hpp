@@ -160,13 +160,32 @@ __device__ __forceinline__ void exp_block_f32(const f32x16& s, float c, float mb
 }
 
 // How Q enters the kernels: as given, with its sign flipped (negative scale, run as |scale|), or
-// as zeros (scale = 0, run with c = 1).  All three are exact.
+// as zeros (scale = 0, run with c = 1).  All three are exact.  The mode is applied branch-free as
+// (w & keep) ^ flip, so the loads that feed it are not split up by control flow.
 enum QMode : int { kQAsIs = 0, kQNegate = 1, kQZero = 2 };
 
-// Q fragment word with the mode applied.
-__device__ __forceinline__ u32x4 q_word(u32x4 w, int qmode) {
-  if (qmode == kQZero) return u32x4{0u, 0u, 0u, 0u};
-  return qmode == kQNegate ? (w ^ 0x80008000u) : w;
+struct QTransform {
+  unsigned keep, flip;
+};
+__device__ __forceinline__ QTransform q_transform(int qmode) {
+  QTransform t;
+  t.keep = qmode == kQZero ? 0u : 0xFFFFFFFFu;
+  t.flip = qmode == kQNegate ? 0x80008000u : 0u;
+  return t;
+}
+
+// Q fragment word with the mode applied; `valid` false gives zeros (a row or head past the end).
+__device__ __forceinline__ u32x4 q_word(u32x4 w, QTransform t, bool valid) {
+  const unsigned keep = valid ? t.keep : 0u;
+  return (w & keep) ^ (valid ? t.flip : 0u);
+}
+
+// Read-only view of a buffer that stays constant for the whole kernel: a load through it at a
+// wave-uniform address becomes a scalar load, which is not counted with the vector loads in
+// flight and so never makes the wave wait for them.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T* kernel_constant(const T* p) {
+  return (const __attribute__((address_space(4))) T*)p;
 }
 
 }  // namespace attnfwd

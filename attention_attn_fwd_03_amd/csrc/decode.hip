@@ -33,13 +33,12 @@ typedef __attribute__((address_space(3))) void lds_void_d;
 
 template <int D>
 struct DecCfg {
-  static constexpr int BKD = kDecodeBlockKeys;  // keys per block
   static constexpr int ROWB = D * 2;            // bytes of one head's K or V row
   static constexpr int CH = D / 8;              // 16-byte chunks per row
   static constexpr int KPB = ROWB + 16;         // K row pitch in LDS: A-operand reads of 16 rows hit distinct banks
   static constexpr int VPB = ROWB + 64;         // V row pitch: transposed reads of 4 rows hit distinct banks
-  static constexpr int K_STAGE = (BKD * KPB + 1023) / 1024 * 1024;
-  static constexpr int V_STAGE = BKD * VPB;
+  static constexpr int K_STAGE = (kDecodeBlockRows * KPB + 1023) / 1024 * 1024;
+  static constexpr int V_STAGE = kDecodeBlockRows * VPB;
   static constexpr int K_LOADS = K_STAGE / 1024;  // wave-wide 16-byte-per-lane loads per stage
   static constexpr int V_LOADS = V_STAGE / 1024;
   static_assert(V_STAGE % 1024 == 0, "a V stage must be whole wave-wide loads");
@@ -54,11 +53,11 @@ __device__ __forceinline__ bool decode_seq_valid(const DecArgs& a, int n, int64_
   return n >= 0 && n <= a.max_len && base >= 0 && base + n <= a.pool_rows;
 }
 
-// 32-key blocks of one row of sequence s; 0 for a sequence that is not read (invalid or empty).
-__device__ __forceinline__ int seq_blocks(const DecArgs& a, int s) {
+// Blocks of one row of sequence s; 0 for a sequence that is not read (invalid or empty).
+__device__ __forceinline__ int seq_blocks(const DecArgs& a, int s, int tpb) {
   const int n = a.lens[s];
   const int64_t base = a.offsets[s];
-  return decode_seq_valid(a, n, base) ? decode_key_blocks(n, a.window) : 0;
+  return decode_seq_valid(a, n, base) ? decode_key_blocks(n, a.window, tpb) : 0;
 }
 
 __device__ __forceinline__ int wave_sum_i32(int x) {
@@ -81,14 +80,20 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t x) {
                    (unsigned)__builtin_amdgcn_readfirstlane((int)x));
 }
 
-// Buffer over one KV head of one sequence's keys [k0, end): view byte r * row_bytes + c is byte c
-// of pool row base + k0 + r, head kvh.  Keys at or past `end` read as zeros without touching
-// memory, so a block issued past the end of a piece costs no bandwidth.
+// Buffer over tokens [k0, end) of one sequence, KV heads kvh .. kvh + pack - 1: view byte 0 is
+// head kvh of pool row base + k0, and the view ends after head kvh + pack - 1 of token end - 1.
+// Anything at or past the end reads as zeros without touching memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t seq_rsrc(const void* pool, int64_t base, int k0, int end, int kvh,
-                                                           int Hkv, int rowb) {
-  const unsigned char* p = (const unsigned char*)pool + ((size_t)(base + k0) * Hkv + kvh) * rowb;
+                                                           int Hkv, int pack, int rowb) {
   const int left = end - k0;
-  return __builtin_amdgcn_make_buffer_rsrc((void*)p, 0, left > 0 ? ((left - 1) * Hkv + 1) * rowb : 0, 0x00020000);
+  // Every input is wave-uniform; passing the address and size through readfirstlane keeps the
+  // descriptor in scalar registers whatever registers the compiler chose for its inputs (a
+  // descriptor it cannot prove uniform would be wrapped in a per-lane loop).
+  const uint64_t addr = (uint64_t)pool + ((uint64_t)(base + k0) * Hkv + kvh) * rowb;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)addr);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(addr >> 32));
+  const int bytes = __builtin_amdgcn_readfirstlane(left > 0 ? ((left - 1) * Hkv + pack) * rowb : 0);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), 0, bytes, 0x00020000);
 }
 
 // Cache policy of the K/V stream: non-temporal.  Every cached row is read exactly once per call,
@@ -106,23 +111,28 @@ __device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t rs, unsigned 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_d*)(stage + j * 1024), 16, voff[j], 0, 0, kStreamPolicy);
 }
 
-// Per-lane source offsets of the loads that fill a stage of `rows` rows at pitch PITCH: lane slot
-// o = j*1024 + 16*lane holds row o / PITCH, chunk (o % PITCH) / 16; pad slots take an offset
-// past any buffer (the hardware returns zeros and reads nothing).
-template <int N, int PITCH, int CH>
-__device__ __forceinline__ void stage_offsets(unsigned (&voff)[N], int lane, int rows, int row_bytes) {
+// Per-lane source offsets of the loads that fill a stage of 32 block rows at pitch PITCH: lane
+// slot o = j*1024 + 16*lane holds row r = o / PITCH, chunk (o % PITCH) / 16.  Block row r is
+// token r / pack, KV head r % pack, i.e. byte (r / pack) * token_bytes + (r % pack) * ROWB of the
+// block's buffer.  Pad slots take an offset past any buffer (the hardware returns zeros and
+// reads nothing).
+template <int N, int PITCH, int CH, int ROWB>
+__device__ __forceinline__ void stage_offsets(unsigned (&voff)[N], int lane, int pack, int token_bytes) {
 #pragma unroll
   for (int j = 0; j < N; ++j) {
     const int o = j * 1024 + 16 * lane;
-    const int row = o / PITCH, ch = (o % PITCH) / 16;
-    voff[j] = (row < rows && ch < CH) ? (unsigned)(row * row_bytes + ch * 16) : 0x80000000u;
+    const int r = o / PITCH, ch = (o % PITCH) / 16;
+    voff[j] = (r < kDecodeBlockRows && ch < CH)
+                  ? (unsigned)((r / pack) * token_bytes + (r % pack) * ROWB + ch * 16)
+                  : 0x80000000u;
   }
 }
 
 template <int D>
-__global__ __launch_bounds__(64, 2) void decode_split_kernel(DecArgs a) {
+// At d = 128 the two LDS stages (38 KB) allow four waves per CU, one per SIMD, so the wave may use
+// the whole register file; at d = 64 two waves per SIMD fit.
+__global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecArgs a) {
   using C = DecCfg<D>;
-  constexpr int BKD = C::BKD;
   // Each pipeline stage is its own LDS object, so reading one does not wait for loads into the other.
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[C::K_STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[C::K_STAGE];
@@ -131,85 +141,115 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(DecArgs a) {
 
   const int lane = threadIdx.x, h = lane >> 5, col = lane & 31;
   const int team = blockIdx.x / a.rows, u = blockIdx.x % a.rows;
-  const int kvh = u / a.hblocks, hb = u % a.hblocks;
+  const int pack = a.pack, tpb = a.tpb, pack_log2 = __builtin_ctz((unsigned)a.pack);
+  const int kvh0 = pack > 1 ? 0 : u / a.hblocks;                               // KV head of block row 0
+  const int qbase = pack > 1 ? 0 : kvh0 * a.group + (u % a.hblocks) * 32;      // query head of column 0
   const bool writer = blockIdx.x == 0;  // publishes the share and the prefix for the merge pass
 
-  // Blocks of one row per sequence, summed over the batch; this team's share of them.
-  int total = 0;
-  for (int g = 0; g < a.n_seq; g += 64) {
-    const int s = g + lane;
-    total += wave_sum_i32(s < a.n_seq ? seq_blocks(a, s) : 0);
-  }
-  total = __builtin_amdgcn_readfirstlane(total);
-  const int share = (total + a.teams - 1) / a.teams;
-  const int start = team * share;
-  const int stop = start + share < total ? start + share : total;
-
-  // The sequence holding block `start` and the block's index in it.  The writer stores the
-  // exclusive prefix of block counts on the way.
-  int s_cur = -1, b_cur = 0;
-  if (writer || start < stop) {
-    int run = 0;
+  // ---- This team's share of the blocks: [start, stop) of the concatenated block order. ----
+  int total = 0, s_cur = -1, b_cur = 0, start = 0, stop = 0;
+  if (a.n_seq <= 64) {
+    const int nbv = lane < a.n_seq ? seq_blocks(a, lane, tpb) : 0;
+    const int incl = wave_inclusive_scan(nbv, lane);
+    total = __builtin_amdgcn_readlane(incl, 63);
+    const int share = (total + a.teams - 1) / a.teams;
+    start = team * share;
+    stop = start + share < total ? start + share : total;
+    const int excl = incl - nbv;
+    if (writer) {
+      if (lane < a.n_seq) a.ws_prefix[lane] = excl;
+      if (lane == 0) {
+        a.ws_prefix[a.n_seq] = total;
+        a.ws_share[0] = share;
+      }
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(nbv > 0 && excl <= start && start < excl + nbv);
+    if (start < stop && hit != 0) {
+      const int l = __builtin_ctzll(hit);
+      s_cur = l;
+      b_cur = start - __builtin_amdgcn_readlane(excl, l);
+    }
+  } else {
     for (int g = 0; g < a.n_seq; g += 64) {
       const int s = g + lane;
-      const int nbv = s < a.n_seq ? seq_blocks(a, s) : 0;
-      const int incl = wave_inclusive_scan(nbv, lane);
-      const int excl = run + incl - nbv;
-      if (writer && s < a.n_seq) a.ws_prefix[s] = excl;
-      const uint64_t hit = __builtin_amdgcn_ballot_w64(nbv > 0 && excl <= start && start < excl + nbv);
-      if (s_cur < 0 && hit != 0) {
-        const int l = __builtin_ctzll(hit);
-        s_cur = g + l;
-        b_cur = start - __builtin_amdgcn_readlane(excl, l);
-      }
-      run += __builtin_amdgcn_readlane(incl, 63);
-      if (!writer && s_cur >= 0) break;
+      total += wave_sum_i32(s < a.n_seq ? seq_blocks(a, s, tpb) : 0);
     }
-    if (writer && lane == 0) {
-      a.ws_prefix[a.n_seq] = total;
-      a.ws_share[0] = share;
+    total = __builtin_amdgcn_readfirstlane(total);
+    const int share = (total + a.teams - 1) / a.teams;
+    start = team * share;
+    stop = start + share < total ? start + share : total;
+    if (writer || start < stop) {
+      int run = 0;
+      for (int g = 0; g < a.n_seq; g += 64) {
+        const int s = g + lane;
+        const int nbv = s < a.n_seq ? seq_blocks(a, s, tpb) : 0;
+        const int incl = wave_inclusive_scan(nbv, lane);
+        const int excl = run + incl - nbv;
+        if (writer && s < a.n_seq) a.ws_prefix[s] = excl;
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(nbv > 0 && excl <= start && start < excl + nbv);
+        if (s_cur < 0 && start < stop && hit != 0) {
+          const int l = __builtin_ctzll(hit);
+          s_cur = g + l;
+          b_cur = start - __builtin_amdgcn_readlane(excl, l);
+        }
+        run += __builtin_amdgcn_readlane(incl, 63);
+        if (!writer && s_cur >= 0) break;
+      }
+      if (writer && lane == 0) {
+        a.ws_prefix[a.n_seq] = total;
+        a.ws_share[0] = share;
+      }
     }
   }
   if (start >= stop || s_cur < 0) return;
 
-  const int h0 = kvh * a.group + hb * 32;                          // first query head of this row
-  const int nh = a.group - hb * 32 < 32 ? a.group - hb * 32 : 32;  // query heads in this row
-  const int row_bytes = a.Hkv * C::ROWB;  // bytes between consecutive tokens of one head
-
+  const int token_bytes = a.Hkv * C::ROWB;  // bytes between consecutive tokens of the pool
   unsigned k_voff[C::K_LOADS], v_voff[C::V_LOADS];
-  stage_offsets<C::K_LOADS, C::KPB, C::CH>(k_voff, lane, BKD, row_bytes);
-  stage_offsets<C::V_LOADS, C::VPB, C::CH>(v_voff, lane, BKD, row_bytes);
-  // K A operand: lane holds K[key = col][16*ks + 8*h .. +7] at LDS byte col*KPB + 32*ks + 16*h.
+  stage_offsets<C::K_LOADS, C::KPB, C::CH, C::ROWB>(k_voff, lane, pack, token_bytes);
+  stage_offsets<C::V_LOADS, C::VPB, C::CH, C::ROWB>(v_voff, lane, pack, token_bytes);
+  // K A operand: lane holds K[row = col][16*ks + 8*h .. +7] at LDS byte col*KPB + 32*ks + 16*h.
   const int k_lane = col * C::KPB + h * 16;
   // ds_read_b64_tr_b16 addressing of the V^T operand (see attn_device.hpp).
   const int v_lane = (4 * h + ((lane & 15) >> 2)) * C::VPB + ((lane >> 4) & 1) * 32 + (lane & 3) * 8;
+  // S^T register i of this lane holds block row r(i) = 8*(i/4) + 4*h + i%4 against query head
+  // qbase + col.  In the packed layout only rows of the head's own KV group count.
+  unsigned head_ok = 0xFFFFu;
+  if (pack > 1) {
+    head_ok = 0u;
+    const int g = col / a.group;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (((8 * (i >> 2) + 4 * h + (i & 3)) % pack) == g) head_ok |= 1u << i;
+  }
   const float c = a.c;
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  // After the next block's loads are issued, wait until only they are outstanding: the current
-  // block's stages have then landed (loads complete in issue order).
-  constexpr unsigned kWaitCurrent = vmcnt_at_most(C::K_LOADS + C::V_LOADS);
+  constexpr int QL = D / 16;  // Q loads per lane
+  constexpr unsigned kWaitBlock = vmcnt_at_most(C::K_LOADS + C::V_LOADS);
 
+  const auto* lens_c = kernel_constant(a.lens);
+  const auto* offs_c = kernel_constant(a.offsets);
+  const QTransform qt = q_transform(a.qmode);
+  const bool q_ok = col < a.nh;  // columns past the row's heads read head qbase and are zeroed
+
+  // One piece per iteration: blocks [b, b + take) of sequence s.
   int pos = start, s = s_cur, b = b_cur;
   for (;;) {
-    const int n = __builtin_amdgcn_readfirstlane(a.lens[s]);
-    const int64_t base = uniform_i64(a.offsets[s]);
-    const int nb = decode_key_blocks(n, a.window);  // > 0: the sequence holds block `pos`
+    const int n = lens_c[s];
+    const int64_t base = offs_c[s];
+    const int nb = decode_key_blocks(n, a.window, tpb);  // > 0: the sequence holds block `pos`
     const int take = nb - b < stop - pos ? nb - b : stop - pos;
     const int lo = n - decode_visible_keys(n, a.window);
-    const int k_begin = lo + b * BKD;
-    const int k_end = lo + (b + take) * BKD < n ? lo + (b + take) * BKD : n;
+    const int t_begin = lo + b * tpb;                                       // first token
+    const int t_end = lo + (b + take) * tpb < n ? lo + (b + take) * tpb : n;  // one past the last
 
-    // Query heads as the B operand of S^T = K Q^T (columns beyond nh are zero).
-    bf16x8 qf[D / 16];
+    bf16x8 qf[QL];
     {
-      const unsigned short* Qg = (const unsigned short*)a.q + ((size_t)s * a.Hq + h0 + col) * D;
+      const unsigned short* Qg =
+          (const unsigned short*)a.q + ((size_t)s * a.Hq + qbase + (q_ok ? col : 0)) * D;
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (col < nh) w = *(const u32x4*)(Qg + ks * 16 + h * 8);
-        qf[ks] = __builtin_bit_cast(bf16x8, q_word(w, a.qmode));
-      }
+      for (int ks = 0; ks < QL; ++ks)
+        qf[ks] = __builtin_bit_cast(bf16x8, q_word(*(const u32x4*)(Qg + ks * 16 + h * 8), qt, q_ok));
     }
     f32x16 o[D / 32];
 #pragma unroll
@@ -218,23 +258,35 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(DecArgs a) {
       for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
     RowState st = {-INFINITY, 0.f};
 
-    // Loads of the block starting at key kb0 into stage STAGE.
-    auto issue = [&](int kb0, auto stage_c) {
+    // Loads of the block starting at token t0 into stage STAGE.
+    auto issue = [&](int t0, auto stage_c) {
       constexpr int STAGE = decltype(stage_c)::value;
-      load_to_lds(seq_rsrc(a.k_pool, base, kb0, k_end, kvh, a.Hkv, C::ROWB), STAGE == 0 ? k_lds0 : k_lds1, k_voff);
-      load_to_lds(seq_rsrc(a.v_pool, base, kb0, k_end, kvh, a.Hkv, C::ROWB), STAGE == 0 ? v_lds0 : v_lds1, v_voff);
+      load_to_lds(seq_rsrc(a.k_pool, base, t0, t_end, kvh0, a.Hkv, pack, C::ROWB), STAGE == 0 ? k_lds0 : k_lds1,
+                  k_voff);
+      load_to_lds(seq_rsrc(a.v_pool, base, t0, t_end, kvh0, a.Hkv, pack, C::ROWB), STAGE == 0 ? v_lds0 : v_lds1,
+                  v_voff);
     };
-    // One 32-key block held in stage STAGE.
-    auto block = [&](int kb0, auto stage_c) {
+    // One block (first token t0) held in stage STAGE.
+    auto block = [&](int t0, auto stage_c) {
       constexpr int STAGE = decltype(stage_c)::value;
       const unsigned char* Ks = (STAGE == 0 ? k_lds0 : k_lds1) + k_lane;
       f32x16 sv[1];
 #pragma unroll
       for (int i = 0; i < 16; ++i) sv[0][i] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks)
+      for (int ks = 0; ks < QL; ++ks)
         sv[0] = mfma_32x32x16(__builtin_bit_cast(bf16x8, *(const u32x4*)(Ks + ks * 32)), qf[ks], sv[0]);
-      if (kb0 + BKD > k_end) mask_tile(sv, -(1 << 30), k_end - 1 - (kb0 + 4 * h));  // keys at or past the end
+      if (t0 + tpb > t_end) {  // the piece ends inside this block (only at the sequence's end)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = 8 * (i >> 2) + 4 * h + (i & 3);
+          const bool ok = ((head_ok >> i) & 1u) && t0 + (r >> pack_log2) < t_end;
+          sv[0][i] = ok ? sv[0][i] : -INFINITY;
+        }
+      } else if (pack > 1) {  // rows of other KV groups
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sv[0][i] = ((head_ok >> i) & 1u) ? sv[0][i] : -INFINITY;
+      }
       const float mb = update_max(sv, st, o, c);
       unsigned pk[8];
       exp_block(sv[0], c, mb, st, pk);
@@ -255,22 +307,22 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(DecArgs a) {
 
     // The block after the current one is always issued, even past the piece's end (it then
     // reads nothing), which keeps the loop free of branches around the loads.
-    issue(k_begin, S0{});
-    for (int kb0 = k_begin;; kb0 += 2 * BKD) {
-      issue(kb0 + BKD, S1{});
-      __builtin_amdgcn_s_waitcnt(kWaitCurrent);
-      block(kb0, S0{});
-      if (kb0 + BKD >= k_end) break;
-      issue(kb0 + 2 * BKD, S0{});
-      __builtin_amdgcn_s_waitcnt(kWaitCurrent);
-      block(kb0 + BKD, S1{});
-      if (kb0 + 2 * BKD >= k_end) break;
+    issue(t_begin, S0{});
+    for (int t0 = t_begin;; t0 += 2 * tpb) {
+      issue(t0 + tpb, S1{});
+      __builtin_amdgcn_s_waitcnt(kWaitBlock);
+      block(t0, S0{});
+      if (t0 + tpb >= t_end) break;
+      issue(t0 + 2 * tpb, S0{});
+      __builtin_amdgcn_s_waitcnt(kWaitBlock);
+      block(t0 + tpb, S1{});
+      if (t0 + 2 * tpb >= t_end) break;
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));  // no load may still target LDS past this point
 
     // Partial of this (team, sequence, row): unnormalised O relative to m, plus (m, l).
     const float l_tot = pair_sum(st.l);
-    if (col < nh) {
+    if (q_ok) {
       const size_t idx = ((size_t)(team + s) * a.rows + u) * a.nh + col;
       float* wo = a.ws_o + idx * D;
 #pragma unroll
@@ -287,13 +339,17 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(DecArgs a) {
 
     pos += take;
     if (pos >= stop) break;
-    // The next sequence that holds blocks starts exactly at `pos`.
+    // The next sequence that holds blocks starts exactly at `pos` (it exists while blocks remain
+    // in the share; the bound only guards the lens/offsets reads).
     b = 0;
-    do {
-      ++s;
-    } while (s < a.n_seq && __builtin_amdgcn_readfirstlane(seq_blocks(a, s)) == 0);
+    for (++s; s < a.n_seq; ++s) {
+      const int n2 = lens_c[s];
+      const int64_t base2 = offs_c[s];
+      if (decode_seq_valid(a, n2, base2) && decode_key_blocks(n2, a.window, tpb) > 0) break;
+    }
     if (s >= a.n_seq) break;
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));  // no load may still target LDS past this point
 }
 
 // One 64-lane workgroup per (query head, sequence).  Lane j holds piece j's (m, l) (64 pieces at a
@@ -315,9 +371,12 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
     if (a.lse != nullptr && lane == 0) a.lse[(size_t)s * a.Hq + hq] = NAN;
     return;
   }
-  const int nb = decode_key_blocks(n, a.window);
+  const int nb = decode_key_blocks(n, a.window, a.tpb);
   const int kvh = hq / a.group, within = hq % a.group;
-  const int u = kvh * a.hblocks + within / 32, col = within % 32;
+  // Slot row and column of this query head: one row holding every head in the packed layout,
+  // else row (KV head, block of 32 heads).
+  const int u = a.pack > 1 ? 0 : kvh * a.hblocks + within / 32;
+  const int col = a.pack > 1 ? hq : within % 32;
 
   float M = -INFINITY, L = 0.f;
   float acc[PER];
@@ -377,9 +436,8 @@ template __global__ void decode_merge_kernel<64>(DecArgs);
 template __global__ void decode_merge_kernel<128>(DecArgs);
 
 DecWorkspaceLayout decode_workspace_layout(int n_seq, int Hq, int Hkv, int d) {
-  const int group = Hq / Hkv;
-  const size_t slots = (size_t)decode_max_slots(n_seq, decode_rows_per_seq(Hkv, group));
-  const size_t nh = (size_t)decode_heads_per_block(group);
+  const size_t slots = (size_t)decode_max_slots(n_seq, decode_rows_per_seq(Hq, Hkv));
+  const size_t nh = (size_t)decode_heads_per_slot(Hq, Hkv);
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   DecWorkspaceLayout l;
   l.share = 0;

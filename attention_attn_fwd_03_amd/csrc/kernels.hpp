@@ -36,8 +36,10 @@ struct DecArgs {
   float* ws_o;
   int64_t pool_rows;
   int n_seq, Hq, Hkv, group, hblocks, max_len, window;
-  int rows;   // rows per sequence: Hkv * hblocks
-  int nh;     // query heads per row slot: min(group, 32)
+  int pack;   // KV heads per 32-row block (Hkv in the packed layout, else 1)
+  int tpb;    // tokens per block: 32 / pack
+  int rows;   // rows per sequence (1 in the packed layout, else Hkv * hblocks)
+  int nh;     // query heads per partial slot
   int teams;  // teams of `rows` workers in the split launch
   float c;
   int qmode;

@@ -101,28 +101,43 @@ ATTN_HD PrefillTile prefill_tile(int bid, int B, int Hq, int group, int n_qt, in
 
 ATTN_HD int prefill_heads_per_xcd(int B, int Hq) { return (B * Hq) % 8 == 0 ? (B * Hq) / 8 : 0; }
 
-// Decode work decomposition.  A "row" is (sequence, KV head, block of up to 32 query heads that
-// share it); U = Hkv * head_blocks rows per sequence, all with the sequence's number of 32-key
-// blocks.  The launch holds `teams` teams of U single-wave workers.  The blocks of all sequences,
+// Decode work decomposition.  A block is 32 K (and V) rows, the M dimension of one MFMA tile.
+//  * Packed layout (Hq <= 32 and Hkv divides 32): a block holds P = Hkv heads of 32 / Hkv
+//    consecutive tokens, i.e. 32 consecutive pool rows, and a worker serves every query head of
+//    the sequence; a row of the block only meets the query heads of its own group (the others
+//    are masked).  Each block is one contiguous stretch of the pool, whatever Hkv is.
+//  * Row layout (otherwise): a block holds 32 consecutive tokens of one KV head (P = 1), and a
+//    worker serves one "row" (a KV head and up to 32 of its query heads); U = Hkv * head_blocks
+//    rows per sequence.
+// The launch holds `teams` teams of U single-wave workers.  The blocks of all sequences,
 // concatenated in sequence order, are cut into `teams` equal shares of q = ceil(T / teams)
-// blocks (T = total blocks of one row per sequence, summed); team t takes share t and its
-// member u runs row u of every sequence the share touches.  A (team, sequence) pair produces at
-// most one partial per row, stored in slot (t + s) * U + u: consecutive sequences' team ranges
-// overlap in at most one team, so slots never collide and at most U * (teams + n_seq) exist.
-constexpr int kDecodeBlockKeys = 32;
+// blocks (T = blocks of one row per sequence, summed); team t takes share t and its member u
+// runs row u over every sequence the share touches.  A (team, sequence) pair produces at most
+// one partial per row, stored in slot (t + s) * U + u: consecutive sequences' team ranges overlap
+// in at most one team, so slots never collide and at most U * (teams + n_seq) exist.
+constexpr int kDecodeBlockRows = 32;
 constexpr int kDecodeMaxWorkers = 2048;  // workers per launch, at most (one resident round)
 
 ATTN_HD int decode_head_blocks(int group) { return (group + 31) / 32; }
-ATTN_HD int decode_heads_per_block(int group) { return group < 32 ? group : 32; }
-ATTN_HD int decode_rows_per_seq(int Hkv, int group) { return Hkv * decode_head_blocks(group); }
+// KV heads per block: Hkv in the packed layout, 1 in the row layout.
+ATTN_HD int decode_pack(int Hq, int Hkv) { return (Hq <= 32 && 32 % Hkv == 0) ? Hkv : 1; }
+ATTN_HD int decode_tokens_per_block(int Hq, int Hkv) { return kDecodeBlockRows / decode_pack(Hq, Hkv); }
+ATTN_HD int decode_rows_per_seq(int Hq, int Hkv) {
+  return decode_pack(Hq, Hkv) > 1 ? 1 : Hkv * decode_head_blocks(Hq / Hkv);
+}
+// Query heads per partial slot.
+ATTN_HD int decode_heads_per_slot(int Hq, int Hkv) {
+  const int group = Hq / Hkv;
+  return decode_pack(Hq, Hkv) > 1 ? Hq : (group < 32 ? group : 32);
+}
 ATTN_HD int decode_teams(int workers, int rows_per_seq) {
   const int t = workers / rows_per_seq;
   return t > 0 ? t : 1;
 }
 // Keys the query of a sequence with n cached tokens sees: all of them, or the last `window`.
 ATTN_HD int decode_visible_keys(int n, int window) { return window > 0 && n > window ? window : n; }
-ATTN_HD int decode_key_blocks(int n, int window) {
-  return (decode_visible_keys(n, window) + kDecodeBlockKeys - 1) / kDecodeBlockKeys;
+ATTN_HD int decode_key_blocks(int n, int window, int tokens_per_block) {
+  return (decode_visible_keys(n, window) + tokens_per_block - 1) / tokens_per_block;
 }
 ATTN_HD long long decode_max_slots(int n_seq, int rows_per_seq) {
   return (long long)rows_per_seq * (decode_teams(kDecodeMaxWorkers, rows_per_seq) + n_seq);

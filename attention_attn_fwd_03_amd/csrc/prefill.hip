@@ -128,12 +128,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   // Q rows as the B operand: lane holds Q[q][16*ks + 8*h .. +7] for every ks.
   bf16x8 qf[D / 16];
   {
+    const QTransform qt = q_transform(a.qmode);
+    const bool q_ok = q < a.Lq;
+    const unsigned short* Qr = Qg + (size_t)(q_ok ? q : 0) * D;  // rows past Lq read row 0, then zero
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (q < a.Lq) w = *(const u32x4*)(Qg + (size_t)q * D + ks * 16 + h * 8);
-      qf[ks] = __builtin_bit_cast(bf16x8, q_word(w, a.qmode));
-    }
+    for (int ks = 0; ks < D / 16; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8, q_word(*(const u32x4*)(Qr + ks * 16 + h * 8), qt, q_ok));
   }
 
   f32x16 o[D / 32];

@@ -64,8 +64,8 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
                  int causal, int window, float scale, void* stream);
 
 /* Bytes of device workspace attn_decode needs for these sizes (0 if a size is invalid).  The size
- * does not depend on max_len or on the device; it is about (2048 + Hkv*ceil(g/32)*(n_seq + 1))
- * * min(g, 32) * (d + 2) * 4 bytes for g = Hq / Hkv. */
+ * does not depend on max_len or on the device: with U rows per sequence and H query heads per
+ * row (attn_decode_plan), about U * (2048 / U + n_seq) * H * (d + 2) * 4 bytes. */
 size_t attn_decode_workspace_size(int n_seq, int Hq, int Hkv, int d, int max_len);
 
 /* Decode: one new query token per sequence against its cached keys and values.
@@ -81,7 +81,7 @@ size_t attn_decode_workspace_size(int n_seq, int Hq, int Hkv, int d, int max_len
  * lens < 0, lens > max_len, offsets < 0 or offsets + lens > pool_rows is not read, and its
  * outputs (o rows and lse) are set to NaN.  `stream` must belong to the current device.
  * Work is split evenly over one resident round of workers whatever the mix of lengths (see
- * attn_decode_plan); n_seq * ceil(max_len / 32) must stay below 2^30. */
+ * attn_decode_plan); n_seq * ceil(max_len / tokens_per_block) must stay below 2^30. */
 int attn_decode(const void* q, const void* k_pool, const void* v_pool,
                 const int64_t* offsets, const int32_t* lens, void* o, float* lse,
                 int n_seq, int Hq, int Hkv, int d, int64_t pool_rows, int max_len, int window,
@@ -114,13 +114,17 @@ int attn_fwd_plan(int B, int Hq, int Hkv, int Lq, int Lk, int d, int causal, int
 int attn_fwd_schedule(int B, int Hq, int Hkv, int Lq, int Lk, int d, int causal, int window,
                       int dtype_f32, int32_t* out, int64_t out_len);
 
-/* Decode work split on the current device.  *rows_per_seq = Hkv * ceil((Hq/Hkv) / 32) rows per
- * sequence (a KV head and up to 32 of its query heads); *teams = teams of rows_per_seq
- * single-wave workers launched.  With nb(s) = ceil(visible keys of s / 32) blocks per row
- * (0 for a sequence that is not read) and T = sum of nb(s), the blocks of all sequences laid
- * end to end are cut into shares of ceil(T / teams) blocks; team t computes share t for every
- * row, one partial per (row, sequence) it meets.  ATTN_ERR_HIP without a usable device. */
-int attn_decode_plan(int n_seq, int Hq, int Hkv, int d, int32_t* teams, int32_t* rows_per_seq);
+/* Decode work split on the current device.  A block is 32 rows of K/V: when Hq <= 32 and Hkv
+ * divides 32 it holds all Hkv heads of 32/Hkv consecutive tokens (one contiguous stretch of the
+ * pool; *rows_per_seq = 1 and one worker serves every query head), otherwise 32 tokens of one KV
+ * head (*rows_per_seq = Hkv * ceil((Hq/Hkv) / 32) rows, each a KV head and up to 32 of its query
+ * heads).  *tokens_per_block = 32/Hkv or 32.  *teams = teams of rows_per_seq single-wave
+ * workers launched.  With nb(s) = ceil(visible keys of s / tokens_per_block) blocks per row (0
+ * for a sequence that is not read) and T = sum of nb(s), the blocks of all sequences laid end
+ * to end are cut into shares of ceil(T / teams) blocks; team t computes share t for every row,
+ * one partial per (row, sequence) it meets.  ATTN_ERR_HIP without a usable device. */
+int attn_decode_plan(int n_seq, int Hq, int Hkv, int d, int32_t* teams, int32_t* rows_per_seq,
+                     int32_t* tokens_per_block);
 
 #ifdef __cplusplus
 }

@@ -95,18 +95,21 @@ def test_decode_rejects_bad_arguments(kw, status):
 
 
 def expected_workspace(n_seq, Hq, Hkv, d):
-    """Partial slots for at most 2048 workers in teams of U = Hkv * ceil(g / 32), plus one team
-    boundary per sequence; each slot holds min(g, 32) heads of (m, l) and d floats of O."""
+    """Partial slots for at most 2048 workers in teams of U rows, plus one team boundary per
+    sequence; each slot holds H query heads of (m, l) and d floats of O.  Packed layout (Hq <= 32,
+    Hkv divides 32): U = 1, H = Hq; else U = Hkv * ceil(g / 32), H = min(g, 32)."""
     g = Hq // Hkv
-    U = Hkv * math.ceil(g / 32)
+    if Hq <= 32 and 32 % Hkv == 0:
+        U, nh = 1, Hq
+    else:
+        U, nh = Hkv * math.ceil(g / 32), min(g, 32)
     slots = U * (max(1, 2048 // U) + n_seq)
-    nh = min(g, 32)
     up = lambda x: -(-x // 256) * 256
     return 256 + up(4 * (n_seq + 1)) + up(slots * nh * 8) + slots * nh * d * 4
 
 
 @pytest.mark.parametrize("n_seq,Hq,Hkv,d", [(64, 32, 8, 128), (64, 32, 1, 128), (3, 5, 5, 64), (7, 64, 1, 128),
-                                            (1, 96, 2, 64)])
+                                            (1, 96, 2, 64), (9, 40, 8, 128), (5, 6, 3, 64)])
 def test_decode_workspace_size(n_seq, Hq, Hkv, d):
     assert af.decode_workspace_size(n_seq, Hq, Hkv, d, 10) == expected_workspace(n_seq, Hq, Hkv, d)
     # independent of max_len
@@ -120,9 +123,10 @@ def test_decode_workspace_size_rejects():
     assert af.decode_workspace_size(4, 32, 8, 128, 0) == 0
 
 
+@pytest.mark.parametrize("tpb", [32, 4, 1])
 @pytest.mark.parametrize("teams", [1, 3, 128, 1024])
 @pytest.mark.parametrize("seed", [0, 1, 2])
-def test_decode_pieces_partition_the_blocks(teams, seed):
+def test_decode_pieces_partition_the_blocks(teams, seed, tpb):
     """The split's pieces (restated on the host) cover every block of every sequence that is
     read exactly once, give each team at most ceil(T / teams) blocks, and map each
     (team, sequence) pair to a distinct slot (t + s) below teams + n_seq."""
@@ -132,9 +136,9 @@ def test_decode_pieces_partition_the_blocks(teams, seed):
     lens[rng.random(n_seq) < 0.2] = 0
     lens[rng.random(n_seq) < 0.1] = int(rng.integers(1, 33))
     window = int(rng.choice([0, 0, 100, 1000]))
-    pieces = af.decode_pieces(lens, teams, window=window)
+    pieces = af.decode_pieces(lens, teams, tokens_per_block=tpb, window=window)
     vis = [min(int(n), window) if (window and n > window) else int(n) for n in lens]
-    nb = [-(-v // 32) for v in vis]
+    nb = [-(-v // tpb) for v in vis]
     total = sum(nb)
     share = -(-total // teams)
     covered = {}

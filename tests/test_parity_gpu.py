@@ -240,21 +240,21 @@ def test_decode_split_edges(Hkv, d):
     """Lengths chosen against the actual split: the batch holds about `teams` shares, so pieces
     start and end on every kind of boundary, including single-block pieces."""
     Hq = 8
-    teams, rows = af.decode_plan(40, Hq, Hkv, d)
+    teams, rows, tpb = af.decode_plan(40, Hq, Hkv, d)
     lens = edge_lens(40, 3)
-    total = sum(-(-n // 32) for n in lens)
+    total = sum(-(-n // tpb) for n in lens)
     # scale the long sequences so that the total is a few blocks per team
     target = 3 * teams
     k = max(1, target // max(total, 1))
     lens = [n * k if n > 100 else n for n in lens]
-    say(f"split edges: teams {teams} rows {rows} total blocks {sum(-(-n // 32) for n in lens)}")
+    say(f"split edges: teams {teams} rows {rows} tpb {tpb} total blocks {sum(-(-n // tpb) for n in lens)}")
     decode_case(lens, Hq, Hkv, d, seed=1000 + Hkv + d)
 
 
 def test_decode_one_long_sequence_over_all_teams():
     """One sequence long enough that every team takes a share of it, next to tiny ones."""
-    teams, _ = af.decode_plan(3, 8, 2, 128)
-    lens = [5, teams * 32 * 2 + 17, 1]
+    teams, _, tpb = af.decode_plan(3, 8, 2, 128)
+    lens = [5, teams * tpb * 2 + 17, 1]
     decode_case(lens, 8, 2, 128, seed=1050)
 
 
