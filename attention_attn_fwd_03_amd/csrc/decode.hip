@@ -148,8 +148,16 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
 
   // ---- This team's share of the blocks: [start, stop) of the concatenated block order. ----
   int total = 0, s_cur = -1, b_cur = 0, start = 0, stop = 0;
+  int n_cur = 0;          // length and first pool row of sequence s_cur
+  int64_t base_cur = 0;
   if (a.n_seq <= 64) {
-    const int nbv = lane < a.n_seq ? seq_blocks(a, lane, tpb) : 0;
+    int n_l = 0;
+    int64_t base_l = 0;
+    if (lane < a.n_seq) {
+      n_l = a.lens[lane];
+      base_l = a.offsets[lane];
+    }
+    const int nbv = lane < a.n_seq && decode_seq_valid(a, n_l, base_l) ? decode_key_blocks(n_l, a.window, tpb) : 0;
     const int incl = wave_inclusive_scan(nbv, lane);
     total = __builtin_amdgcn_readlane(incl, 63);
     const int share = (total + a.teams - 1) / a.teams;
@@ -168,6 +176,9 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
       const int l = __builtin_ctzll(hit);
       s_cur = l;
       b_cur = start - __builtin_amdgcn_readlane(excl, l);
+      n_cur = __builtin_amdgcn_readlane(n_l, l);
+      base_cur = (int64_t)(((uint64_t)(unsigned)__builtin_amdgcn_readlane((int)(base_l >> 32), l) << 32) |
+                           (unsigned)__builtin_amdgcn_readlane((int)base_l, l));
     }
   } else {
     for (int g = 0; g < a.n_seq; g += 64) {
@@ -232,11 +243,16 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
   const QTransform qt = q_transform(a.qmode);
   const bool q_ok = col < a.nh;  // columns past the row's heads read head qbase and are zeroed
 
+  if (a.n_seq > 64) {
+    n_cur = lens_c[s_cur];
+    base_cur = offs_c[s_cur];
+  }
+
   // One piece per iteration: blocks [b, b + take) of sequence s.
   int pos = start, s = s_cur, b = b_cur;
+  int n = n_cur;
+  int64_t base = base_cur;
   for (;;) {
-    const int n = lens_c[s];
-    const int64_t base = offs_c[s];
     const int nb = decode_key_blocks(n, a.window, tpb);  // > 0: the sequence holds block `pos`
     const int take = nb - b < stop - pos ? nb - b : stop - pos;
     const int lo = n - decode_visible_keys(n, a.window);
@@ -343,9 +359,9 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
     // in the share; the bound only guards the lens/offsets reads).
     b = 0;
     for (++s; s < a.n_seq; ++s) {
-      const int n2 = lens_c[s];
-      const int64_t base2 = offs_c[s];
-      if (decode_seq_valid(a, n2, base2) && decode_key_blocks(n2, a.window, tpb) > 0) break;
+      n = lens_c[s];
+      base = offs_c[s];
+      if (decode_seq_valid(a, n, base) && decode_key_blocks(n, a.window, tpb) > 0) break;
     }
     if (s >= a.n_seq) break;
   }
@@ -362,8 +378,11 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
   constexpr int PER = D / 64;
   constexpr int MB = 16;
   const int hq = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
+  // Independent loads first: one memory round trip for all of them.
   const int n = a.lens[s];
   const int64_t base = a.offsets[s];
+  const int share = a.ws_share[0];
+  const int p0 = a.ws_prefix[s];
   unsigned short* O = (unsigned short*)a.o + ((size_t)s * a.Hq + hq) * D;
   if (!decode_seq_valid(a, n, base)) {
     const __bf16 nanb = (__bf16)NAN;
@@ -383,34 +402,47 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   if (nb > 0) {
-    const int share = a.ws_share[0];
-    const int p0 = a.ws_prefix[s];
     const int t0 = p0 / share;
     const int np = (p0 + nb - 1) / share - t0 + 1;  // teams whose share meets this sequence
     // Partial index of piece j: slot (t0 + j + s) * rows + u, head col.
     const size_t idx0 = ((size_t)(t0 + s) * a.rows + u) * a.nh + col;
     const size_t step = (size_t)a.rows * a.nh;
     const float* wo0 = a.ws_o + idx0 * D + lane * PER;
-    for (int j = lane; j < np; j += 64) M = fmaxf(M, a.ws_ml[2 * (idx0 + j * step)]);
+    for (int j0 = 0; j0 < np; j0 += 64) {
+      const int cnt = np - j0 < 64 ? np - j0 : 64;
+      // (m, l) of piece j0 + lane, and the O rows of the first MB pieces, in one round trip.
+      float mj = -INFINITY, lj = 0.f;
+      if (lane < cnt) {
+        const size_t idx = idx0 + (size_t)(j0 + lane) * step;
+        mj = a.ws_ml[2 * idx];
+        lj = a.ws_ml[2 * idx + 1];
+      }
+      float ov[MB][PER];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    if (M != -INFINITY) {
-      for (int j0 = 0; j0 < np; j0 += 64) {
-        const int j = j0 + lane;
-        float w = 0.f;
-        if (j < np) {
-          const size_t idx = idx0 + j * step;
-          w = __builtin_amdgcn_exp2f(a.ws_ml[2 * idx] - M);
-          L += w * a.ws_ml[2 * idx + 1];
-        }
-        const int cnt = np - j0 < 64 ? np - j0 : 64;
+      for (int jj = 0; jj < MB; ++jj)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) ov[jj][e] = jj < cnt ? wo0[((size_t)(j0 + jj) * step) * D + e] : 0.f;
+      // Rescale what is accumulated so far to the new maximum, then add these pieces.
+      float Mc = mj;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) Mc = fmaxf(Mc, __shfl_xor(Mc, off));
+      const float Mn = fmaxf(M, Mc);
+      if (Mn != -INFINITY) {
+        const float alpha = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+        L *= alpha;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] *= alpha;
+        M = Mn;
+        const float w = lane < cnt ? __builtin_amdgcn_exp2f(mj - M) : 0.f;
+        L += w * lj;
         for (int jb = 0; jb < cnt; jb += MB) {
-          float ov[MB][PER];
+          if (jb > 0) {
 #pragma unroll
-          for (int jj = 0; jj < MB; ++jj)
+            for (int jj = 0; jj < MB; ++jj)
 #pragma unroll
-            for (int e = 0; e < PER; ++e)
-              ov[jj][e] = jb + jj < cnt ? wo0[((size_t)(j0 + jb + jj) * step) * D + e] : 0.f;
+              for (int e = 0; e < PER; ++e)
+                ov[jj][e] = jb + jj < cnt ? wo0[((size_t)(j0 + jb + jj) * step) * D + e] : 0.f;
+          }
 #pragma unroll
           for (int jj = 0; jj < MB; ++jj) {
             const float wj =
@@ -420,9 +452,9 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
           }
         }
       }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   for (int e = 0; e < PER; ++e) O[lane * PER + e] = __builtin_bit_cast(unsigned short, (__bf16)(acc[e] * inv));
