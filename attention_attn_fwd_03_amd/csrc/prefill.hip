@@ -23,7 +23,6 @@
 //     straddle a boundary are masked.
 #include <hip/hip_runtime.h>
 
-#include <cstdlib>
 #include <type_traits>
 
 #include "attn_device.hpp"
@@ -89,7 +88,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const unsigned short
                                            left * row_bytes, 0x00020000);
 }
 
-template <int D, int BK, int PIPE>
+// Two workgroups share a CU (the two LDS stages of K and V take 74 KB at d = 128), so each SIMD
+// runs two waves, one from each workgroup.
+template <int D, int BK>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   using C = Bf16Cfg<D, BK>;
   constexpr int NB = C::NB;
@@ -113,7 +114,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   using S1 = std::integral_constant<int, 1>;
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: kept in an SGPR
+  // Uniform (kept in an SGPR), and visibly below WAVES, so load guards that always hold fold away.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (C::WAVES - 1);
   const int h = lane >> 5, col = lane & 31;
   const PrefillTile t = prefill_tile(blockIdx.x, a.B, a.Hq, a.group, a.n_qt, a.causal, a.heads_per_xcd);
   const int q_start = t.qt * C::BQ;
@@ -235,67 +237,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     __syncthreads();
   };
 
-  // S-ahead schedule: K runs one tile ahead of V.  In the tile on stage STAGE, S(kt+1) is computed
-  // from the other K stage while the exponentials of S(kt) are formed, so the MFMA pipe has
-  // independent work during the softmax.  K(kt+2) and V(kt+1) load meanwhile.  (On the last tile
-  // the extra S is computed from a stale stage and discarded, which keeps the block branch-free.)
-  auto step_ahead = [&](int kt, auto stage_c, f32x16 (&s_cur)[NB], f32x16 (&s_next)[NB]) {
-    constexpr int STAGE = decltype(stage_c)::value;
-    using Cur = std::integral_constant<int, STAGE>;
-    using Oth = std::integral_constant<int, STAGE ^ 1>;
-    if (kt + 2 <= hi) issue_k(Cur{}, kt + 2);
-    if (kt + 1 <= hi) issue_v(Oth{}, kt + 1);
-    const int k0 = kt * BK;
-    if (!tile_full(k0, q_start, C::BQ, a.Lq, a.Lk, BK, a.causal, a.window)) {
-      int elo, ehi;
-      edge_limits(k0, h, q, a, elo, ehi);
-      mask_tile(s_cur, elo, ehi);
-    }
-    const float mb = update_max(s_cur, st, o, c);
-    qk(Oth{}, s_next);
-#pragma unroll
-    for (int kb = 0; kb < NB; ++kb) {
-      unsigned pk[8];
-      exp_block(s_cur[kb], c, mb, st, pk);
-      const u32x4 pw[2] = {u32x4{pk[0], pk[1], pk[2], pk[3]}, u32x4{pk[4], pk[5], pk[6], pk[7]}};
-      pv(Cur{}, kb, pw);
-    }
-    if constexpr (PIPE == 2) {
-      // Issue order: each S(kt+1) MFMA with its K read and a slice of the exponentials, so the
-      // VALU work sits between MFMAs of this wave; then the P.V MFMAs with their V reads.
-#pragma unroll
-      for (int g = 0; g < NB * (D / 16); ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
-      }
-#pragma unroll
-      for (int g = 0; g < (BK / 16) * (D / 32); ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  };
-
-  if constexpr (PIPE != 0) {
-    if (lo <= hi) {
-      issue_k(S0{}, lo);
-      issue_v(S0{}, lo);
-      if (lo + 1 <= hi) issue_k(S1{}, lo + 1);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      f32x16 sa[NB], sb[NB];
-      qk(S0{}, sa);
-      __syncthreads();  // every wave is done with K(lo) before its stage is refilled
-      for (int kt = lo; kt <= hi; kt += 2) {
-        step_ahead(kt, S0{}, sa, sb);
-        if (kt + 1 <= hi) step_ahead(kt + 1, S1{}, sb, sa);
-      }
-    }
-  } else if (lo <= hi) {
+  if (lo <= hi) {
     issue_k(S0{}, lo);
     issue_v(S0{}, lo);
     __builtin_amdgcn_s_waitcnt(0);
@@ -459,12 +401,8 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------------------------
 
 // Explicit instantiations: the host pass must emit a launch stub for every variant.
-template __global__ void fwd_bf16_kernel<64, 64, 0>(FwdArgs);
-template __global__ void fwd_bf16_kernel<128, 64, 0>(FwdArgs);
-template __global__ void fwd_bf16_kernel<64, 64, 1>(FwdArgs);
-template __global__ void fwd_bf16_kernel<128, 64, 1>(FwdArgs);
-template __global__ void fwd_bf16_kernel<64, 64, 2>(FwdArgs);
-template __global__ void fwd_bf16_kernel<128, 64, 2>(FwdArgs);
+template __global__ void fwd_bf16_kernel<64, 64>(FwdArgs);
+template __global__ void fwd_bf16_kernel<128, 64>(FwdArgs);
 template __global__ void fwd_f32_kernel<64>(FwdArgs);
 template __global__ void fwd_f32_kernel<128>(FwdArgs);
 
@@ -476,15 +414,6 @@ int prefill_lds_bytes(bool f32, int d) {
   return d == 64 ? Bf16Cfg<64, 64>::LDS_BYTES : Bf16Cfg<128, 64>::LDS_BYTES;
 }
 
-// Schedule choice for tuning (ATTNFWD_PREFILL_PIPE=0/1/2), read once.
-static int prefill_schedule() {
-  static const int v = [] {
-    const char* e = getenv("ATTNFWD_PREFILL_PIPE");
-    return e != nullptr ? atoi(e) : 0;
-  }();
-  return v;
-}
-
 hipError_t launch_prefill(const FwdArgs& a, bool f32, int d, hipStream_t stream) {
   const int64_t grid = (int64_t)a.n_qt * a.B * a.Hq;
   const dim3 g((unsigned)grid), b(256);
@@ -492,19 +421,8 @@ hipError_t launch_prefill(const FwdArgs& a, bool f32, int d, hipStream_t stream)
     if (d == 64) hipLaunchKernelGGL(fwd_f32_kernel<64>, g, b, 0, stream, a);
     else hipLaunchKernelGGL(fwd_f32_kernel<128>, g, b, 0, stream, a);
   } else {
-    switch (prefill_schedule()) {
-      case 1:
-        if (d == 64) hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, 1>), g, b, 0, stream, a);
-        else hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, 1>), g, b, 0, stream, a);
-        break;
-      case 2:
-        if (d == 64) hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, 2>), g, b, 0, stream, a);
-        else hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, 2>), g, b, 0, stream, a);
-        break;
-      default:
-        if (d == 64) hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, 0>), g, b, 0, stream, a);
-        else hipLaunchKernelGGL((fwd_bf16_kernel<128, 64, 0>), g, b, 0, stream, a);
-    }
+    if (d == 64) hipLaunchKernelGGL((fwd_bf16_kernel<64, 64>), g, b, 0, stream, a);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<128, 64>), g, b, 0, stream, a);
   }
   return hipGetLastError();
 }

@@ -14,13 +14,22 @@ on, over the timed steps.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
   python bench.py --suite        # one JSON line per workload (all five), for the tables
   python bench.py --copy-calib   # a plain device copy of known size, to scale HBM counters
+  python bench.py --summarize-counters FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
+                                 # rocprofv3 --pmc outputs -> per-launch HBM bytes (profiles/hbm_traffic.md)
+
+The roofline "traffic" fields come from profiles/hbm_traffic.md (FETCH_SIZE / WRITE_SIZE counter
+runs of this same command, scaled by what the counters read for a plain copy of known size); they
+are reported only while the kernel sources still hash to what was profiled, and are null otherwise.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -73,6 +82,66 @@ def decode_flops(n_tokens: int, Hq: int, Hkv: int, d: int) -> int:
     return 4 * d * n_tokens * Hq
 
 
+# ---- HBM traffic from counter runs -------------------------------------------------------------
+
+KERNEL_SOURCES = ["attn_device.hpp", "kernels.hpp", "plan.hpp", "prefill.hip", "decode.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "attention_attn_fwd_03_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_means(path: str) -> dict:
+    """rocprofv3 --pmc CSV -> {kernel name: mean counter value per dispatch}."""
+    vals = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir) -> dict:
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE of the attention kernels, scaled to bytes with the
+    factors a 1 GiB device copy (--copy-calib) gives for the same counters."""
+    def load(d):
+        return _counter_means(os.path.join(d, "run_counter_collection.csv"))
+    fetch, write = load(fetch_dir), load(write_dir)
+    cf, cw = load(copy_fetch_dir), load(copy_write_dir)
+    copy_bytes = 1 << 30
+    # true bytes per counted byte (the counters report KiB)
+    f_scale = copy_bytes / (max(cf.values()) * 1024)
+    w_scale = copy_bytes / (max(cw.values()) * 1024)
+    out = {"kernel_source_sha": kernel_source_hash(), "fetch_scale": round(f_scale, 4),
+           "write_scale": round(w_scale, 4), "kernels": {}}
+    for name in sorted(set(fetch) | set(write)):
+        if "attnfwd::" not in name:
+            continue
+        short = re.sub(r"^void attnfwd::|\(attnfwd::\w+\)$", "", name)
+        fb, wb = fetch.get(name, 0.0) * 1024 * f_scale, write.get(name, 0.0) * 1024 * w_scale
+        out["kernels"][short] = {"FETCH_SIZE_KiB": round(fetch.get(name, 0.0), 1),
+                                 "WRITE_SIZE_KiB": round(write.get(name, 0.0), 1),
+                                 "read_bytes": int(fb), "write_bytes": int(wb), "traffic_bytes": int(fb + wb)}
+    return out
+
+
+def load_traffic() -> dict | None:
+    """The committed counter summary, if it was taken on the kernel sources as they are now."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    data = json.loads(m.group(1))
+    return data if data.get("kernel_source_sha") == kernel_source_hash() else None
+
+
 # ---- timing helpers ---------------------------------------------------------------------------
 
 def _events(n):
@@ -105,7 +174,13 @@ def main():
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="profile helper: run only one half of the step")
     ap.add_argument("--workload", default=None, help="with --suite: run only this workload")
+    ap.add_argument("--summarize-counters", nargs=4, metavar="DIR", default=None,
+                    help="rocprofv3 --pmc output dirs: FETCH_SIZE, WRITE_SIZE, and both for --copy-calib")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(*args.summarize_counters), indent=1))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the attention kernels here run on a single device and this "
@@ -223,6 +298,15 @@ def main():
                             "kernels": "decode_split_kernel<128> + decode_merge_kernel<128>",
                             "per_launch": f"{dbytes / 1e9:.3f} GB (one read of live K/V rows + q, O, LSE)"},
     }
+    traffic = load_traffic()
+    if traffic is not None:
+        kp = traffic["kernels"].get("fwd_bf16_kernel<128, 64>")
+        ks = traffic["kernels"].get("decode_split_kernel<128>")
+        km = traffic["kernels"].get("decode_merge_kernel<128>")
+        if kp:
+            line["roofline"]["traffic"] = kp["traffic_bytes"]
+        if ks and km:
+            line["roofline_decode"]["traffic"] = ks["traffic_bytes"] + km["traffic_bytes"]
     if not args.no_cpu_baseline and do_pre:
         print("# timing the oracle on the host", file=sys.stderr, flush=True)
         cb = cpu_baseline(cp, q.cpu(), k.cpu(), v.cpu())
