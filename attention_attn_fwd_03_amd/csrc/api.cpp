@@ -179,7 +179,7 @@ int attn_fwd_plan(int B, int Hq, int Hkv, int Lq, int Lk, int d, int causal, int
   const int st = check_fwd(p, p, p, p, nullptr, B, Hq, Hkv, Lq, Lk, d, causal, window, 1.0f);
   if (st != ATTN_OK) return st;
   const bool f32 = dtype_f32 != 0;
-  const int bq = prefill_block_q(f32), bk = prefill_block_k(f32);
+  const int bq = prefill_block_q(f32), bk = prefill_block_k(f32, d);
   out->block_q = bq;
   out->block_k = bk;
   out->threads = prefill_threads(f32);

@@ -51,7 +51,7 @@ struct DecWorkspaceLayout {
 DecWorkspaceLayout decode_workspace_layout(int n_seq, int Hq, int Hkv, int d);
 
 int prefill_block_q(bool f32);
-int prefill_block_k(bool f32);
+int prefill_block_k(bool f32, int d);
 int prefill_threads(bool f32);
 int prefill_lds_bytes(bool f32, int d);
 hipError_t launch_prefill(const FwdArgs& a, bool f32, int d, hipStream_t stream);

@@ -11,7 +11,8 @@
 //   [LLM-Attn] "LLM中的Attention实现及优化": GQA shares one K/V head among consecutive query
 //              heads (repeat_kv semantics, but the copy is never made).
 //
-// Design (one workgroup = 4 waves = 128 query rows of one (batch, query head)):
+// Design (one workgroup = 4 waves = 128 query rows of one (batch, query head); three workgroups
+// share a CU, so each SIMD runs three waves):
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: K (A operand) from LDS, Q (B operand) held in
 //     registers for the whole key loop.  Computing the transpose puts one query row per lane
 //     (rows = keys), so a row's max and sum need one exchange between lanes l and l ^ 32.
@@ -40,7 +41,8 @@ struct Bf16Cfg {
   // reads (16 consecutive rows, one chunk each) hit 16 distinct slots; V rows sit 64 bytes apart,
   // so a transposed read (4 consecutive rows x 64 bytes per half-wave) covers the bank space once.
   static constexpr int KPB = ROWB + 16, VPB = ROWB + 64;
-  static constexpr int K_TILE = BK * KPB, V_TILE = BK * VPB;  // LDS bytes per stage
+  // LDS bytes per stage, rounded up to whole wave-wide loads (the rows past BK are never read).
+  static constexpr int K_TILE = (BK * KPB + 1023) / 1024 * 1024, V_TILE = (BK * VPB + 1023) / 1024 * 1024;
   static constexpr int K_LOADS = (K_TILE + 1023) / 1024;      // wave-wide 16-byte loads per tile
   static constexpr int V_LOADS = (V_TILE + 1023) / 1024;
   static constexpr int KL_PER_WAVE = (K_LOADS + WAVES - 1) / WAVES;
@@ -88,10 +90,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const unsigned short
                                            left * row_bytes, 0x00020000);
 }
 
-// Two workgroups share a CU (the two LDS stages of K and V take 74 KB at d = 128), so each SIMD
-// runs two waves, one from each workgroup.
+// Three workgroups share a CU: each SIMD runs three waves, one from each.  That needs at most
+// 168 VGPRs and 53 KB of LDS per workgroup, which is why d = 128 walks the keys in tiles of 32
+// (two stages of K and V take 38 KB; tiles of 64 would take 74 KB) and d = 64 in tiles of 64 (42 KB).
 template <int D, int BK>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(FwdArgs a) {
   using C = Bf16Cfg<D, BK>;
   constexpr int NB = C::NB;
   // Two K stages and two V stages, filled straight from global memory by buffer loads while the
@@ -251,20 +254,36 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   // ---- epilogue: O = acc / l (bf16, round to nearest even), LSE in natural log ----
   const float l_tot = pair_sum(st.l);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (q < a.Lq) {
-    unsigned short* Og = (unsigned short*)a.o + ((size_t)(t.b * a.Hq + t.hq) * a.Lq + q) * D;
+  // O leaves through LDS so that each store instruction writes whole rows: the accumulator layout
+  // gives every lane 8 bytes of one row, four times per 32 columns.  All LDS stages are free here
+  // (the last step ended with a barrier and no loads in flight); each wave stages its 32 rows in
+  // a stage of its own.
+  constexpr int OPB = D * 2 + 8;  // LDS row pitch of the staged O tile
+  static_assert(32 * OPB <= C::K_TILE && 32 * OPB <= C::V_TILE, "a stage holds one wave's O tile");
+  unsigned char* ot = wave == 0 ? k_lds0 : wave == 1 ? k_lds1 : wave == 2 ? v_lds0 : v_lds1;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2 w = {pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv),
-                         pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv)};
-        *(u32x2*)(Og + dt * 32 + g * 8 + h * 4) = w;
-      }
-    if (a.lse != nullptr && h == 0)
-      a.lse[(size_t)(t.b * a.Hq + t.hq) * a.Lq + q] =
-          l_tot > 0.f ? (st.m + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+    for (int g = 0; g < 4; ++g) {
+      const u32x2 w = {pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv),
+                       pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv)};
+      *(u32x2*)(ot + col * OPB + (dt * 32 + g * 8 + h * 4) * 2) = w;
+    }
+  // The reads see the writes above: LDS executes one wave's instructions in order.  Each
+  // wave-wide read takes 16 bytes per lane, RPI whole rows.
+  constexpr int RPI = 1024 / (D * 2);
+  const int r_in = lane / (D / 8), chunk = lane % (D / 8);
+  unsigned short* Oh = (unsigned short*)a.o + ((size_t)(t.b * a.Hq + t.hq) * a.Lq) * D;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + r_in;
+    const u32x4 w = *(const u32x4*)(ot + r * OPB + chunk * 16);
+    const int qr = q_start + wave * 32 + r;
+    if (qr < a.Lq) *(u32x4*)(Oh + (size_t)qr * D + chunk * 8) = w;
   }
+  if (a.lse != nullptr && h == 0 && q < a.Lq)
+    a.lse[(size_t)(t.b * a.Hq + t.hq) * a.Lq + q] =
+        l_tot > 0.f ? (st.m + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -402,16 +421,16 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
 
 // Explicit instantiations: the host pass must emit a launch stub for every variant.
 template __global__ void fwd_bf16_kernel<64, 64>(FwdArgs);
-template __global__ void fwd_bf16_kernel<128, 64>(FwdArgs);
+template __global__ void fwd_bf16_kernel<128, 32>(FwdArgs);
 template __global__ void fwd_f32_kernel<64>(FwdArgs);
 template __global__ void fwd_f32_kernel<128>(FwdArgs);
 
-int prefill_block_q(bool f32) { return f32 ? F32Cfg<64>::BQ : Bf16Cfg<128, 64>::BQ; }
-int prefill_block_k(bool f32) { return f32 ? F32Cfg<64>::BK : 64; }
+int prefill_block_q(bool f32) { return f32 ? F32Cfg<64>::BQ : Bf16Cfg<128, 32>::BQ; }
+int prefill_block_k(bool f32, int d) { return f32 ? F32Cfg<64>::BK : (d == 128 ? 32 : 64); }
 int prefill_threads(bool) { return 256; }
 int prefill_lds_bytes(bool f32, int d) {
   if (f32) return d == 64 ? 2 * F32Cfg<64>::STAGE * 4 : 2 * F32Cfg<128>::STAGE * 4;
-  return d == 64 ? Bf16Cfg<64, 64>::LDS_BYTES : Bf16Cfg<128, 64>::LDS_BYTES;
+  return d == 64 ? Bf16Cfg<64, 64>::LDS_BYTES : Bf16Cfg<128, 32>::LDS_BYTES;
 }
 
 hipError_t launch_prefill(const FwdArgs& a, bool f32, int d, hipStream_t stream) {
@@ -422,7 +441,7 @@ hipError_t launch_prefill(const FwdArgs& a, bool f32, int d, hipStream_t stream)
     else hipLaunchKernelGGL(fwd_f32_kernel<128>, g, b, 0, stream, a);
   } else {
     if (d == 64) hipLaunchKernelGGL((fwd_bf16_kernel<64, 64>), g, b, 0, stream, a);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<128, 64>), g, b, 0, stream, a);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<128, 32>), g, b, 0, stream, a);
   }
   return hipGetLastError();
 }

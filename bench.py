@@ -105,9 +105,37 @@ def _counter_means(path: str) -> dict:
     return {k: sum(v) / len(v) for k, v in vals.items()}
 
 
-def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir) -> dict:
+N_XCD, N_SIMD = 8, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+
+
+def _mfma_counters(path: str) -> dict:
+    """rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES CSV -> per kernel: the fraction of
+    SIMD cycles the matrix core was busy, and the engine clock over the dispatch.  GRBM_GUI_ACTIVE
+    comes summed over the XCDs (each counts the kernel's cycles); SQ_VALU_MFMA_BUSY_CYCLES summed
+    over every SIMD."""
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = per.setdefault(r["Kernel_Name"], {}).setdefault(r["Dispatch_Id"], {})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+            d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    out = {}
+    for name, ds in per.items():
+        ds = [d for d in ds.values() if "GRBM_GUI_ACTIVE" in d and "SQ_VALU_MFMA_BUSY_CYCLES" in d]
+        if not ds:
+            continue
+        cyc = sum(d["GRBM_GUI_ACTIVE"] for d in ds) / len(ds) / N_XCD
+        busy = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in ds) / len(ds) / N_SIMD
+        ns = sum(d["ns"] for d in ds) / len(ds)
+        out[name] = {"dispatches": len(ds), "mfma_busy_frac": round(busy / cyc, 4),
+                     "engine_clock_ghz": round(cyc / ns, 3), "mean_us": round(ns / 1e3, 1)}
+    return out
+
+
+def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, mfma_dir=None) -> dict:
     """Per-dispatch FETCH_SIZE / WRITE_SIZE of the attention kernels, scaled to bytes with the
-    factors a 1 GiB device copy (--copy-calib) gives for the same counters."""
+    factors a 1 GiB device copy (--copy-calib) gives for the same counters; with `mfma_dir`, also
+    the matrix-core busy fraction and engine clock of each kernel."""
     def load(d):
         return _counter_means(os.path.join(d, "run_counter_collection.csv"))
     fetch, write = load(fetch_dir), load(write_dir)
@@ -118,6 +146,7 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir) -> 
     w_scale = copy_bytes / (max(cw.values()) * 1024)
     out = {"kernel_source_sha": kernel_source_hash(), "fetch_scale": round(f_scale, 4),
            "write_scale": round(w_scale, 4), "kernels": {}}
+    mfma = _mfma_counters(os.path.join(mfma_dir, "run_counter_collection.csv")) if mfma_dir else {}
     for name in sorted(set(fetch) | set(write)):
         if "attnfwd::" not in name:
             continue
@@ -126,6 +155,8 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir) -> 
         out["kernels"][short] = {"FETCH_SIZE_KiB": round(fetch.get(name, 0.0), 1),
                                  "WRITE_SIZE_KiB": round(write.get(name, 0.0), 1),
                                  "read_bytes": int(fb), "write_bytes": int(wb), "traffic_bytes": int(fb + wb)}
+        if name in mfma:
+            out["kernels"][short].update(mfma[name])
     return out
 
 
@@ -174,11 +205,14 @@ def main():
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="profile helper: run only one half of the step")
     ap.add_argument("--workload", default=None, help="with --suite: run only this workload")
-    ap.add_argument("--summarize-counters", nargs=4, metavar="DIR", default=None,
-                    help="rocprofv3 --pmc output dirs: FETCH_SIZE, WRITE_SIZE, and both for --copy-calib")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR", default=None,
+                    help="rocprofv3 --pmc output dirs: FETCH_SIZE, WRITE_SIZE, both for --copy-calib, "
+                         "and optionally a GRBM_GUI_ACTIVE + SQ_VALU_MFMA_BUSY_CYCLES pass")
     args = ap.parse_args()
 
     if args.summarize_counters:
+        if len(args.summarize_counters) not in (4, 5):
+            ap.error("--summarize-counters takes 4 or 5 directories")
         print(json.dumps(summarize_counters(*args.summarize_counters), indent=1))
         return
 
@@ -291,7 +325,7 @@ def main():
         },
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "fwd_bf16_kernel<128,64>",
+                     "kernel": "fwd_bf16_kernel<128,32>",
                      "per_launch": f"{pflops / 1e9:.1f} GFLOP useful (4*d per visible pair, 64 heads)"},
         "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None,
@@ -300,11 +334,14 @@ def main():
     }
     traffic = load_traffic()
     if traffic is not None:
-        kp = traffic["kernels"].get("fwd_bf16_kernel<128, 64>")
+        kp = traffic["kernels"].get("fwd_bf16_kernel<128, 32>")
         ks = traffic["kernels"].get("decode_split_kernel<128>")
         km = traffic["kernels"].get("decode_merge_kernel<128>")
         if kp:
             line["roofline"]["traffic"] = kp["traffic_bytes"]
+            for key in ("mfma_busy_frac", "engine_clock_ghz"):
+                if key in kp:
+                    line["roofline"]["counters_" + key] = kp[key]
         if ks and km:
             line["roofline_decode"]["traffic"] = ks["traffic_bytes"] + km["traffic_bytes"]
     if not args.no_cpu_baseline and do_pre:

@@ -33,3 +33,26 @@ def test_gpus_above_one_is_refused():
     import sys
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_mfma_counter_summary(tmp_path):
+    """GRBM_GUI_ACTIVE arrives summed over the 8 XCDs and SQ_VALU_MFMA_BUSY_CYCLES over the 1024
+    SIMDs; the summary divides both back and averages over dispatches."""
+    import csv
+    path = tmp_path / "run_counter_collection.csv"
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    rows = []
+    # two dispatches of 100 us: 180k and 200k cycles per XCD, matrix core busy 90k / 120k per SIMD
+    for disp, cyc, busy, t0 in ((1, 180_000, 90_000, 0), (2, 200_000, 120_000, 1_000_000)):
+        for name, val in (("GRBM_GUI_ACTIVE", cyc * 8), ("SQ_VALU_MFMA_BUSY_CYCLES", busy * 1024)):
+            rows.append({"Dispatch_Id": disp, "Kernel_Name": "k", "Counter_Name": name, "Counter_Value": val,
+                         "Start_Timestamp": t0, "End_Timestamp": t0 + 100_000})
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=cols)
+        w.writeheader()
+        w.writerows(rows)
+    m = bench._mfma_counters(str(path))["k"]
+    assert m["dispatches"] == 2
+    assert m["mfma_busy_frac"] == round(105_000 / 190_000, 4)
+    assert m["engine_clock_ghz"] == round(190_000 / 100_000, 3)
+    assert m["mean_us"] == 100.0

@@ -214,12 +214,16 @@ def test_plan_skips_the_causal_upper_triangle():
     """Causal L=4096: about half of the dense tiles are never visited ("注意力机制深度优化"
     §一.2 claims the skip saves work; here the saving is exact)."""
     info = af.fwd_plan(2, 32, 8, 4096, 4096, 128, True, 0)
-    dense = info["num_q_tiles"] * math.ceil(4096 / info["block_k"])
-    assert info["tiles_per_head"] == sum(2 * (i + 1) for i in range(32))  # BQ = 2 BK
+    bq, bk = info["block_q"], info["block_k"]
+    assert bq % bk == 0
+    dense = info["num_q_tiles"] * math.ceil(4096 / bk)
+    # query tile i sees keys [0, (i + 1) * bq): (i + 1) * bq / bk tiles
+    assert info["tiles_per_head"] == sum((bq // bk) * (i + 1) for i in range(4096 // bq))
     assert info["tiles_per_head"] / dense < 0.52
-    # with the 4k window at 16k only the band around the diagonal is visited
+    # with the 4k window at 16k only the band around the diagonal is visited: a query tile
+    # touches at most window + bq consecutive keys, so (4096 + bq) / bk + 1 tiles
     info = af.fwd_plan(1, 32, 8, 16384, 16384, 128, True, 4096)
-    assert info["tiles_per_head"] <= 128 * (4096 // 64 + 3)
+    assert info["tiles_per_head"] <= info["num_q_tiles"] * ((4096 + bq) // bk + 1)
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,L,causal", [(2, 32, 8, 4096, True), (4, 16, 16, 1024, False),
