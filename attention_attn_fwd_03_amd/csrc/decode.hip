@@ -492,6 +492,7 @@ int decode_workers(int d) {
   const hipError_t e = d == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<128>, 64, 0)
                                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<64>, 64, 0);
   if (e != hipSuccess || cus <= 0 || per_cu <= 0) return -1;
+  if (per_cu > kDecodeWorkersPerCu) per_cu = kDecodeWorkersPerCu;
   w = cus * per_cu < kDecodeMaxWorkers ? cus * per_cu : kDecodeMaxWorkers;
   slot.store(w, std::memory_order_relaxed);
   return w;
