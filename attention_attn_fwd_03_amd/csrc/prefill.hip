@@ -209,6 +209,9 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(FwdArgs a) {
     }
   };
   const int lo = kr.kt_lo, hi = kr.kt_hi;
+  const int w_start = q_start + wave * 32;  // this wave's rows: [w_start, w_start + 32)
+  const KeyRange wkr = key_range(w_start, 32, a.Lq, a.Lk, BK, a.causal, a.window);
+  const int w_lo = wkr.kt_lo, w_hi = wkr.kt_hi;
   // One tile on stage `stage` (a compile-time constant after the unroll below): start the loads of
   // tile kt+1 into the other stage, S = K Q^T, mask (edge tiles only), the online softmax of S,
   // O += P V, then wait for the loads and synchronise.
@@ -220,21 +223,25 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(FwdArgs a) {
       issue_k(Oth{}, kt + 1);
       issue_v(Oth{}, kt + 1);
     }
-    f32x16 sc[NB];
-    qk(Cur{}, sc);
-    const int k0 = kt * BK;
-    if (!tile_full(k0, q_start, C::BQ, a.Lq, a.Lk, BK, a.causal, a.window)) {
-      int elo, ehi;
-      edge_limits(k0, h, q, a, elo, ehi);
-      mask_tile(sc, elo, ehi);
-    }
-    const float mb = update_max(sc, st, o, c);
+    // A wave skips tiles that no row of its own 32 sees (above its diagonal, before its window);
+    // skipping equals running them fully masked.  Tiles all its rows see fully are not masked.
+    if (kt >= w_lo && kt <= w_hi) {
+      f32x16 sc[NB];
+      qk(Cur{}, sc);
+      const int k0 = kt * BK;
+      if (!tile_full(k0, w_start, 32, a.Lq, a.Lk, BK, a.causal, a.window)) {
+        int elo, ehi;
+        edge_limits(k0, h, q, a, elo, ehi);
+        mask_tile(sc, elo, ehi);
+      }
+      const float mb = update_max(sc, st, o, c);
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb) {
-      unsigned pk[8];
-      exp_block(sc[kb], c, mb, st, pk);
-      const u32x4 pw[2] = {u32x4{pk[0], pk[1], pk[2], pk[3]}, u32x4{pk[4], pk[5], pk[6], pk[7]}};
-      pv(Cur{}, kb, pw);
+      for (int kb = 0; kb < NB; ++kb) {
+        unsigned pk[8];
+        exp_block(sc[kb], c, mb, st, pk);
+        const u32x4 pw[2] = {u32x4{pk[0], pk[1], pk[2], pk[3]}, u32x4{pk[4], pk[5], pk[6], pk[7]}};
+        pv(Cur{}, kb, pw);
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's global->LDS loads have landed
     __syncthreads();
