@@ -17,6 +17,8 @@ Sources (web articles on attention optimisation, cited by title and section):
   [MQA-GQA]  tqpw.cn article on MQA → GQA → FlashAttention: §2.1 MQA shares one K/V over
              all heads; §3.1 uniform GQA grouping; §5.3 tunable sm_scale.
   [Deep-Opt] "注意力机制深度优化" (kler.cn): §一.2 causal mask, upper-right triangle skipped.
+  [FlashMLA] "高效多头潜在注意力解码技术：Flash MLA深度解析" (developer.baidu.com): §3.2
+             performance tuning, paged GPU memory for long sequences.
 
 What it computes (the plain definition, [DS-Attn §一]): for every batch b and query head h,
 with kh = floor(h / (Hq / Hkv)) ([LLM-Attn] repeat_kv copies each KV head to consecutive
@@ -229,6 +231,49 @@ def decode(q, k_pool, v_pool, offsets, lens, scale: float | None = None, window:
         start, n_tok = int(offsets[s]), int(lens[s])
         kseq = _f64(k_pool[start:start + n_tok])      # [n_tok, Hkv, d]
         vseq = _f64(v_pool[start:start + n_tok])
+        for h in range(Hq):
+            kh = kv_head(h, Hq, Hkv)
+            o, l = attention_head(q[s, h][None, :], kseq[:, kh], vseq[:, kh], scale, True, window)
+            O[n, h], LSE[n, h] = o[0], l[0]
+
+    _run(list(enumerate(seqs)), one, threads)
+    return O, LSE
+
+
+def paged_rows(table_row, n: int, page_size: int) -> np.ndarray:
+    """Pool rows of tokens 0 .. n-1 of one sequence in a paged cache: token t sits at offset
+    t mod page_size of the page listed at index floor(t / page_size) of the sequence's table."""
+    t = np.arange(n)
+    pages = np.asarray(table_row, dtype=np.int64)[t // page_size]
+    return pages * page_size + t % page_size
+
+
+def decode_paged(q, k_pool, v_pool, block_table, lens, page_size: int, scale: float | None = None,
+                 window: int = 0, threads: int | None = None, seqs=None):
+    """decode() over a paged KV cache.
+
+    [LLM-Attn], PagedAttention: the cache is handed out in small fixed-size pieces, so one
+    sequence's keys need not be contiguous; [FlashMLA §3.2]: paged GPU memory for long
+    sequences.  Reading taken for the layout the articles leave open: k_pool and v_pool are
+    [pool_pages * page_size, Hkv, d], physical page p is rows p * page_size ..
+    (p + 1) * page_size - 1, and block_table[s][j] names the page holding tokens
+    j * page_size .. (j + 1) * page_size - 1 of sequence s.  The sequence's keys are gathered
+    in token order and attended exactly as in decode(): the query is the newest token, it sees
+    every key, or only the last W with a window.  Returns O [N, Hq, d], LSE [N, Hq]."""
+    q = np.asarray(q)
+    N, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    seqs = list(range(N)) if seqs is None else [int(s) for s in seqs]
+    O = np.empty((len(seqs), Hq, v_pool.shape[2]))
+    LSE = np.empty((len(seqs), Hq))
+
+    def one(n_s):
+        n, s = n_s
+        rows = paged_rows(block_table[s], int(lens[s]), page_size)
+        kseq = _f64(k_pool[rows])      # [n_tok, Hkv, d], in token order
+        vseq = _f64(v_pool[rows])
         for h in range(Hq):
             kh = kv_head(h, Hq, Hkv)
             o, l = attention_head(q[s, h][None, :], kseq[:, kh], vseq[:, kh], scale, True, window)

@@ -10,6 +10,7 @@ Articles cited (by title and section):
   [LLM-Attn] "LLM中的Attention实现及优化" (zeeklog.com)
   [MQA-GQA]  tqpw.cn article on MQA → GQA → FlashAttention
   [Deep-Opt] "注意力机制深度优化" (kler.cn)
+  [FlashMLA] "高效多头潜在注意力解码技术：Flash MLA深度解析" (developer.baidu.com)
 """
 from __future__ import annotations
 
@@ -338,6 +339,79 @@ def check_pool_addressing(seed=22):
     assert np.all(O3[1] == 0) and np.all(np.isneginf(L3[1]))
 
 
+def paged_pool(kseq, vseq, page_size, n_pages, rng):
+    """Scatter each sequence's rows over pages picked at random from a pool of n_pages (unused
+    pages hold NaN).  Returns the pool and the [N, max pages] table (unused entries -1)."""
+    N = len(kseq)
+    Hkv, d = kseq[0].shape[1], kseq[0].shape[2]
+    need = [-(-len(k) // page_size) for k in kseq]
+    order = rng.permutation(n_pages)[:sum(need)]
+    pk = np.full((n_pages * page_size, Hkv, d), np.nan)
+    pv = np.full((n_pages * page_size, Hkv, d), np.nan)
+    table = np.full((N, max(max(need), 1)), -1, np.int64)
+    used = 0
+    for s in range(N):
+        for j in range(need[s]):
+            page = int(order[used])
+            used += 1
+            table[s, j] = page
+            lo, hi = j * page_size, min((j + 1) * page_size, len(kseq[s]))
+            pk[page * page_size:page * page_size + hi - lo] = kseq[s][lo:hi]
+            pv[page * page_size:page * page_size + hi - lo] = vseq[s][lo:hi]
+    return pk, pv, table
+
+
+def check_paged_matches_contiguous(seed=23):
+    """A paged cache ([LLM-Attn], PagedAttention: the cache in small pieces that need not be
+    contiguous) holds the same keys as a contiguous pool: scattering every sequence over pages
+    in random order, with NaN in unused pages and unused page slots, changes nothing."""
+    rng = _rng(seed)
+    Hq, Hkv, d = 4, 2, 5
+    lens = np.array([1, 7, 8, 13, 0, 21])
+    kseq = [rng.standard_normal((n, Hkv, d)) for n in lens]
+    vseq = [rng.standard_normal((n, Hkv, d)) for n in lens]
+    qd = rng.standard_normal((len(lens), Hq, d))
+    packed_k, packed_v = np.concatenate(kseq), np.concatenate(vseq)
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    for P in (1, 3, 4, 8, 32):
+        pk, pv, table = paged_pool(kseq, vseq, P, int(sum(-(-n // P) for n in lens)) + 3, rng)
+        for W in (0, 1, 5):
+            O1, L1 = oracle.decode(qd, packed_k, packed_v, offs, lens, scale=0.6, window=W)
+            O2, L2 = oracle.decode_paged(qd, pk, pv, table, lens, P, scale=0.6, window=W)
+            assert np.array_equal(O1, O2) and np.array_equal(L1, L2), (P, W)
+            assert np.all(np.isfinite(O2[lens > 0]))
+
+
+def check_paged_brute_force(seed=24):
+    """Pure-Python walk of the page table, page by page: for page slot j of sequence s and
+    offset r inside it, token j * P + r (if it exists) lives in pool row table[s][j] * P + r."""
+    rng = _rng(seed)
+    Hq, Hkv, d, P = 2, 1, 3, 4
+    lens = [3, 9, 4]
+    kseq = [rng.standard_normal((n, Hkv, d)) for n in lens]
+    vseq = [rng.standard_normal((n, Hkv, d)) for n in lens]
+    qd = rng.standard_normal((len(lens), Hq, d))
+    pk, pv, table = paged_pool(kseq, vseq, P, 9, rng)
+    for W in (0, 2):
+        O, LSE = oracle.decode_paged(qd, pk, pv, table, np.array(lens), P, scale=0.8, window=W)
+        for s, n in enumerate(lens):
+            keys = []
+            for j in range(table.shape[1]):
+                for r in range(P):
+                    t = j * P + r
+                    if t < n and (W == 0 or t >= n - W):
+                        keys.append(int(table[s, j]) * P + r)
+            for h in range(Hq):
+                sc = [0.8 * math.fsum(float(qd[s, h, c]) * float(pk[row, 0, c]) for c in range(d)) for row in keys]
+                mx = max(sc)
+                w = [math.exp(x - mx) for x in sc]
+                tot = math.fsum(w)
+                for c in range(d):
+                    ref = math.fsum(wi * float(pv[row, 0, c]) for wi, row in zip(w, keys)) / tot
+                    assert abs(O[s, h, c] - ref) <= 1e-12, (s, h, c, W)
+                assert abs(LSE[s, h] - (mx + math.log(tot))) <= 1e-12, (s, h, W)
+
+
 def check_golden():
     """Hand-derived exact values (tests/golden/worked_example.json)."""
     g = json.load(open(GOLDEN))
@@ -372,4 +446,4 @@ def check_visible_pairs():
 ALL_CHECKS = [check_golden, check_brute_force, check_torch_sdpa, check_softmax_rows, check_constant_scores,
               check_causal_boundary, check_window_convention, check_gqa_mapping, check_pv_invariants,
               check_lse_identity, check_split_merge, check_decode_is_last_row, check_pool_addressing,
-              check_visible_pairs]
+              check_paged_matches_contiguous, check_paged_brute_force, check_visible_pairs]

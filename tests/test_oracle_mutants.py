@@ -88,6 +88,18 @@ def _decode_window_from_start(q, k_pool, v_pool, offsets, lens, scale=None, wind
     return O, L
 
 
+def _paged_rows_unscaled(table_row, n, page_size):
+    # forgot to multiply the page number by the page size
+    t = np.arange(n)
+    return np.asarray(table_row, np.int64)[t // page_size] + t % page_size
+
+
+def _paged_rows_swapped(table_row, n, page_size):
+    # page slot and offset inside the page exchanged
+    t = np.arange(n)
+    return np.asarray(table_row, np.int64)[t % page_size % len(table_row)] * page_size + t // page_size
+
+
 MUTANTS = {
     "gqa_interleaved": ("kv_head", _interleaved_kv_head),
     "window_off_by_one": ("_visibility_rows", _window_one_too_wide),
@@ -99,6 +111,8 @@ MUTANTS = {
     "softmax_not_normalised": ("masked_softmax", "no_normalise"),
     "lse_base2": ("masked_softmax", "log2_lse"),
     "merge_unweighted": ("merge_partials", _merge_unweighted),
+    "paged_rows_unscaled": ("paged_rows", _paged_rows_unscaled),
+    "paged_rows_swapped": ("paged_rows", _paged_rows_swapped),
 }
 
 
