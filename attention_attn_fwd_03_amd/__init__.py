@@ -17,8 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libattnfwd.so")
 
 ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(6)
 
-EXPORTS = ["attn_fwd", "attn_fwd_f32", "attn_decode_workspace_size", "attn_decode", "attn_status_str",
-           "attn_fwd_plan", "attn_fwd_schedule", "attn_decode_plan"]
+EXPORTS = ["attn_fwd", "attn_fwd_f32", "attn_decode_workspace_size", "attn_decode", "attn_decode_paged",
+           "attn_status_str", "attn_fwd_plan", "attn_fwd_schedule", "attn_decode_plan"]
 
 
 class FwdPlanInfo(ctypes.Structure):
@@ -48,6 +48,9 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_workspace_size.restype = sz
     L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, i32, f32, vp, sz, vp]
     L.attn_decode.restype = i32
+    L.attn_decode_paged.argtypes = [vp, vp, vp, vp, i32, i32, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+                                    vp, sz, vp]
+    L.attn_decode_paged.restype = i32
     L.attn_status_str.argtypes = [i32]
     L.attn_status_str.restype = ctypes.c_char_p
     L.attn_fwd_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(FwdPlanInfo)]
@@ -149,6 +152,47 @@ def attn_decode(q, k_pool, v_pool, offsets, lens, *, max_len: int, window: int =
     return (o, lse) if return_lse else o
 
 
+def attn_decode_paged(q, k_pool, v_pool, block_table, lens, *, page_size: int, max_len: int, window: int = 0,
+                      scale: float | None = None, return_lse: bool = False, workspace=None, out=None,
+                      lse_out=None):
+    """Decode one query token per sequence against a paged KV cache.
+
+    q [N, Hq, d] bf16; k_pool, v_pool [pool_pages * page_size, Hkv, d] bf16 (physical page p
+    is rows p * page_size .. + page_size - 1); block_table int32 [N, table_stride] (entry j of
+    sequence s: the page holding its tokens j * page_size .. + page_size - 1); lens int32 [N];
+    max_len >= max(lens).  Returns O [N, Hq, d] bf16 and, when ``return_lse``, LSE [N, Hq]."""
+    import torch
+    _require_gpu(q, k_pool, v_pool, block_table, lens)
+    if q.dtype != torch.bfloat16 or k_pool.dtype != torch.bfloat16 or v_pool.dtype != torch.bfloat16:
+        raise ValueError("decode takes bfloat16 q and pools")
+    if block_table.dtype != torch.int32 or lens.dtype != torch.int32:
+        raise ValueError("block_table and lens must be int32")
+    if block_table.dim() != 2 or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous [N, table_stride] tensor")
+    N, Hq, d = q.shape
+    T, Hkv, dk = k_pool.shape
+    if page_size < 1 or T % page_size != 0:
+        raise ValueError("the pools must hold a whole number of pages")
+    if (dk != d or tuple(v_pool.shape) != tuple(k_pool.shape) or block_table.shape[0] != N
+            or lens.numel() != N):
+        raise ValueError("shape mismatch between q, pools, block_table and lens")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = decode_workspace_size(N, Hq, Hkv, d, max_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    o = torch.empty_like(q) if out is None else out
+    lse = None
+    if return_lse:
+        lse = torch.empty((N, Hq), device=q.device, dtype=torch.float32) if lse_out is None else lse_out
+    _check(lib().attn_decode_paged(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), block_table.data_ptr(),
+                                   int(block_table.shape[1]), int(page_size), T // page_size, lens.data_ptr(),
+                                   o.data_ptr(), lse.data_ptr() if lse is not None else None, N, Hq, Hkv, d,
+                                   int(max_len), int(window), float(scale), workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), _stream()))
+    return (o, lse) if return_lse else o
+
+
 def fwd_plan(B, Hq, Hkv, Lq, Lk, d, causal=False, window=0, f32=False) -> dict:
     info = FwdPlanInfo()
     _check(lib().attn_fwd_plan(B, Hq, Hkv, Lq, Lk, d, int(bool(causal)), int(window), int(bool(f32)),
@@ -174,9 +218,11 @@ def decode_plan(n_seq: int, Hq: int, Hkv: int, d: int) -> tuple[int, int, int]:
 
 
 def decode_pieces(lens, teams: int, tokens_per_block: int = 32, window: int = 0, max_len: int | None = None,
-                  pool_rows: int | None = None, offsets=None) -> list[tuple[int, int, int, int]]:
+                  pool_rows: int | None = None, offsets=None, aligned: bool = False) -> list[tuple[int, int, int, int]]:
     """The (team, sequence, first block, blocks) pieces of one row of the decode split, in the
-    order the split computes them (host-side restatement of the plan for tests and tools)."""
+    order the split computes them (host-side restatement of the plan for tests and tools).
+    ``aligned`` (paged caches): block 0 starts at the tokens_per_block boundary at or below the
+    first visible key instead of at the key itself."""
     nb = []
     for s, n in enumerate(lens):
         n = int(n)
@@ -184,7 +230,10 @@ def decode_pieces(lens, teams: int, tokens_per_block: int = 32, window: int = 0,
         if offsets is not None:
             ok = ok and int(offsets[s]) >= 0 and (pool_rows is None or int(offsets[s]) + n <= pool_rows)
         vis = min(n, window) if (window > 0 and n > window) else n
-        nb.append(-(-vis // tokens_per_block) if ok else 0)
+        org = n - vis
+        if aligned:
+            org -= org % tokens_per_block
+        nb.append(-(-(n - org) // tokens_per_block) if ok and n > org else 0)
     total = sum(nb)
     share = -(-total // teams) if total else 0
     out, p = [], 0

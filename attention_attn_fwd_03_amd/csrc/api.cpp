@@ -100,12 +100,16 @@ size_t attn_decode_workspace_size(int n_seq, int Hq, int Hkv, int d, int max_len
   return decode_workspace_layout(n_seq, Hq, Hkv, d).total;
 }
 
-int attn_decode(const void* q, const void* k_pool, const void* v_pool, const int64_t* offsets,
-                const int32_t* lens, void* o, float* lse, int n_seq, int Hq, int Hkv, int d, int64_t pool_rows,
-                int max_len, int window, float scale, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k_pool || !v_pool || !offsets || !lens || !o) return ATTN_ERR_NULL;
-  if (n_seq <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_len < 1 || window < 0 || pool_rows < 0)
-    return ATTN_ERR_SHAPE;
+}  // extern "C"
+
+namespace {
+
+// Shared by the contiguous and the paged entry points: everything but the addressing of the pool.
+int decode_common(const void* q, const void* k_pool, const void* v_pool, const int32_t* lens, void* o,
+                  float* lse, int n_seq, int Hq, int Hkv, int d, int max_len, int window, float scale,
+                  void* workspace, size_t workspace_bytes, void* stream, DecArgs& a) {
+  if (!q || !k_pool || !v_pool || !lens || !o) return ATTN_ERR_NULL;
+  if (n_seq <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_len < 1 || window < 0) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
@@ -120,17 +124,16 @@ int attn_decode(const void* q, const void* k_pool, const void* v_pool, const int
   // block counts summed over the batch are kept in 32 bits
   if ((int64_t)n_seq * ((max_len + tpb - 1) / tpb) >= (int64_t)1 << 30)
     return ATTN_ERR_SHAPE;
+  if (a.paged && a.page_size % tpb != 0) return ATTN_ERR_UNSUPPORTED;
   const DecWorkspaceLayout lay = decode_workspace_layout(n_seq, Hq, Hkv, d);
   if (workspace == nullptr || workspace_bytes < lay.total) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_UNSUPPORTED;
   const int workers = decode_workers(d);
   if (workers <= 0) return ATTN_ERR_HIP;
 
-  DecArgs a;
   a.q = q;
   a.k_pool = k_pool;
   a.v_pool = v_pool;
-  a.offsets = offsets;
   a.lens = lens;
   a.o = o;
   a.lse = lse;
@@ -139,7 +142,6 @@ int attn_decode(const void* q, const void* k_pool, const void* v_pool, const int
   a.ws_prefix = reinterpret_cast<int*>(ws + lay.prefix);
   a.ws_ml = reinterpret_cast<float*>(ws + lay.ml);
   a.ws_o = reinterpret_cast<float*>(ws + lay.o);
-  a.pool_rows = pool_rows;
   a.n_seq = n_seq;
   a.Hq = Hq;
   a.Hkv = Hkv;
@@ -155,6 +157,46 @@ int attn_decode(const void* q, const void* k_pool, const void* v_pool, const int
   set_scale(scale, a.c, a.qmode);
   const hipError_t e = launch_decode(a, d, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode(const void* q, const void* k_pool, const void* v_pool, const int64_t* offsets,
+                const int32_t* lens, void* o, float* lse, int n_seq, int Hq, int Hkv, int d, int64_t pool_rows,
+                int max_len, int window, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!offsets) return ATTN_ERR_NULL;
+  if (pool_rows < 0) return ATTN_ERR_SHAPE;
+  DecArgs a{};
+  a.offsets = offsets;
+  a.pool_rows = pool_rows;
+  a.paged = 0;
+  return decode_common(q, k_pool, v_pool, lens, o, lse, n_seq, Hq, Hkv, d, max_len, window, scale, workspace,
+                       workspace_bytes, stream, a);
+}
+
+int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                      int table_stride, int page_size, int64_t pool_pages, const int32_t* lens, void* o, float* lse,
+                      int n_seq, int Hq, int Hkv, int d, int max_len, int window, float scale, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (!block_table) return ATTN_ERR_NULL;
+  if (page_size < 1 || pool_pages < 0 || max_len < 1 || table_stride < 1) return ATTN_ERR_SHAPE;
+  // every token a valid sequence may hold has a table entry
+  if ((int64_t)table_stride < ((int64_t)max_len + page_size - 1) / page_size) return ATTN_ERR_SHAPE;
+  if ((int64_t)n_seq * table_stride >= (int64_t)1 << 40) return ATTN_ERR_SHAPE;
+  // one page of one head is addressed with 32-bit byte offsets
+  if ((int64_t)page_size * Hkv * d * 2 >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
+  DecArgs a{};
+  a.offsets = nullptr;
+  a.block_table = block_table;
+  a.table_stride = table_stride;
+  a.page_size = page_size;
+  a.pool_pages = pool_pages;
+  a.pool_rows = pool_pages * page_size;
+  a.paged = 1;
+  return decode_common(q, k_pool, v_pool, lens, o, lse, n_seq, Hq, Hkv, d, max_len, window, scale, workspace,
+                       workspace_bytes, stream, a);
 }
 
 const char* attn_status_str(int status) {

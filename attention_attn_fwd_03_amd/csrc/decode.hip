@@ -18,6 +18,11 @@
 //      K comes back as the MFMA A operand, V transposed through ds_read_b64_tr_b16.
 //   2. decode_merge_kernel: per (sequence, query head), rescales its partials to a common
 //      maximum and writes O (bf16) and the natural-log LSE (fp32).
+// A paged cache ("LLM中的Attention实现及优化", PagedAttention: the cache in small fixed-size pages
+// that need not be contiguous) uses the same two passes; only the split's addressing changes:
+// each block is looked up in the sequence's row of the page table and read from its page (the
+// page size is a multiple of the block's token count, and a sequence's blocks start on a block
+// boundary, so no block straddles two pages).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -49,15 +54,16 @@ struct DecCfg {
 // leaves the LDS/scalar and export counters unconstrained (vmcnt split over bits 3:0 and 15:14).
 constexpr unsigned vmcnt_at_most(unsigned n) { return 0x0F70u | (n & 0xFu) | ((n >> 4) << 14); }
 
-__device__ __forceinline__ bool decode_seq_valid(const DecArgs& a, int n, int64_t base) {
+__device__ __forceinline__ bool decode_seq_valid(const DecArgs& a, int n, int64_t base, bool paged) {
+  if (paged) return n >= 0 && n <= a.max_len;  // page entries are checked as they are read
   return n >= 0 && n <= a.max_len && base >= 0 && base + n <= a.pool_rows;
 }
 
 // Blocks of one row of sequence s; 0 for a sequence that is not read (invalid or empty).
-__device__ __forceinline__ int seq_blocks(const DecArgs& a, int s, int tpb) {
+__device__ __forceinline__ int seq_blocks(const DecArgs& a, int s, int tpb, bool paged) {
   const int n = a.lens[s];
-  const int64_t base = a.offsets[s];
-  return decode_seq_valid(a, n, base) ? decode_key_blocks(n, a.window, tpb) : 0;
+  const int64_t base = paged ? 0 : a.offsets[s];
+  return decode_seq_valid(a, n, base, paged) ? decode_key_blocks(n, a.window, tpb, paged) : 0;
 }
 
 __device__ __forceinline__ int wave_sum_i32(int x) {
@@ -128,7 +134,9 @@ __device__ __forceinline__ void stage_offsets(unsigned (&voff)[N], int lane, int
   }
 }
 
-template <int D>
+// PAGED selects the pool addressing at compile time, so the contiguous kernel carries none of the
+// page-table code.
+template <int D, bool PAGED>
 // At d = 128 the two LDS stages (38 KB) allow four waves per CU, one per SIMD, so the wave may use
 // the whole register file; at d = 64 two waves per SIMD fit.
 __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecArgs a) {
@@ -155,9 +163,10 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
     int64_t base_l = 0;
     if (lane < a.n_seq) {
       n_l = a.lens[lane];
-      base_l = a.offsets[lane];
+      base_l = PAGED ? 0 : a.offsets[lane];
     }
-    const int nbv = lane < a.n_seq && decode_seq_valid(a, n_l, base_l) ? decode_key_blocks(n_l, a.window, tpb) : 0;
+    const int nbv =
+        lane < a.n_seq && decode_seq_valid(a, n_l, base_l, PAGED) ? decode_key_blocks(n_l, a.window, tpb, PAGED) : 0;
     const int incl = wave_inclusive_scan(nbv, lane);
     total = __builtin_amdgcn_readlane(incl, 63);
     const int share = (total + a.teams - 1) / a.teams;
@@ -183,7 +192,7 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
   } else {
     for (int g = 0; g < a.n_seq; g += 64) {
       const int s = g + lane;
-      total += wave_sum_i32(s < a.n_seq ? seq_blocks(a, s, tpb) : 0);
+      total += wave_sum_i32(s < a.n_seq ? seq_blocks(a, s, tpb, PAGED) : 0);
     }
     total = __builtin_amdgcn_readfirstlane(total);
     const int share = (total + a.teams - 1) / a.teams;
@@ -193,7 +202,7 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
       int run = 0;
       for (int g = 0; g < a.n_seq; g += 64) {
         const int s = g + lane;
-        const int nbv = s < a.n_seq ? seq_blocks(a, s, tpb) : 0;
+        const int nbv = s < a.n_seq ? seq_blocks(a, s, tpb, PAGED) : 0;
         const int incl = wave_inclusive_scan(nbv, lane);
         const int excl = run + incl - nbv;
         if (writer && s < a.n_seq) a.ws_prefix[s] = excl;
@@ -245,7 +254,7 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
 
   if (a.n_seq > 64) {
     n_cur = lens_c[s_cur];
-    base_cur = offs_c[s_cur];
+    base_cur = PAGED ? 0 : offs_c[s_cur];
   }
 
   // One piece per iteration: blocks [b, b + take) of sequence s.
@@ -253,20 +262,32 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
   int n = n_cur;
   int64_t base = base_cur;
   for (;;) {
-    const int nb = decode_key_blocks(n, a.window, tpb);  // > 0: the sequence holds block `pos`
+    const int nb = decode_key_blocks(n, a.window, tpb, PAGED);  // > 0: the sequence holds block `pos`
     const int take = nb - b < stop - pos ? nb - b : stop - pos;
-    const int lo = n - decode_visible_keys(n, a.window);
-    const int t_begin = lo + b * tpb;                                       // first token
-    const int t_end = lo + (b + take) * tpb < n ? lo + (b + take) * tpb : n;  // one past the last
+    const int vis_lo = n - decode_visible_keys(n, a.window);           // first visible key
+    const int org = decode_block_origin(n, a.window, tpb, PAGED);       // first token of block 0
+    const int t_begin = org + b * tpb;                                        // first token
+    const int t_end = org + (b + take) * tpb < n ? org + (b + take) * tpb : n;  // one past the last
 
-    bf16x8 qf[QL];
+    // Paged: the table entries of the piece's first 64 pages, lane i holding page slot pg0 + i
+    // (loaded next to Q, one round trip for both); entries past the table row read as -1.
+    int pg0 = 0, pg_win = -1;
+    auto load_window = [&](int j) {
+      pg0 = j;
+      pg_win = j + lane < a.table_stride ? a.block_table[(size_t)s * a.table_stride + j + lane] : -1;
+    };
+    if constexpr (PAGED) load_window(t_begin / a.page_size);
+
+    // Q is loaded raw here and transformed only after the first block's loads are issued (below),
+    // so all its loads are in flight together and the K/V loads start without waiting for them.
+    u32x4 qraw[QL];
     {
       const unsigned short* Qg =
           (const unsigned short*)a.q + ((size_t)s * a.Hq + qbase + (q_ok ? col : 0)) * D;
 #pragma unroll
-      for (int ks = 0; ks < QL; ++ks)
-        qf[ks] = __builtin_bit_cast(bf16x8, q_word(*(const u32x4*)(Qg + ks * 16 + h * 8), qt, q_ok));
+      for (int ks = 0; ks < QL; ++ks) qraw[ks] = *(const u32x4*)(Qg + ks * 16 + h * 8);
     }
+    bf16x8 qf[QL];
     f32x16 o[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -274,12 +295,34 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
       for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
     RowState st = {-INFINITY, 0.f};
 
-    // Loads of the block starting at token t0 into stage STAGE.
+    // Loads of the block starting at token t0 into stage STAGE.  Contiguous pool: a buffer over
+    // the piece's remaining tokens.  Paged pool: the block lies inside one page (t0 is a multiple
+    // of tpb, the page size a multiple of tpb); its entry is looked up and the buffer covers the
+    // block's tokens in that page.  An entry outside [0, pool_pages) reads nothing and marks the
+    // piece bad.  A block past the piece's end reads nothing and looks nothing up.
+    bool bad = false;
     auto issue = [&](int t0, auto stage_c) {
       constexpr int STAGE = decltype(stage_c)::value;
-      load_to_lds(seq_rsrc(a.k_pool, base, t0, t_end, kvh0, a.Hkv, pack, C::ROWB), STAGE == 0 ? k_lds0 : k_lds1,
+      int64_t rbase = base;  // pool row of token 0 of the sequence, as if it were contiguous
+      int end = t_end;
+      if constexpr (PAGED) {
+        rbase = 0;
+        end = t0;
+        if (t0 < t_end) {
+          const int j = t0 / a.page_size;
+          if (j - pg0 >= 64) load_window(j);  // pages are visited in order
+          const int64_t pg = __builtin_amdgcn_readlane(pg_win, j - pg0);
+          if (pg >= 0 && pg < a.pool_pages) {
+            rbase = (pg - j) * a.page_size;  // rbase + t0 = pg * page_size + t0 % page_size
+            end = t0 + tpb < t_end ? t0 + tpb : t_end;
+          } else {
+            bad = true;
+          }
+        }
+      }
+      load_to_lds(seq_rsrc(a.k_pool, rbase, t0, end, kvh0, a.Hkv, pack, C::ROWB), STAGE == 0 ? k_lds0 : k_lds1,
                   k_voff);
-      load_to_lds(seq_rsrc(a.v_pool, base, t0, t_end, kvh0, a.Hkv, pack, C::ROWB), STAGE == 0 ? v_lds0 : v_lds1,
+      load_to_lds(seq_rsrc(a.v_pool, rbase, t0, end, kvh0, a.Hkv, pack, C::ROWB), STAGE == 0 ? v_lds0 : v_lds1,
                   v_voff);
     };
     // One block (first token t0) held in stage STAGE.
@@ -292,11 +335,14 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
 #pragma unroll
       for (int ks = 0; ks < QL; ++ks)
         sv[0] = mfma_32x32x16(__builtin_bit_cast(bf16x8, *(const u32x4*)(Ks + ks * 32)), qf[ks], sv[0]);
-      if (t0 + tpb > t_end) {  // the piece ends inside this block (only at the sequence's end)
+      // The piece ends inside this block (only at the sequence's end), or the block starts
+      // before the first visible key (only a paged cache under a window).
+      if (t0 + tpb > t_end || (PAGED && t0 < vis_lo)) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int r = 8 * (i >> 2) + 4 * h + (i & 3);
-          const bool ok = ((head_ok >> i) & 1u) && t0 + (r >> pack_log2) < t_end;
+          const int tok = t0 + (r >> pack_log2);
+          const bool ok = ((head_ok >> i) & 1u) && tok < t_end && (!PAGED || tok >= vis_lo);
           sv[0][i] = ok ? sv[0][i] : -INFINITY;
         }
       } else if (pack > 1) {  // rows of other KV groups
@@ -324,6 +370,9 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
     // The block after the current one is always issued, even past the piece's end (it then
     // reads nothing), which keeps the loop free of branches around the loads.
     issue(t_begin, S0{});
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < QL; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, q_word(qraw[ks], qt, q_ok));
     for (int t0 = t_begin;; t0 += 2 * tpb) {
       issue(t0 + tpb, S1{});
       __builtin_amdgcn_s_waitcnt(kWaitBlock);
@@ -347,9 +396,9 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
         for (int g = 0; g < 4; ++g)
           *(f32x4*)(wo + dt * 32 + g * 8 + h * 4) =
               f32x4{o[dt][4 * g], o[dt][4 * g + 1], o[dt][4 * g + 2], o[dt][4 * g + 3]};
-      if (h == 0) {
-        a.ws_ml[2 * idx] = st.m;
-        a.ws_ml[2 * idx + 1] = l_tot;
+      if (h == 0) {  // a piece that met a bad page entry is marked with NaN for the merge
+        a.ws_ml[2 * idx] = bad ? NAN : st.m;
+        a.ws_ml[2 * idx + 1] = bad ? NAN : l_tot;
       }
     }
 
@@ -360,8 +409,8 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
     b = 0;
     for (++s; s < a.n_seq; ++s) {
       n = lens_c[s];
-      base = offs_c[s];
-      if (decode_seq_valid(a, n, base) && decode_key_blocks(n, a.window, tpb) > 0) break;
+      base = PAGED ? 0 : offs_c[s];
+      if (decode_seq_valid(a, n, base, PAGED) && decode_key_blocks(n, a.window, tpb, PAGED) > 0) break;
     }
     if (s >= a.n_seq) break;
   }
@@ -380,17 +429,17 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
   const int hq = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
   // Independent loads first: one memory round trip for all of them.
   const int n = a.lens[s];
-  const int64_t base = a.offsets[s];
+  const int64_t base = a.paged ? 0 : a.offsets[s];
   const int share = a.ws_share[0];
   const int p0 = a.ws_prefix[s];
   unsigned short* O = (unsigned short*)a.o + ((size_t)s * a.Hq + hq) * D;
-  if (!decode_seq_valid(a, n, base)) {
+  if (!decode_seq_valid(a, n, base, a.paged)) {
     const __bf16 nanb = (__bf16)NAN;
     for (int e = 0; e < PER; ++e) O[lane * PER + e] = __builtin_bit_cast(unsigned short, nanb);
     if (a.lse != nullptr && lane == 0) a.lse[(size_t)s * a.Hq + hq] = NAN;
     return;
   }
-  const int nb = decode_key_blocks(n, a.window, a.tpb);
+  const int nb = decode_key_blocks(n, a.window, a.tpb, a.paged);
   const int kvh = hq / a.group, within = hq % a.group;
   // Slot row and column of this query head: one row holding every head in the packed layout,
   // else row (KV head, block of 32 heads).
@@ -398,6 +447,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
   const int col = a.pack > 1 ? hq : within % 32;
 
   float M = -INFINITY, L = 0.f;
+  bool bad = false;  // a piece read a page entry outside the pool (its m is NaN)
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
@@ -423,6 +473,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
 #pragma unroll
         for (int e = 0; e < PER; ++e) ov[jj][e] = jj < cnt ? wo0[((size_t)(j0 + jj) * step) * D + e] : 0.f;
       // Rescale what is accumulated so far to the new maximum, then add these pieces.
+      if (__builtin_amdgcn_ballot_w64(lane < cnt && __builtin_isnan(mj)) != 0) bad = true;
       float Mc = mj;
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) Mc = fmaxf(Mc, __shfl_xor(Mc, off));
@@ -457,13 +508,16 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
     for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  for (int e = 0; e < PER; ++e) O[lane * PER + e] = __builtin_bit_cast(unsigned short, (__bf16)(acc[e] * inv));
+  for (int e = 0; e < PER; ++e)
+    O[lane * PER + e] = __builtin_bit_cast(unsigned short, (__bf16)(bad ? NAN : acc[e] * inv));
   if (a.lse != nullptr && lane == 0)
-    a.lse[(size_t)s * a.Hq + hq] = L > 0.f ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
+    a.lse[(size_t)s * a.Hq + hq] = bad ? NAN : L > 0.f ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
 }
 
-template __global__ void decode_split_kernel<64>(DecArgs);
-template __global__ void decode_split_kernel<128>(DecArgs);
+template __global__ void decode_split_kernel<64, false>(DecArgs);
+template __global__ void decode_split_kernel<128, false>(DecArgs);
+template __global__ void decode_split_kernel<64, true>(DecArgs);
+template __global__ void decode_split_kernel<128, true>(DecArgs);
 template __global__ void decode_merge_kernel<64>(DecArgs);
 template __global__ void decode_merge_kernel<128>(DecArgs);
 
@@ -489,8 +543,9 @@ int decode_workers(int d) {
   if (w > 0) return w;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-  const hipError_t e = d == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<128>, 64, 0)
-                                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<64>, 64, 0);
+  const hipError_t e =
+      d == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<128, false>, 64, 0)
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<64, false>, 64, 0);
   if (e != hipSuccess || cus <= 0 || per_cu <= 0) return -1;
   if (per_cu > kDecodeWorkersPerCu) per_cu = kDecodeWorkersPerCu;
   w = cus * per_cu < kDecodeMaxWorkers ? cus * per_cu : kDecodeMaxWorkers;
@@ -502,10 +557,12 @@ hipError_t launch_decode(const DecArgs& a, int d, hipStream_t stream) {
   const dim3 g1((unsigned)(a.teams * a.rows));
   const dim3 g2((unsigned)a.Hq, (unsigned)a.n_seq);
   if (d == 64) {
-    hipLaunchKernelGGL(decode_split_kernel<64>, g1, dim3(64), 0, stream, a);
+    if (a.paged) hipLaunchKernelGGL((decode_split_kernel<64, true>), g1, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL((decode_split_kernel<64, false>), g1, dim3(64), 0, stream, a);
     hipLaunchKernelGGL(decode_merge_kernel<64>, g2, dim3(64), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(decode_split_kernel<128>, g1, dim3(64), 0, stream, a);
+    if (a.paged) hipLaunchKernelGGL((decode_split_kernel<128, true>), g1, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL((decode_split_kernel<128, false>), g1, dim3(64), 0, stream, a);
     hipLaunchKernelGGL(decode_merge_kernel<128>, g2, dim3(64), 0, stream, a);
   }
   return hipGetLastError();

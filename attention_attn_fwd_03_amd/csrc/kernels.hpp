@@ -35,6 +35,11 @@ struct DecArgs {
   float* ws_ml;
   float* ws_o;
   int64_t pool_rows;
+  // Paged cache (paged != 0): token t of sequence s is pool row
+  // block_table[s * table_stride + t / page_size] * page_size + t % page_size; offsets is unused.
+  const int32_t* block_table;
+  int64_t pool_pages;
+  int table_stride, page_size, paged;
   int n_seq, Hq, Hkv, group, hblocks, max_len, window;
   int pack;   // KV heads per 32-row block (Hkv in the packed layout, else 1)
   int tpb;    // tokens per block: 32 / pack

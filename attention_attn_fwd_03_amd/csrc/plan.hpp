@@ -140,8 +140,16 @@ ATTN_HD int decode_teams(int workers, int rows_per_seq) {
 }
 // Keys the query of a sequence with n cached tokens sees: all of them, or the last `window`.
 ATTN_HD int decode_visible_keys(int n, int window) { return window > 0 && n > window ? window : n; }
-ATTN_HD int decode_key_blocks(int n, int window, int tokens_per_block) {
-  return (decode_visible_keys(n, window) + tokens_per_block - 1) / tokens_per_block;
+// First token of a sequence's block 0: its first visible key, or, in a paged cache (aligned),
+// the start of the tokens_per_block group holding it, so that no block straddles a page (the
+// page size is a multiple of tokens_per_block); keys before the first visible one are masked.
+ATTN_HD int decode_block_origin(int n, int window, int tokens_per_block, int aligned) {
+  const int lo = n - decode_visible_keys(n, window);
+  return aligned ? lo - lo % tokens_per_block : lo;
+}
+ATTN_HD int decode_key_blocks(int n, int window, int tokens_per_block, int aligned) {
+  const int org = decode_block_origin(n, window, tokens_per_block, aligned);
+  return n > org ? (n - org + tokens_per_block - 1) / tokens_per_block : 0;
 }
 ATTN_HD long long decode_max_slots(int n_seq, int rows_per_seq) {
   return (long long)rows_per_seq * (decode_teams(kDecodeMaxWorkers, rows_per_seq) + n_seq);

@@ -12,7 +12,8 @@ reported beside it.  Kernel times come from HIP events recorded on the stream th
 on, over the timed steps.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-  python bench.py --suite        # one JSON line per workload (all five), for the tables
+  python bench.py --suite        # one JSON line per workload (the five, and both decode batches
+                                 # in a paged cache), for the tables
   python bench.py --copy-calib   # a plain device copy of known size, to scale HBM counters
   python bench.py --summarize-counters FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
                                  # rocprofv3 --pmc outputs -> per-launch HBM bytes (profiles/hbm_traffic.md)
@@ -351,6 +352,9 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+PAGE_SIZE = 64  # tokens per page of the paged-cache suite lines
+
+
 def run_suite(args):
     """One JSON line per workload: median kernel time over timed calls, TFLOP/s or GB/s."""
     import torch
@@ -392,7 +396,8 @@ def run_suite(args):
                           "GB/s_algorithmic": round(prefill_bytes(c) / (med * 1e-3) / 1e9, 1)}), flush=True)
         del q, k, v, o, lse
     for name, c in wl.DECODE.items():
-        if not wanted(name):
+        paged_name = f"{name}_paged_P{PAGE_SIZE}"
+        if not wanted(name) and not wanted(paged_name):
             continue
         lens = wl.decode_lens(c.n_seq, c.len_lo, c.len_hi, c.lens_seed)
         max_len = int(lens.max())
@@ -416,16 +421,35 @@ def run_suite(args):
             it[0] += 1
             af.attn_decode(qd, kp, vp, offs, lens_t, max_len=max_len, scale=c.scale, return_lse=True,
                            workspace=ws, out=od, lse_out=lsed)
-        med, mn = timeit(call)
         n_tok = int(lens.sum())
         by = decode_bytes(n_tok, c.n_seq, c.Hq, c.Hkv, c.d)
-        gbs = by / (med * 1e-3) / 1e9
-        print(json.dumps({"workload": name, "kind": "decode", "dtype": "bf16", "median_ms": round(med, 4),
-                          "min_ms": round(mn, 4), "kv_tokens": n_tok, "pool_replicas": n_rep,
-                          "algorithmic_gb": round(by / 1e9, 4), "GB/s": round(gbs, 1),
-                          "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-                          "useful_gflop": round(decode_flops(n_tok, c.Hq, c.Hkv, c.d) / 1e9, 3)}), flush=True)
+
+        def report(wname, med, mn, extra):
+            gbs = by / (med * 1e-3) / 1e9
+            print(json.dumps({"workload": wname, "kind": "decode", "dtype": "bf16", "median_ms": round(med, 4),
+                              "min_ms": round(mn, 4), "kv_tokens": n_tok, "pool_replicas": n_rep, **extra,
+                              "algorithmic_gb": round(by / 1e9, 4), "GB/s": round(gbs, 1),
+                              "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                              "useful_gflop": round(decode_flops(n_tok, c.Hq, c.Hkv, c.d) / 1e9, 3)}), flush=True)
+
+        if wanted(name):
+            med, mn = timeit(call)
+            report(name, med, mn, {})
         del reps_data
+        if wanted(paged_name):
+            # The same batch in a paged cache: 64-token pages scattered over the pool in a seeded
+            # order, 97 spare pages, unused rows NaN.
+            paged = [wl.paged_decode_inputs(c.n_seq, c.Hq, c.Hkv, c.d, lens, PAGE_SIZE, seed=c.value_seed + 100 * r,
+                                            device=dev, extra_pages=97)[:5] for r in range(n_rep)]
+
+            def call_paged():
+                qd, kp, vp, table, lens_t = paged[it[0] % n_rep]
+                it[0] += 1
+                af.attn_decode_paged(qd, kp, vp, table, lens_t, page_size=PAGE_SIZE, max_len=max_len, scale=c.scale,
+                                     return_lse=True, workspace=ws, out=od, lse_out=lsed)
+            med, mn = timeit(call_paged)
+            report(paged_name, med, mn, {"page_size": PAGE_SIZE})
+            del paged
 
 
 if __name__ == "__main__":

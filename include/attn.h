@@ -87,6 +87,27 @@ int attn_decode(const void* q, const void* k_pool, const void* v_pool,
                 int n_seq, int Hq, int Hkv, int d, int64_t pool_rows, int max_len, int window,
                 float scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decode against a paged KV cache ("LLM中的Attention实现及优化", PagedAttention: the cache is
+ * handed out in small fixed-size pages that need not be contiguous; "高效多头潜在注意力解码技术：
+ * Flash MLA深度解析" §3.2: paged GPU memory for long sequences).  As attn_decode, except for the
+ * addressing of the pool:
+ *   k_pool, v_pool [pool_pages * page_size, Hkv, d] bf16: physical page p is pool rows
+ *   p * page_size .. (p + 1) * page_size - 1.
+ *   block_table [n_seq, table_stride] int32 (device memory): block_table[s * table_stride + j]
+ *   is the page holding tokens j * page_size .. (j + 1) * page_size - 1 of sequence s.  Only
+ *   the entries of pages holding keys the query sees are read; table_stride must be at least
+ *   ceil(max_len / page_size).  Pages may be shared between sequences and appear in any order.
+ *   page_size must be a multiple of the decode block's token count (attn_decode_plan's
+ *   tokens_per_block: 32 / Hkv in the packed layout, else 32); ATTN_ERR_UNSUPPORTED otherwise.
+ * A sequence with lens < 0 or lens > max_len is not read, and one whose visible keys lie on a
+ * page entry outside [0, pool_pages) reads nothing from that page; the outputs of both are set
+ * to NaN.  Uses the same workspace (attn_decode_workspace_size). */
+int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_table, int table_stride, int page_size, int64_t pool_pages,
+                      const int32_t* lens, void* o, float* lse,
+                      int n_seq, int Hq, int Hkv, int d, int max_len, int window,
+                      float scale, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* attn_status_str(int status);
 

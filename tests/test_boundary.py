@@ -94,6 +94,49 @@ def test_decode_rejects_bad_arguments(kw, status):
     assert dec(**kw) == status
 
 
+def dec_paged(**kw):
+    # N=4, Hq=8, Hkv=2: packed layout, 16 tokens per block; 7 table entries cover max_len=100
+    a = dict(q=P, kp=P, vp=P, table=P, stride=7, page=16, pages=100, lens=P, o=P, lse=None, N=4, Hq=8, Hkv=2,
+             d=128, max_len=100, window=0, scale=0.1, ws=P, ws_bytes=1 << 30)
+    a.update(kw)
+    return af.lib().attn_decode_paged(a["q"], a["kp"], a["vp"], a["table"], a["stride"], a["page"], a["pages"],
+                                      a["lens"], a["o"], a["lse"], a["N"], a["Hq"], a["Hkv"], a["d"], a["max_len"],
+                                      a["window"], a["scale"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(table=None), af.ATTN_ERR_NULL), (dict(q=None), af.ATTN_ERR_NULL), (dict(lens=None), af.ATTN_ERR_NULL),
+    (dict(kp=None), af.ATTN_ERR_NULL), (dict(o=None), af.ATTN_ERR_NULL),
+    (dict(page=0), af.ATTN_ERR_SHAPE), (dict(pages=-1), af.ATTN_ERR_SHAPE), (dict(stride=0), af.ATTN_ERR_SHAPE),
+    (dict(stride=6), af.ATTN_ERR_SHAPE),                      # ceil(100 / 16) = 7 entries needed
+    (dict(page=1 << 22, stride=1), af.ATTN_ERR_SHAPE),       # one page of one head past 2^31 bytes
+    (dict(N=0), af.ATTN_ERR_SHAPE), (dict(Hq=8, Hkv=3), af.ATTN_ERR_SHAPE), (dict(window=-1), af.ATTN_ERR_SHAPE),
+    (dict(page=8, stride=13), af.ATTN_ERR_UNSUPPORTED),      # pages smaller than a 16-token block
+    (dict(page=24, stride=5), af.ATTN_ERR_UNSUPPORTED),      # not a multiple of 16
+    (dict(Hkv=1, page=16), af.ATTN_ERR_UNSUPPORTED),         # MQA blocks hold 32 tokens
+    (dict(d=32), af.ATTN_ERR_UNSUPPORTED), (dict(scale=math.nan), af.ATTN_ERR_UNSUPPORTED),
+    (dict(ws=None), af.ATTN_ERR_WORKSPACE), (dict(ws_bytes=16), af.ATTN_ERR_WORKSPACE),
+])
+def test_decode_paged_rejects_bad_arguments(kw, status):
+    assert dec_paged(**kw) == status
+
+
+@pytest.mark.parametrize("window,tpb", [(0, 4), (7, 4), (33, 4), (5, 32), (100, 32), (1, 1)])
+def test_decode_pieces_aligned_cover_the_visible_keys(window, tpb):
+    """With aligned blocks (paged caches), block 0 starts at the tpb boundary at or below the first
+    visible key: the blocks cover the visible keys, and at most tpb - 1 keys before them."""
+    lens = [0, 1, 3, 4, 5, 31, 32, 33, 100, 257]
+    for s, n in enumerate(lens):
+        one = af.decode_pieces([n], teams=1, tokens_per_block=tpb, window=window, aligned=True)
+        blocks = sum(p[3] for p in one)
+        vis = min(n, window) if window and n > window else n
+        lo = n - vis
+        org = lo - lo % tpb
+        assert blocks == (-(-(n - org) // tpb) if n > 0 else 0), (n, window, tpb)
+        assert org <= lo and lo - org < tpb and org % tpb == 0
+        assert blocks * tpb >= n - org > (blocks - 1) * tpb if blocks else n == 0
+
+
 def expected_workspace(n_seq, Hq, Hkv, d):
     """Partial slots for at most 2048 workers in teams of U rows, plus one team boundary per
     sequence; each slot holds H query heads of (m, l) and d floats of O.  Packed layout (Hq <= 32,

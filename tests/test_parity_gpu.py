@@ -302,6 +302,148 @@ def test_decode_invalid_sequences_report_nan():
     check(o[:1].double().numpy(), O_ref, lse[:1].numpy(), L_ref, "bf16", "valid neighbour")
 
 
+# ---------------------------------------------------------------------------------------------
+# Decode over a paged KV cache.
+
+def run_decode_paged(q, kp, vp, table, lens, page_size, max_len, window, scale):
+    N, Hq, d = q.shape
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((N, Hq), float("nan"), device=q.device, dtype=torch.float32)
+    af.attn_decode_paged(q, kp, vp, table, lens, page_size=page_size, max_len=max_len, window=window, scale=scale,
+                         return_lse=True, out=o, lse_out=lse)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def oracle_decode_paged(q, kp, vp, table, lens, page_size, seqs, scale, window=0):
+    """The paged oracle on a compact pool holding only the pages of the chosen sequences (each
+    page copied once, the table renumbered)."""
+    table, lens = np.asarray(table), np.asarray(lens)
+    used = sorted({int(table[s, j]) for s in seqs for j in range(-(-int(lens[s]) // page_size))})
+    new = {p: i for i, p in enumerate(used)}
+    rows = torch.tensor([p * page_size + r for p in used for r in range(page_size)], dtype=torch.int64)
+    kc = kp.index_select(0, rows.to(kp.device)).cpu().float().numpy()
+    vc = vp.index_select(0, rows.to(vp.device)).cpu().float().numpy()
+    sub = np.full((len(seqs), table.shape[1]), -1, np.int64)
+    for i, s in enumerate(seqs):
+        for j in range(-(-int(lens[s]) // page_size)):
+            sub[i, j] = new[int(table[s, j])]
+    qs = q.cpu().float().numpy()[seqs]
+    return oracle.decode_paged(qs, kc, vc, sub, lens[seqs], page_size, scale=scale, window=window)
+
+
+def decode_paged_case(lens, Hq, Hkv, d, page_size, window=0, seed=0, scale=None, extra_pages=5, table_fn=None,
+                      seqs=None):
+    lens = np.asarray(lens, np.int32)
+    label = f"paged decode N{len(lens)} Hq{Hq} Hkv{Hkv} d{d} P{page_size} W{window} seed{seed} lens[:8]={lens[:8].tolist()}"
+    say(label)
+    q, kp, vp, table, lens_t, layout = wl.paged_decode_inputs(len(lens), Hq, Hkv, d, lens, page_size, seed=seed,
+                                                              device="cpu", extra_pages=extra_pages)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    ktab = table.clone() if table_fn is None else table_fn(table.clone(), layout)
+    o, lse = run_decode_paged(q.to(DEV), kp.to(DEV), vp.to(DEV), ktab.to(DEV), lens_t.to(DEV), page_size,
+                              int(max(lens.max(), 1)), window, scale)
+    seqs = list(range(len(lens))) if seqs is None else seqs
+    O_ref, L_ref = oracle_decode_paged(q, kp, vp, layout.table, layout.lens, page_size, seqs, scale, window)
+    return check(to64(o)[seqs], O_ref, lse.cpu().numpy()[seqs], L_ref, "bf16", label)
+
+
+@pytest.mark.parametrize("name", ["gqa_decode_bf16", "mqa_decode_bf16"])
+def test_named_decode_paged(name):
+    """The full decode batch with its cache in 64-token pages scattered over the pool (unused
+    pages and page tails NaN): every output finite, 16+ sequences against the oracle, and the
+    result bit-identical to the contiguous entry point on the same keys (same split, same
+    arithmetic)."""
+    c = wl.DECODE[name]
+    P = 64
+    lens = wl.decode_lens(c.n_seq, c.len_lo, c.len_hi, c.lens_seed)
+    say(f"paged decode {name} full size on device, P{P}")
+    q, kp, vp, table, lens_t, layout = wl.paged_decode_inputs(c.n_seq, c.Hq, c.Hkv, c.d, lens, P, seed=c.value_seed,
+                                                              device=DEV, extra_pages=97)
+    o, lse = run_decode_paged(q, kp, vp, table, lens_t, P, int(lens.max()), 0, c.scale)
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+    seqs = sorted(set(np.random.default_rng(c.value_seed).choice(c.n_seq, 16, replace=False).tolist())
+                  | {int(np.argmax(lens)), int(np.argmin(lens))})
+    O_ref, L_ref = oracle_decode_paged(q, kp, vp, layout.table, layout.lens, P, seqs, c.scale)
+    stats = check(to64(o)[seqs], O_ref, lse.cpu().numpy()[seqs], L_ref, "bf16", name + " paged")
+    say(name, "paged", stats)
+    # the same keys laid out contiguously, through attn_decode
+    rows = np.concatenate([(layout.table[s, :-(-int(n) // P)].astype(np.int64)[:, None] * P
+                            + np.arange(P)[None, :]).ravel()[:int(n)] for s, n in enumerate(lens)])
+    rows = torch.from_numpy(rows).to(DEV)
+    kc, vc = kp.index_select(0, rows), vp.index_select(0, rows)
+    offs = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)).to(DEV)
+    o2, lse2 = run_decode(q, kc, vc, offs, lens_t, int(lens.max()), 0, c.scale)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Hkv", [8, 2, 1])
+def test_decode_paged_page_sizes(Hkv, d):
+    """Page sizes from one block up to 256 tokens, lengths on both sides of block and page
+    boundaries, against the split's real share size."""
+    Hq = 8
+    teams, rows, tpb = af.decode_plan(24, Hq, Hkv, d)
+    lens = [0, 1, tpb - 1, tpb, tpb + 1, 63, 64, 65, 255, 256, 257, 1000, 3 * teams * tpb + 11, 7, 2, 500,
+            129, 130, 31, 33, 4096, 17, 900, 1]
+    for P in sorted({tpb, 2 * tpb, max(64, tpb), 256}):
+        decode_paged_case(lens, Hq, Hkv, d, P, seed=1800 + P + Hkv + d)
+
+
+@pytest.mark.parametrize("W", [1, 31, 100, 600, 5000])
+def test_decode_paged_window(W):
+    """Under a window the first block starts at the page boundary below the first visible key
+    (masked up to it); table entries of pages wholly before the window are set to -1 for the
+    kernel, which must not read them."""
+    P = 32
+
+    def drop_early_pages(table, layout):
+        for s, n in enumerate(layout.lens):
+            lo = max(int(n) - W, 0)
+            table[s, :lo // P] = -1
+        return table
+
+    decode_paged_case([1, 50, 1031, 3 * 1024 + 1, 2000, 33, 64], 8, 2, 128, P, window=W, seed=1900 + W,
+                      table_fn=drop_early_pages)
+
+
+def test_decode_paged_shared_pages():
+    """Pages shared between sequences (a common prefix held once) and pages listed out of order."""
+    P = 32
+    lens = np.array([300, 500, 64, 200], np.int32)
+
+    def share_prefix(table, layout):
+        table[1, :4] = table[0, :4]      # sequence 1 starts with sequence 0's first 128 tokens
+        table[3, :3] = table[3, :3].flip(0)
+        return table
+
+    say("paged decode shared pages")
+    q, kp, vp, table, lens_t, layout = wl.paged_decode_inputs(4, 8, 2, 128, lens, P, seed=2000, device="cpu")
+    ktab = share_prefix(table.clone(), layout)
+    o, lse = run_decode_paged(q.to(DEV), kp.to(DEV), vp.to(DEV), ktab.to(DEV), lens_t.to(DEV), P, 500, 0, 0.1)
+    O_ref, L_ref = oracle_decode_paged(q, kp, vp, ktab.numpy(), layout.lens, P, [0, 1, 2, 3], 0.1)
+    check(to64(o), O_ref, lse.cpu().numpy(), L_ref, "bf16", "shared pages")
+
+
+def test_decode_paged_bad_entries_report_nan():
+    """A sequence whose visible keys lie on a page entry outside [0, pool_pages) reads nothing from
+    it and reports NaN; so do lengths past max_len or negative; other sequences are unaffected."""
+    P = 32
+    lens = np.array([100, 90, 70, 60, 80], np.int32)
+    q, kp, vp, table, lens_t, layout = wl.paged_decode_inputs(5, 8, 2, 128, lens, P, seed=2100, device="cpu")
+    bad = table.clone()
+    bad[1, 2] = layout.pool_pages          # one past the last page
+    bad[2, 0] = -5
+    bad_lens = lens_t.clone()
+    bad_lens[3] = 101                      # longer than max_len = 100
+    bad_lens[4] = -1
+    o, lse = run_decode_paged(q.to(DEV), kp.to(DEV), vp.to(DEV), bad.to(DEV), bad_lens.to(DEV), P, 100, 0, 0.1)
+    o, lse = o.cpu().float(), lse.cpu()
+    assert torch.isnan(o[1:]).all() and torch.isnan(lse[1:]).all()
+    O_ref, L_ref = oracle_decode_paged(q, kp, vp, layout.table, layout.lens, P, [0], 0.1)
+    check(o[:1].double().numpy(), O_ref, lse[:1].numpy(), L_ref, "bf16", "valid neighbour")
+
+
 def test_decode_matches_prefill_last_row():
     """Decode of a sequence equals the last row of causal prefill over it (GPU vs GPU, both
     checked against the oracle elsewhere)."""

@@ -163,6 +163,56 @@ def decode_inputs_for(cfg: DecodeConfig, device="cpu"):
                          max_gap=cfg.max_gap)
 
 
+@dataclass
+class PagedLayout:
+    lens: np.ndarray        # int32 [n_seq]
+    page_size: int
+    table: np.ndarray       # int32 [n_seq, stride]: page of each sequence's j-th page slot, -1 if none
+    pool_pages: int
+    row_owner: np.ndarray   # bool [pool_pages * page_size]: the row holds some sequence's token
+
+
+def paged_layout(lens: np.ndarray, page_size: int, seed: int, extra_pages: int = 0,
+                 stride: int | None = None) -> PagedLayout:
+    """Give sequence s ceil(lens[s] / page_size) pages, drawn in a seeded random order from a
+    pool of (pages needed + extra_pages); page slots a sequence does not use hold -1."""
+    rng = np.random.default_rng(seed + 104729)
+    need = [-(-int(n) // page_size) for n in lens]
+    pool_pages = sum(need) + extra_pages
+    perm = rng.permutation(pool_pages)
+    stride = max(max(need), 1) if stride is None else stride
+    table = np.full((len(lens), stride), -1, np.int32)
+    owner = np.zeros(pool_pages * page_size, bool)
+    k = 0
+    for s, m in enumerate(need):
+        for j in range(m):
+            page = int(perm[k])
+            k += 1
+            table[s, j] = page
+            owner[page * page_size:page * page_size + min(page_size, int(lens[s]) - j * page_size)] = True
+    return PagedLayout(lens=np.asarray(lens, np.int32), page_size=page_size, table=table,
+                       pool_pages=pool_pages, row_owner=owner)
+
+
+def paged_decode_inputs(n_seq, Hq, Hkv, d, lens, page_size, *, seed, device="cpu", dtype=torch.bfloat16,
+                        extra_pages=0, stride=None, poison=float("nan")):
+    """q [n_seq, Hq, d]; k_pool, v_pool [pool_pages * page_size, Hkv, d]; block table int32;
+    lens int32.  Rows that hold no sequence's token (unused pages, the tail of each sequence's
+    last page) are filled with ``poison``."""
+    layout = paged_layout(np.asarray(lens), page_size, seed, extra_pages=extra_pages, stride=stride)
+    g = make_generator(seed, device)
+    q = normal((n_seq, Hq, d), g, device, dtype)
+    rows = layout.pool_pages * page_size
+    k_pool = normal((rows, Hkv, d), g, device, dtype)
+    v_pool = normal((rows, Hkv, d), g, device, dtype)
+    free = torch.from_numpy(~layout.row_owner).to(device)
+    k_pool[free] = poison
+    v_pool[free] = poison
+    table = torch.from_numpy(layout.table).to(device)
+    lens_t = torch.from_numpy(layout.lens).to(device)
+    return q, k_pool, v_pool, table, lens_t, layout
+
+
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact upcast of a float32 or bfloat16 tensor to a float64 numpy array."""
     return t.detach().to("cpu").to(torch.float64).numpy()
