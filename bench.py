@@ -330,13 +330,13 @@ def main():
                      "per_launch": f"{pflops / 1e9:.1f} GFLOP useful (4*d per visible pair, 64 heads)"},
         "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                            "kernels": "decode_split_kernel<128> + decode_merge_kernel<128>",
+                            "kernels": "decode_split_kernel<128, false> + decode_merge_kernel<128>",
                             "per_launch": f"{dbytes / 1e9:.3f} GB (one read of live K/V rows + q, O, LSE)"},
     }
     traffic = load_traffic()
     if traffic is not None:
         kp = traffic["kernels"].get("fwd_bf16_kernel<128, 32>")
-        ks = traffic["kernels"].get("decode_split_kernel<128>")
+        ks = traffic["kernels"].get("decode_split_kernel<128, false>")
         km = traffic["kernels"].get("decode_merge_kernel<128>")
         if kp:
             line["roofline"]["traffic"] = kp["traffic_bytes"]
