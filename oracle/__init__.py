@@ -4,9 +4,9 @@ Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import 
 package.  It shares no code with the GPU path and imports nothing from it.
 """
 from .attention import (attention, attention_head, attention_rows, decode, decode_paged, host_cores, kv_head,
-                        masked_softmax, merge_partials, paged_rows, scores, useful_flops, visibility,
-                        visible_pairs)
+                        masked_softmax, merge_partials, paged_rows, prefill_varlen, scores, useful_flops,
+                        visibility, visible_pairs)
 
 __all__ = ["attention", "attention_head", "attention_rows", "decode", "decode_paged", "host_cores", "kv_head",
-           "masked_softmax", "merge_partials", "paged_rows", "scores", "useful_flops", "visibility",
-           "visible_pairs"]
+           "masked_softmax", "merge_partials", "paged_rows", "prefill_varlen", "scores", "useful_flops",
+           "visibility", "visible_pairs"]

@@ -283,6 +283,50 @@ def decode_paged(q, k_pool, v_pool, block_table, lens, page_size: int, scale: fl
     return O, LSE
 
 
+def _seq_rows(pool, start: int, n: int) -> np.ndarray:
+    """Rows start .. start + n - 1 of a token-major pool, upcast."""
+    return _f64(pool[start:start + n])
+
+
+def prefill_varlen(q, k_pool, v_pool, cu_seqlens_q, offsets, lens_k, scale: float | None = None,
+                   causal: bool = True, window: int = 0, threads: int | None = None):
+    """Prefill of new tokens of several sequences, packed end to end, against each one's keys in a
+    shared pool.
+
+    [Deep-Opt §二.1]: continuous batching puts requests of different lengths in one batch;
+    [FlashMLA §一, §2.2]: variable-length sequences, processed chunk by chunk against their
+    history.  q [total_q, Hq, d]: rows cu_seqlens_q[s] .. cu_seqlens_q[s+1] - 1 are the Lq_s new
+    tokens of sequence s.  k_pool, v_pool [T, Hkv, d]: its Lk_s = lens_k[s] keys (the cached ones
+    followed by the new tokens' own) are rows offsets[s] .. offsets[s] + Lk_s - 1 ([DS-Attn
+    §三.3]).  Query i of sequence s sits at position i + Lk_s - Lq_s (bottom-right, the KV-cache
+    convention), and is attended exactly as in attention().  Returns O [total_q, Hq, d] and
+    LSE [total_q, Hq]."""
+    q = np.asarray(q)
+    total, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if window and not causal:
+        raise ValueError("a sliding window is defined only together with causal masking")
+    cu = [int(x) for x in cu_seqlens_q]
+    O = np.zeros((total, Hq, v_pool.shape[2]))
+    LSE = np.zeros((total, Hq))
+
+    def one(s):
+        a, b = cu[s], cu[s + 1]
+        if b <= a:
+            return
+        ks = _seq_rows(k_pool, int(offsets[s]), int(lens_k[s]))
+        vs = _seq_rows(v_pool, int(offsets[s]), int(lens_k[s]))
+        for h in range(Hq):
+            kh = kv_head(h, Hq, Hkv)
+            o, l = attention_head(q[a:b, h], ks[:, kh], vs[:, kh], scale, causal, window)
+            O[a:b, h], LSE[a:b, h] = o, l
+
+    _run(list(range(len(cu) - 1)), one, threads)
+    return O, LSE
+
+
 def merge_partials(outs, lses):
     """Combine attention results taken over disjoint key subsets into the result over their
     union.  outs [C, ..., d] are the per-subset normalised outputs, lses [C, ...] their

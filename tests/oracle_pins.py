@@ -412,6 +412,82 @@ def check_paged_brute_force(seed=24):
                 assert abs(LSE[s, h] - (mx + math.log(tot))) <= 1e-12, (s, h, W)
 
 
+def varlen_pool(seq_k, seq_v, rng, max_gap=4):
+    """Sequences' key rows placed in a token-major pool in random order with NaN gaps."""
+    n = len(seq_k)
+    Hkv, d = seq_k[0].shape[1], seq_k[0].shape[2]
+    gaps = rng.integers(0, max_gap + 1, size=n + 1)
+    T = sum(len(k) for k in seq_k) + int(gaps.sum())
+    pk = np.full((T, Hkv, d), np.nan)
+    pv = np.full((T, Hkv, d), np.nan)
+    offs = np.zeros(n, np.int64)
+    pos = 0
+    for slot, s in enumerate(rng.permutation(n)):
+        pos += int(gaps[slot])
+        offs[s] = pos
+        pk[pos:pos + len(seq_k[s])], pv[pos:pos + len(seq_k[s])] = seq_k[s], seq_v[s]
+        pos += len(seq_k[s])
+    return pk, pv, offs
+
+
+def check_varlen_brute_force(seed=25):
+    """Ragged prefill against a pool ([Deep-Opt §二.1] continuous batching; [FlashMLA §一, §2.2]
+    variable lengths): every sequence's rows equal the pure-Python triple loop on that sequence
+    alone (new tokens as the last Lq_s of its Lk_s positions), with NaN between sequences."""
+    rng = _rng(seed)
+    Hq, Hkv, d = 4, 2, 3
+    lq = [3, 1, 0, 5, 2]
+    lk = [7, 1, 4, 5, 9]
+    seq_k = [rng.standard_normal((n, Hkv, d)) for n in lk]
+    seq_v = [rng.standard_normal((n, Hkv, d)) for n in lk]
+    pk, pv, offs = varlen_pool(seq_k, seq_v, rng)
+    cu = np.concatenate([[0], np.cumsum(lq)])
+    q = rng.standard_normal((int(cu[-1]), Hq, d))
+    for causal, W in ((True, 0), (True, 2), (False, 0)):
+        O, LSE = oracle.prefill_varlen(q, pk, pv, cu, offs, lk, scale=0.45, causal=causal, window=W)
+        for s in range(len(lq)):
+            if lq[s] == 0:
+                continue
+            qs = q[cu[s]:cu[s + 1]].transpose(1, 0, 2)[None]
+            ks = seq_k[s].transpose(1, 0, 2)[None]
+            vs = seq_v[s].transpose(1, 0, 2)[None]
+            Ob, Lb = brute_force(qs, ks, vs, 0.45, causal, W)
+            o, l = O[cu[s]:cu[s + 1]].transpose(1, 0, 2)[None], LSE[cu[s]:cu[s + 1]].T[None]
+            fin = np.isfinite(Lb)
+            assert np.array_equal(np.isneginf(l), np.isneginf(Lb)), (s, causal, W)
+            assert np.max(np.abs(o - Ob)) <= 1e-12, (s, causal, W)
+            assert np.max(np.abs(l[fin] - Lb[fin]), initial=0) <= 1e-12, (s, causal, W)
+
+
+def check_varlen_chunks(seed=26):
+    """Chunked prefill: feeding a sequence's new tokens in two chunks (the first against the keys up
+    to its end, the second against all of them) gives the same rows as one prefill of all of them,
+    which holds only with bottom-right alignment and correct pool addressing."""
+    rng = _rng(seed)
+    Hq, Hkv, d = 2, 1, 4
+    cached, new1, new2 = 6, 3, 4
+    L = cached + new1 + new2
+    k = rng.standard_normal((L, Hkv, d))
+    v = rng.standard_normal((L, Hkv, d))
+    pk, pv, offs = varlen_pool([k], [v], rng)
+    q = rng.standard_normal((new1 + new2, Hq, d))
+    for W in (0, 3):
+        O, LSE = oracle.prefill_varlen(q, pk, pv, [0, new1 + new2], offs, [L], scale=0.7, window=W)
+        O1, L1 = oracle.prefill_varlen(q[:new1], pk, pv, [0, new1], offs, [cached + new1], scale=0.7, window=W)
+        O2, L2 = oracle.prefill_varlen(q[new1:], pk, pv, [0, new2], offs, [L], scale=0.7, window=W)
+        assert np.max(np.abs(np.concatenate([O1, O2]) - O)) <= 1e-13, W
+        assert np.max(np.abs(np.concatenate([L1, L2]) - LSE)) <= 1e-13, W
+    # one new token per sequence is decode
+    lens = [5, 9, 1]
+    seq_k = [rng.standard_normal((n, 2, 3)) for n in lens]
+    seq_v = [rng.standard_normal((n, 2, 3)) for n in lens]
+    pk, pv, offs = varlen_pool(seq_k, seq_v, rng)
+    qd = rng.standard_normal((3, 4, 3))
+    Ov, Lv = oracle.prefill_varlen(qd, pk, pv, [0, 1, 2, 3], offs, lens, scale=0.5, window=4)
+    Od, Ld = oracle.decode(qd, pk, pv, offs, lens, scale=0.5, window=4)
+    assert np.max(np.abs(Ov - Od)) <= 1e-14 and np.max(np.abs(Lv - Ld)) <= 1e-14
+
+
 def check_golden():
     """Hand-derived exact values (tests/golden/worked_example.json)."""
     g = json.load(open(GOLDEN))
@@ -446,4 +522,5 @@ def check_visible_pairs():
 ALL_CHECKS = [check_golden, check_brute_force, check_torch_sdpa, check_softmax_rows, check_constant_scores,
               check_causal_boundary, check_window_convention, check_gqa_mapping, check_pv_invariants,
               check_lse_identity, check_split_merge, check_decode_is_last_row, check_pool_addressing,
-              check_paged_matches_contiguous, check_paged_brute_force, check_visible_pairs]
+              check_paged_matches_contiguous, check_paged_brute_force, check_varlen_brute_force,
+              check_varlen_chunks, check_visible_pairs]

@@ -100,6 +100,11 @@ def _paged_rows_swapped(table_row, n, page_size):
     return np.asarray(table_row, np.int64)[t % page_size % len(table_row)] * page_size + t // page_size
 
 
+def _seq_rows_from_zero(pool, start, n):
+    # the sequence's offset into the pool forgotten
+    return np.asarray(pool[:n], np.float64)
+
+
 MUTANTS = {
     "gqa_interleaved": ("kv_head", _interleaved_kv_head),
     "window_off_by_one": ("_visibility_rows", _window_one_too_wide),
@@ -113,6 +118,7 @@ MUTANTS = {
     "merge_unweighted": ("merge_partials", _merge_unweighted),
     "paged_rows_unscaled": ("paged_rows", _paged_rows_unscaled),
     "paged_rows_swapped": ("paged_rows", _paged_rows_swapped),
+    "varlen_offsets_ignored": ("_seq_rows", _seq_rows_from_zero),
 }
 
 
