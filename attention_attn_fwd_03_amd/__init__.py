@@ -17,8 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libattnfwd.so")
 
 ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(6)
 
-EXPORTS = ["attn_fwd", "attn_fwd_f32", "attn_decode_workspace_size", "attn_decode", "attn_decode_paged",
-           "attn_status_str", "attn_fwd_plan", "attn_fwd_schedule", "attn_decode_plan"]
+EXPORTS = ["attn_fwd", "attn_fwd_f32", "attn_fwd_varlen", "attn_decode_workspace_size", "attn_decode",
+           "attn_decode_paged", "attn_status_str", "attn_fwd_plan", "attn_fwd_schedule", "attn_decode_plan"]
 
 
 class FwdPlanInfo(ctypes.Structure):
@@ -44,6 +44,8 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd.restype = i32
     L.attn_fwd_f32.argtypes = L.attn_fwd.argtypes
     L.attn_fwd_f32.restype = i32
+    L.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, i64, i32, i32, f32, vp]
+    L.attn_fwd_varlen.restype = i32
     L.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     L.attn_decode_workspace_size.restype = sz
     L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, i32, f32, vp, sz, vp]
@@ -117,6 +119,38 @@ def attn_fwd(q, k, v, *, causal: bool = False, window: int = 0, scale: float | N
 
 def decode_workspace_size(n_seq: int, Hq: int, Hkv: int, d: int, max_len: int) -> int:
     return int(lib().attn_decode_workspace_size(n_seq, Hq, Hkv, d, max_len))
+
+
+def attn_fwd_varlen(q, k_pool, v_pool, cu_seqlens_q, kv_offsets, kv_lens, *, max_seqlen_q: int, causal: bool = True,
+                    window: int = 0, scale: float | None = None, return_lse: bool = False, out=None, lse_out=None):
+    """Ragged prefill: new tokens of several sequences packed in q [total_q, Hq, d] (sequence s's
+    rows cu_seqlens_q[s] .. cu_seqlens_q[s+1] - 1), each attending to its kv_lens[s] keys at pool
+    rows kv_offsets[s] .. (pools [T, Hkv, d]), bottom-right aligned.  bf16; cu_seqlens_q and
+    kv_lens int32, kv_offsets int64, all on the device; max_seqlen_q >= every sequence's new
+    tokens.  Returns O [total_q, Hq, d] and, when ``return_lse``, LSE [total_q, Hq] fp32."""
+    import torch
+    _require_gpu(q, k_pool, v_pool, cu_seqlens_q, kv_offsets, kv_lens)
+    if q.dtype != torch.bfloat16 or k_pool.dtype != torch.bfloat16 or v_pool.dtype != torch.bfloat16:
+        raise ValueError("ragged prefill takes bfloat16 q and pools")
+    if cu_seqlens_q.dtype != torch.int32 or kv_lens.dtype != torch.int32 or kv_offsets.dtype != torch.int64:
+        raise ValueError("cu_seqlens_q and kv_lens must be int32, kv_offsets int64")
+    total_q, Hq, d = q.shape
+    T, Hkv, dk = k_pool.shape
+    n_seq = kv_lens.numel()
+    if (dk != d or tuple(v_pool.shape) != tuple(k_pool.shape) or cu_seqlens_q.numel() != n_seq + 1
+            or kv_offsets.numel() != n_seq):
+        raise ValueError("shape mismatch between q, pools, cu_seqlens_q, kv_offsets and kv_lens")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    lse = None
+    if return_lse:
+        lse = torch.empty((total_q, Hq), device=q.device, dtype=torch.float32) if lse_out is None else lse_out
+    _check(lib().attn_fwd_varlen(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), o.data_ptr(),
+                                 lse.data_ptr() if lse is not None else None, cu_seqlens_q.data_ptr(),
+                                 kv_offsets.data_ptr(), kv_lens.data_ptr(), n_seq, Hq, Hkv, d, int(max_seqlen_q),
+                                 total_q, T, int(bool(causal)), int(window), float(scale), _stream()))
+    return (o, lse) if return_lse else o
 
 
 def attn_decode(q, k_pool, v_pool, offsets, lens, *, max_len: int, window: int = 0, scale: float | None = None,

@@ -51,7 +51,7 @@ int check_fwd(const void* q, const void* k, const void* v, const void* o, const 
 FwdArgs make_fwd_args(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                       int Lq, int Lk, int d, int causal, int window, float scale, bool f32) {
   (void)d;
-  FwdArgs a;
+  FwdArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -93,6 +93,29 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int Hq, int Hkv,
                  int Lq, int Lk, int d, int causal, int window, float scale, void* stream) {
   return fwd_common(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d, causal, window, scale, stream, true);
+}
+
+int attn_fwd_varlen(const void* q, const void* k_pool, const void* v_pool, void* o, float* lse,
+                    const int32_t* cu_seqlens_q, const int64_t* kv_offsets, const int32_t* kv_lens, int n_seq, int Hq,
+                    int Hkv, int d, int max_seqlen_q, int64_t total_q, int64_t pool_rows, int causal, int window,
+                    float scale, void* stream) {
+  if (!cu_seqlens_q || !kv_offsets || !kv_lens) return ATTN_ERR_NULL;
+  if (n_seq <= 0 || max_seqlen_q <= 0 || total_q < 0 || pool_rows < 0) return ATTN_ERR_SHAPE;
+  // The per-sequence key counts live on the device; their tiles are addressed one BK-row buffer at
+  // a time, so only the row pitch of the pool bounds the 32-bit offsets here.
+  const int st = check_fwd(q, k_pool, v_pool, o, lse, n_seq, Hq, Hkv, max_seqlen_q, 1, d, causal, window, scale);
+  if (st != ATTN_OK) return st;
+  if ((int64_t)Hkv * d * 2 * 64 >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
+  if (total_q == 0) return ATTN_OK;  // no query rows: nothing to write
+  FwdArgs a = make_fwd_args(q, k_pool, v_pool, o, lse, n_seq, Hq, Hkv, max_seqlen_q, 1, d, causal, window, scale,
+                            false);
+  a.cu_q = cu_seqlens_q;
+  a.kv_offs = kv_offsets;
+  a.kv_lens = kv_lens;
+  a.total_q = total_q;
+  a.pool_rows = pool_rows;
+  const hipError_t e = launch_prefill_varlen(a, d, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 size_t attn_decode_workspace_size(int n_seq, int Hq, int Hkv, int d, int max_len) {

@@ -16,8 +16,16 @@ struct FwdArgs {
   int causal, window;
   float c;            // |scale| * log2(e), or 1 when scale = 0
   int qmode;          // kQAsIs, kQNegate (scale < 0) or kQZero (scale = 0): c is always > 0
-  int n_qt;           // query tiles per head
+  int n_qt;           // query tiles per head (ragged batches: of the longest sequence)
   int heads_per_xcd;  // > 0: XCD-banded block order (see plan.hpp)
+  // Ragged batches against a pool (fwd_bf16_kernel<..., true>): B is the number of sequences;
+  // q and o are [total_q, Hq, d] with sequence b's rows cu_q[b] .. cu_q[b+1] - 1; k and v are the
+  // pools [pool_rows, Hkv, d] with its keys at rows kv_offs[b] .. + kv_lens[b] - 1; lse is
+  // [total_q, Hq].  Lq and Lk are the largest query count (max_seqlen_q) and unused.
+  const int32_t* cu_q;
+  const int64_t* kv_offs;
+  const int32_t* kv_lens;
+  int64_t total_q, pool_rows;
 };
 
 struct DecArgs {
@@ -60,6 +68,7 @@ int prefill_block_k(bool f32, int d);
 int prefill_threads(bool f32);
 int prefill_lds_bytes(bool f32, int d);
 hipError_t launch_prefill(const FwdArgs& a, bool f32, int d, hipStream_t stream);
+hipError_t launch_prefill_varlen(const FwdArgs& a, int d, hipStream_t stream);
 
 int decode_workers(int d);  // one resident round of split workers on the current device, or < 0
 hipError_t launch_decode(const DecArgs& a, int d, hipStream_t stream);

@@ -90,10 +90,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const unsigned short
                                            left * row_bytes, 0x00020000);
 }
 
+// Buffer descriptor over at most max_rows rows, from row0 on, of nrows rows stride_bytes apart
+// (each row_bytes long) at `base`: the rows of one head of a token-major pool.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t strided_rows_rsrc(const unsigned short* base, int row0, int nrows,
+                                                                    int stride_bytes, int row_bytes, int max_rows) {
+  int left = nrows - row0 > 0 ? nrows - row0 : 0;
+  if (left > max_rows) left = max_rows;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned char*)base + (size_t)row0 * stride_bytes), 0,
+                                           left > 0 ? (left - 1) * stride_bytes + row_bytes : 0, 0x00020000);
+}
+
 // Three workgroups share a CU: each SIMD runs three waves, one from each.  That needs at most
 // 168 VGPRs and 53 KB of LDS per workgroup, which is why d = 128 walks the keys in tiles of 32
 // (two stages of K and V take 38 KB; tiles of 64 would take 74 KB) and d = 64 in tiles of 64 (42 KB).
-template <int D, int BK>
+// VARLEN: a ragged batch against a pool (see FwdArgs): each workgroup finds its sequence's query
+// rows and keys, rows are strided by the head count, and tiles past a sequence's end exit at once.
+template <int D, int BK, bool VARLEN>
 __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(FwdArgs a) {
   using C = Bf16Cfg<D, BK>;
   constexpr int NB = C::NB;
@@ -123,10 +135,47 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(FwdArgs a) {
   const PrefillTile t = prefill_tile(blockIdx.x, a.B, a.Hq, a.group, a.n_qt, a.causal, a.heads_per_xcd);
   const int q_start = t.qt * C::BQ;
   const int q = q_start + wave * 32 + col;  // query row of this lane
-  const KeyRange kr = key_range(q_start, C::BQ, a.Lq, a.Lk, BK, a.causal, a.window);
 
-  const unsigned short* Qg = (const unsigned short*)a.q + ((size_t)(t.b * a.Hq + t.hq) * a.Lq) * D;
-  const size_t kv_off = ((size_t)(t.b * a.Hkv + t.hkv) * a.Lk) * D;
+  // Rows of this (batch, head): Q and O rows q_rs elements apart, K and V rows kv_rs apart.
+  const unsigned short* Qg;
+  size_t kv_off;
+  int q_rs = D, kv_rs = D;
+  int64_t row0 = 0;  // ragged: first packed query row of the sequence
+  if constexpr (VARLEN) {
+    const auto* cu = kernel_constant(a.cu_q);
+    const int64_t c0 = cu[t.b], c1 = cu[t.b + 1];
+    const int n_k = kernel_constant(a.kv_lens)[t.b];
+    const int64_t off = kernel_constant(a.kv_offs)[t.b];
+    const bool rows_ok = c0 >= 0 && c0 <= c1 && c1 <= a.total_q;
+    const bool ok = rows_ok && c1 - c0 <= a.Lq && n_k >= 0 && off >= 0 && off + n_k <= a.pool_rows;
+    if (!ok) {
+      // A sequence that is not read: its rows (when they can be told) report NaN.
+      if (rows_ok && q_start < c1 - c0) {
+        const int n_q = (int)(c1 - c0);
+        const __bf16 nanb = (__bf16)NAN;
+        unsigned short* Or = (unsigned short*)a.o + ((size_t)c0 * a.Hq + t.hq) * D;
+        for (int r = tid >> 3; r < C::BQ; r += C::THREADS >> 3)
+          if (q_start + r < n_q)
+            for (int e = (tid & 7); e < D; e += 8)
+              Or[(size_t)(q_start + r) * a.Hq * D + e] = __builtin_bit_cast(unsigned short, nanb);
+        if (a.lse != nullptr && tid < C::BQ && q_start + tid < n_q)
+          a.lse[(size_t)(c0 + q_start + tid) * a.Hq + t.hq] = NAN;
+      }
+      return;
+    }
+    a.Lq = (int)(c1 - c0);
+    a.Lk = n_k;
+    if (q_start >= a.Lq) return;  // this tile lies past the sequence's queries
+    row0 = c0;
+    q_rs = a.Hq * D;
+    kv_rs = a.Hkv * D;
+    Qg = (const unsigned short*)a.q + ((size_t)c0 * a.Hq + t.hq) * D;
+    kv_off = ((size_t)off * a.Hkv + t.hkv) * D;
+  } else {
+    Qg = (const unsigned short*)a.q + ((size_t)(t.b * a.Hq + t.hq) * a.Lq) * D;
+    kv_off = ((size_t)(t.b * a.Hkv + t.hkv) * a.Lk) * D;
+  }
+  const KeyRange kr = key_range(q_start, C::BQ, a.Lq, a.Lk, BK, a.causal, a.window);
   const unsigned short* Kh = (const unsigned short*)a.k + kv_off;  // this head's K and V rows
   const unsigned short* Vh = (const unsigned short*)a.v + kv_off;
 
@@ -135,7 +184,7 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(FwdArgs a) {
   {
     const QTransform qt = q_transform(a.qmode);
     const bool q_ok = q < a.Lq;
-    const unsigned short* Qr = Qg + (size_t)(q_ok ? q : 0) * D;  // rows past Lq read row 0, then zero
+    const unsigned short* Qr = Qg + (size_t)(q_ok ? q : 0) * q_rs;  // rows past Lq read row 0, then zero
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
       qf[ks] = __builtin_bit_cast(bf16x8, q_word(*(const u32x4*)(Qr + ks * 16 + h * 8), qt, q_ok));
@@ -159,19 +208,27 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(FwdArgs a) {
   for (int i = 0; i < C::KL_PER_WAVE; ++i) {
     const int o = (wave + C::WAVES * i) * 1024 + 16 * lane;
     const int row = o / C::KPB, chunk = (o % C::KPB) / 16;
-    k_voff[i] = (row < BK && chunk < C::CH) ? (unsigned)(row * C::ROWB + chunk * 16) : kPastEnd;
+    k_voff[i] = (row < BK && chunk < C::CH) ? (unsigned)(row * kv_rs * 2 + chunk * 16) : kPastEnd;
   }
 #pragma unroll
   for (int i = 0; i < C::VL_PER_WAVE; ++i) {
     const int o = (wave + C::WAVES * i) * 1024 + 16 * lane;
     const int row = o / C::VPB, chunk = (o % C::VPB) / 16;
-    v_voff[i] = (row < BK && chunk < C::CH) ? (unsigned)(row * C::ROWB + chunk * 16) : kPastEnd;
+    v_voff[i] = (row < BK && chunk < C::CH) ? (unsigned)(row * kv_rs * 2 + chunk * 16) : kPastEnd;
   }
   auto issue_k = [&](auto st_c, int kt) {
-    issue_loads(rows_rsrc(Kh, kt * BK, a.Lk, C::ROWB), k_stage(st_c), wave, C::WAVES, C::K_LOADS, k_voff);
+    if constexpr (VARLEN)
+      issue_loads(strided_rows_rsrc(Kh, kt * BK, a.Lk, kv_rs * 2, C::ROWB, BK), k_stage(st_c), wave, C::WAVES,
+                  C::K_LOADS, k_voff);
+    else
+      issue_loads(rows_rsrc(Kh, kt * BK, a.Lk, C::ROWB), k_stage(st_c), wave, C::WAVES, C::K_LOADS, k_voff);
   };
   auto issue_v = [&](auto st_c, int kt) {
-    issue_loads(rows_rsrc(Vh, kt * BK, a.Lk, C::ROWB), v_stage(st_c), wave, C::WAVES, C::V_LOADS, v_voff);
+    if constexpr (VARLEN)
+      issue_loads(strided_rows_rsrc(Vh, kt * BK, a.Lk, kv_rs * 2, C::ROWB, BK), v_stage(st_c), wave, C::WAVES,
+                  C::V_LOADS, v_voff);
+    else
+      issue_loads(rows_rsrc(Vh, kt * BK, a.Lk, C::ROWB), v_stage(st_c), wave, C::WAVES, C::V_LOADS, v_voff);
   };
 
   // K reads for S^T = K Q^T: lane reads row 32*kb + col, elements 16*ks + 8*h .. +7.
@@ -280,16 +337,17 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(FwdArgs a) {
   // wave-wide read takes 16 bytes per lane, RPI whole rows.
   constexpr int RPI = 1024 / (D * 2);
   const int r_in = lane / (D / 8), chunk = lane % (D / 8);
-  unsigned short* Oh = (unsigned short*)a.o + ((size_t)(t.b * a.Hq + t.hq) * a.Lq) * D;
+  unsigned short* Oh = (unsigned short*)a.o + (VARLEN ? ((size_t)row0 * a.Hq + t.hq) * D
+                                                      : ((size_t)(t.b * a.Hq + t.hq) * a.Lq) * D);
 #pragma unroll
   for (int i = 0; i < 32 / RPI; ++i) {
     const int r = i * RPI + r_in;
     const u32x4 w = *(const u32x4*)(ot + r * OPB + chunk * 16);
     const int qr = q_start + wave * 32 + r;
-    if (qr < a.Lq) *(u32x4*)(Oh + (size_t)qr * D + chunk * 8) = w;
+    if (qr < a.Lq) *(u32x4*)(Oh + (size_t)qr * q_rs + chunk * 8) = w;
   }
   if (a.lse != nullptr && h == 0 && q < a.Lq)
-    a.lse[(size_t)(t.b * a.Hq + t.hq) * a.Lq + q] =
+    a.lse[VARLEN ? (size_t)(row0 + q) * a.Hq + t.hq : (size_t)(t.b * a.Hq + t.hq) * a.Lq + q] =
         l_tot > 0.f ? (st.m + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
 }
 
@@ -427,8 +485,10 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------------------------
 
 // Explicit instantiations: the host pass must emit a launch stub for every variant.
-template __global__ void fwd_bf16_kernel<64, 64>(FwdArgs);
-template __global__ void fwd_bf16_kernel<128, 32>(FwdArgs);
+template __global__ void fwd_bf16_kernel<64, 64, false>(FwdArgs);
+template __global__ void fwd_bf16_kernel<128, 32, false>(FwdArgs);
+template __global__ void fwd_bf16_kernel<64, 64, true>(FwdArgs);
+template __global__ void fwd_bf16_kernel<128, 32, true>(FwdArgs);
 template __global__ void fwd_f32_kernel<64>(FwdArgs);
 template __global__ void fwd_f32_kernel<128>(FwdArgs);
 
@@ -447,9 +507,17 @@ hipError_t launch_prefill(const FwdArgs& a, bool f32, int d, hipStream_t stream)
     if (d == 64) hipLaunchKernelGGL(fwd_f32_kernel<64>, g, b, 0, stream, a);
     else hipLaunchKernelGGL(fwd_f32_kernel<128>, g, b, 0, stream, a);
   } else {
-    if (d == 64) hipLaunchKernelGGL((fwd_bf16_kernel<64, 64>), g, b, 0, stream, a);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<128, 32>), g, b, 0, stream, a);
+    if (d == 64) hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, false>), g, b, 0, stream, a);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<128, 32, false>), g, b, 0, stream, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_varlen(const FwdArgs& a, int d, hipStream_t stream) {
+  const int64_t grid = (int64_t)a.n_qt * a.B * a.Hq;
+  const dim3 g((unsigned)grid), b(256);
+  if (d == 64) hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, true>), g, b, 0, stream, a);
+  else hipLaunchKernelGGL((fwd_bf16_kernel<128, 32, true>), g, b, 0, stream, a);
   return hipGetLastError();
 }
 

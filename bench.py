@@ -12,8 +12,8 @@ reported beside it.  Kernel times come from HIP events recorded on the stream th
 on, over the timed steps.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-  python bench.py --suite        # one JSON line per workload (the five, and both decode batches
-                                 # in a paged cache), for the tables
+  python bench.py --suite        # one JSON line per workload (the five, both decode batches in a
+                                 # paged cache, and a ragged chunked-prefill batch), for the tables
   python bench.py --copy-calib   # a plain device copy of known size, to scale HBM counters
   python bench.py --summarize-counters FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
                                  # rocprofv3 --pmc outputs -> per-launch HBM bytes (profiles/hbm_traffic.md)
@@ -395,6 +395,24 @@ def run_suite(args):
                           "frac_mfma_peak": round(tf / peak, 4), "peak_TFLOP/s": peak,
                           "GB/s_algorithmic": round(prefill_bytes(c) / (med * 1e-3) / 1e9, 1)}), flush=True)
         del q, k, v, o, lse
+    for name, c in wl.VARLEN.items():
+        if not wanted(name):
+            continue
+        lq, lk = c.lengths()
+        q, kp, vp, cu, offs, lens, layout = wl.varlen_inputs(lq, lk, c.Hq, c.Hkv, c.d, seed=c.seed, device=dev)
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:2], device=dev, dtype=torch.float32)
+        med, mn = timeit(lambda: af.attn_fwd_varlen(q, kp, vp, cu, offs, lens, max_seqlen_q=int(lq.max()),
+                                                    causal=c.causal, window=c.window, scale=c.scale,
+                                                    return_lse=True, out=o, lse_out=lse))
+        fl = sum(4 * c.d * c.Hq * visible_pairs(int(a), int(b), c.causal, c.window) for a, b in zip(lq, lk))
+        tf = fl / (med * 1e-3) / 1e12
+        print(json.dumps({"workload": name, "kind": "prefill_varlen", "dtype": "bf16", "median_ms": round(med, 4),
+                          "min_ms": round(mn, 4), "sequences": c.n_seq, "new_tokens": int(lq.sum()),
+                          "keys": int(lk.sum()), "useful_gflop": round(fl / 1e9, 4), "TFLOP/s": round(tf, 2),
+                          "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4), "peak_TFLOP/s": PEAK_BF16_TFLOPS}),
+              flush=True)
+        del q, kp, vp, o, lse
     for name, c in wl.DECODE.items():
         paged_name = f"{name}_paged_P{PAGE_SIZE}"
         if not wanted(name) and not wanted(paged_name):

@@ -63,6 +63,26 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
                  int B, int Hq, int Hkv, int Lq, int Lk, int d,
                  int causal, int window, float scale, void* stream);
 
+/* Ragged prefill against a pooled KV cache (continuous batching: "注意力机制深度优化" §二.1;
+ * variable-length sequences processed in chunks against their history: "高效多头潜在注意力解码技术：
+ * Flash MLA深度解析" §一, §2.2).  bf16.
+ *   q, o [total_q, Hq, d]: rows cu_seqlens_q[s] .. cu_seqlens_q[s+1] - 1 are the Lq_s new tokens
+ *   of sequence s (cu_seqlens_q[n_seq + 1] int32, device memory).
+ *   k_pool, v_pool [pool_rows, Hkv, d]: sequence s's Lk_s = kv_lens[s] keys are pool rows
+ *   kv_offsets[s] .. kv_offsets[s] + Lk_s - 1 (int64 / int32 arrays in device memory); they
+ *   include the new tokens' own keys, last.
+ *   Query i of sequence s sits at position i + Lk_s - Lq_s (bottom-right, as in attn_fwd), so a
+ *   chunk of new tokens sees the whole cache and, with causal, the new tokens before it.
+ *   lse [total_q, Hq] fp32, natural log; may be NULL.  max_seqlen_q >= every Lq_s sizes the grid.
+ * Sequences are checked on the device: one with cu_seqlens_q[s] > cu_seqlens_q[s+1], a row past
+ * total_q, Lq_s > max_seqlen_q, kv_lens < 0, kv_offsets < 0 or offsets + lens > pool_rows is not
+ * read; its rows (when its query range lies inside [0, total_q]) are set to NaN.  Other rules
+ * and status codes as attn_fwd; total_q = 0 returns ATTN_OK without device work. */
+int attn_fwd_varlen(const void* q, const void* k_pool, const void* v_pool, void* o, float* lse,
+                    const int32_t* cu_seqlens_q, const int64_t* kv_offsets, const int32_t* kv_lens,
+                    int n_seq, int Hq, int Hkv, int d, int max_seqlen_q, int64_t total_q, int64_t pool_rows,
+                    int causal, int window, float scale, void* stream);
+
 /* Bytes of device workspace attn_decode needs for these sizes (0 if a size is invalid).  The size
  * does not depend on max_len or on the device: with U rows per sequence and H query heads per
  * row (attn_decode_plan), about U * (2048 / U + n_seq) * H * (d + 2) * 4 bytes. */

@@ -69,6 +69,29 @@ def test_fwd_rejects_bad_arguments(kw, status):
                                  a["Lk"], a["d"], a["causal"], a["window"], a["scale"], None) == status
 
 
+def fv(**kw):
+    a = dict(q=P, kp=P, vp=P, o=P, lse=None, cu=P, offs=P, lens=P, N=4, Hq=8, Hkv=2, d=128, maxq=100, total=300,
+             T=1000, causal=1, window=0, scale=0.1)
+    a.update(kw)
+    return af.lib().attn_fwd_varlen(a["q"], a["kp"], a["vp"], a["o"], a["lse"], a["cu"], a["offs"], a["lens"], a["N"],
+                                    a["Hq"], a["Hkv"], a["d"], a["maxq"], a["total"], a["T"], a["causal"],
+                                    a["window"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=None), af.ATTN_ERR_NULL), (dict(offs=None), af.ATTN_ERR_NULL), (dict(lens=None), af.ATTN_ERR_NULL),
+    (dict(q=None), af.ATTN_ERR_NULL), (dict(vp=None), af.ATTN_ERR_NULL), (dict(o=None), af.ATTN_ERR_NULL),
+    (dict(N=0), af.ATTN_ERR_SHAPE), (dict(maxq=0), af.ATTN_ERR_SHAPE), (dict(total=-1), af.ATTN_ERR_SHAPE),
+    (dict(T=-1), af.ATTN_ERR_SHAPE), (dict(Hq=8, Hkv=3), af.ATTN_ERR_SHAPE), (dict(window=-1), af.ATTN_ERR_SHAPE),
+    (dict(causal=2), af.ATTN_ERR_SHAPE),
+    (dict(d=96), af.ATTN_ERR_UNSUPPORTED), (dict(window=5, causal=0), af.ATTN_ERR_UNSUPPORTED),
+    (dict(scale=math.nan), af.ATTN_ERR_UNSUPPORTED), (dict(kp=MISALIGNED), af.ATTN_ERR_UNSUPPORTED),
+    (dict(total=0), af.ATTN_OK),  # no rows: returns before any device work
+])
+def test_fwd_varlen_rejects_bad_arguments(kw, status):
+    assert fv(**kw) == status
+
+
 def dec(**kw):
     a = dict(q=P, kp=P, vp=P, offs=P, lens=P, o=P, lse=None, N=4, Hq=8, Hkv=2, d=128, T=1000, max_len=100, window=0,
              scale=0.1, ws=P, ws_bytes=1 << 30)

@@ -156,6 +156,124 @@ def test_large_values_and_nan_propagation():
 
 
 # ---------------------------------------------------------------------------------------------
+# Ragged (chunked) prefill against a pooled KV cache.
+
+def run_varlen(q, kp, vp, cu, offs, lens, max_q, causal, window, scale):
+    total, Hq, d = q.shape
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((total, Hq), float("nan"), device=q.device, dtype=torch.float32)
+    af.attn_fwd_varlen(q, kp, vp, cu, offs, lens, max_seqlen_q=max_q, causal=causal, window=window, scale=scale,
+                       return_lse=True, out=o, lse_out=lse)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def varlen_case(lq, lk, Hq, Hkv, d, causal=True, window=0, seed=0, scale=None, max_gap=37):
+    lq, lk = np.asarray(lq, np.int32), np.asarray(lk, np.int32)
+    label = f"varlen N{len(lq)} Hq{Hq} Hkv{Hkv} d{d} causal{causal} W{window} seed{seed} lq[:6]={lq[:6].tolist()}"
+    say(label)
+    q, kp, vp, cu, offs, lens, layout = wl.varlen_inputs(lq, lk, Hq, Hkv, d, seed=seed, device="cpu", max_gap=max_gap)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    o, lse = run_varlen(q.to(DEV), kp.to(DEV), vp.to(DEV), cu.to(DEV), offs.to(DEV), lens.to(DEV),
+                        int(max(lq.max(), 1)), causal, window, scale)
+    O_ref, L_ref = oracle.prefill_varlen(q.float().numpy(), kp.float().numpy(), vp.float().numpy(), cu.numpy(),
+                                         layout.offsets, layout.lens, scale=scale, causal=causal, window=window)
+    return check(to64(o), O_ref, lse.cpu().numpy(), L_ref, "bf16", label)
+
+
+VARLEN_LQ = [1, 17, 128, 129, 300, 0, 64, 1000, 33, 256]
+VARLEN_CACHED = [0, 100, 500, 0, 4000, 10, 64, 2000, 1, 255]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal,window", [(True, 0), (False, 0), (True, 1), (True, 100), (True, 777)])
+def test_varlen_chunked_prefill(causal, window, d):
+    """New tokens of ten sequences (0 to 1000 each, ragged against the 128-row tiles) over caches
+    of 0 to 4000 keys, NaN between the sequences in the pool."""
+    lk = [a + b for a, b in zip(VARLEN_LQ, VARLEN_CACHED)]
+    varlen_case(VARLEN_LQ, lk, 8, 2, d, causal=causal, window=window, seed=2200 + d + window)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 1), (12, 4)])
+def test_varlen_head_groups(Hq, Hkv):
+    varlen_case([70, 200, 5], [70, 600, 5], Hq, Hkv, 128, seed=2300 + Hq + Hkv)
+
+
+def test_varlen_more_queries_than_keys():
+    """Lq_s > Lk_s with causal masking: the first rows see no key (O = 0, LSE = -inf)."""
+    varlen_case([50, 10], [20, 10], 4, 2, 128, seed=2400)
+
+
+def test_varlen_matches_dense_per_sequence():
+    """Every sequence of the batch gives bit for bit what attn_fwd gives on that sequence alone
+    (same tiles, same arithmetic; only the addressing differs)."""
+    lq = [300, 1, 129, 700]
+    lk = [300, 2000, 129, 1500]
+    Hq, Hkv, d = 8, 2, 128
+    q, kp, vp, cu, offs, lens, layout = wl.varlen_inputs(lq, lk, Hq, Hkv, d, seed=2500, device=DEV)
+    o, lse = run_varlen(q, kp, vp, cu, offs, lens, max(lq), True, 0, 0.1)
+    for s, (a, n_q, n_k) in enumerate(zip(cu.tolist()[:-1], lq, lk)):
+        off = int(layout.offsets[s])
+        qs = q[a:a + n_q].transpose(0, 1).contiguous()[None]          # [1, Hq, Lq, d]
+        ks = kp[off:off + n_k].transpose(0, 1).contiguous()[None]     # [1, Hkv, Lk, d]
+        vs = vp[off:off + n_k].transpose(0, 1).contiguous()[None]
+        od, ld = af.attn_fwd(qs, ks, vs, causal=True, scale=0.1, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o[a:a + n_q], od[0].transpose(0, 1)), s
+        assert torch.equal(lse[a:a + n_q], ld[0].transpose(0, 1)), s
+
+
+def test_varlen_invalid_sequences_report_nan():
+    """A sequence whose keys fall outside the pool, whose length is negative or whose query count
+    exceeds max_seqlen_q is not read; its rows are NaN and the others are unaffected."""
+    lq, lk = [40, 30, 20, 60], [100, 80, 20, 60]
+    q, kp, vp, cu, offs, lens, layout = wl.varlen_inputs(lq, lk, 8, 2, 128, seed=2600, device="cpu")
+    T = kp.shape[0]
+    bad_offs, bad_lens = offs.clone(), lens.clone()
+    bad_offs[1] = T - 10          # keys run past the pool
+    bad_lens[2] = -1
+    o, lse = run_varlen(q.to(DEV), kp.to(DEV), vp.to(DEV), cu.to(DEV), bad_offs.to(DEV), bad_lens.to(DEV), 50,
+                        True, 0, 0.1)      # max_seqlen_q = 50 < 60: sequence 3 is rejected too
+    o, lse = o.cpu().float(), lse.cpu()
+    c = cu.tolist()
+    assert torch.isnan(o[c[1]:]).all() and torch.isnan(lse[c[1]:]).all()
+    O_ref, L_ref = oracle.prefill_varlen(q[:c[1]].float().numpy(), kp.float().numpy(), vp.float().numpy(),
+                                         [0, c[1]], layout.offsets[:1], layout.lens[:1], scale=0.1)
+    check(o[:c[1]].double().numpy(), O_ref, lse[:c[1]].numpy(), L_ref, "bf16", "valid neighbour")
+
+
+def test_named_varlen_chunked_prefill():
+    """The chunked-prefill batch at full size (16 sequences, 512-2048 new tokens over 0-14k cached
+    keys, Hq 32 / Hkv 8, d 128): all outputs finite, every sequence bit-identical to attn_fwd on it
+    alone, and sampled rows of three sequences against the oracle."""
+    c = wl.VARLEN["chunked_prefill_bf16"]
+    lq, lk = c.lengths()
+    say(f"varlen {c.name} full size on device: lq {lq.tolist()}")
+    q, kp, vp, cu, offs, lens, layout = wl.varlen_inputs(lq, lk, c.Hq, c.Hkv, c.d, seed=c.seed, device=DEV)
+    o, lse = run_varlen(q, kp, vp, cu, offs, lens, int(lq.max()), c.causal, c.window, c.scale)
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+    rng = np.random.default_rng(c.seed)
+    cl = cu.tolist()
+    for s in range(c.n_seq):
+        off, n_q, n_k = int(layout.offsets[s]), int(lq[s]), int(lk[s])
+        qs = q[cl[s]:cl[s] + n_q].transpose(0, 1).contiguous()[None]
+        ks = kp[off:off + n_k].transpose(0, 1).contiguous()[None]
+        vs = vp[off:off + n_k].transpose(0, 1).contiguous()[None]
+        od, ld = af.attn_fwd(qs, ks, vs, causal=c.causal, window=c.window, scale=c.scale, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o[cl[s]:cl[s] + n_q], od[0].transpose(0, 1)), s
+        if s in (0, int(np.argmax(lk)), int(np.argmin(lq))):
+            rows = sorted(set(rng.integers(0, n_q, 6).tolist()) | {0, n_q - 1})
+            samples = [(0, h, i) for h in (0, 5, c.Hq - 1) for i in rows]
+            O_ref, L_ref = oracle.attention_rows(qs.cpu().float().numpy(), ks.cpu().float().numpy(),
+                                                 vs.cpu().float().numpy(), samples, scale=c.scale, causal=c.causal,
+                                                 window=c.window)
+            got_o = np.stack([to64(o[cl[s] + i, h]) for (_, h, i) in samples])
+            got_l = np.array([float(lse[cl[s] + i, h]) for (_, h, i) in samples])
+            check(got_o, O_ref, got_l, L_ref, "bf16", f"{c.name} seq {s}")
+
+
+# ---------------------------------------------------------------------------------------------
 # Decode over a pooled KV cache.
 
 def gather_pool(kp, vp, offsets, lens, seqs):

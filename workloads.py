@@ -77,6 +77,41 @@ DECODE = {
 }
 
 
+@dataclass(frozen=True)
+class VarlenConfig:
+    """A ragged chunked-prefill batch: each sequence adds new_lo..new_hi tokens on top of
+    cached_lo..cached_hi cached ones (both uniform, seeded)."""
+    name: str
+    n_seq: int
+    Hq: int
+    Hkv: int
+    d: int
+    new_lo: int
+    new_hi: int
+    cached_lo: int
+    cached_hi: int
+    seed: int
+    causal: bool = True
+    window: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.d))
+
+    def lengths(self):
+        """(new tokens, keys) per sequence; keys = cached + new."""
+        rng = np.random.default_rng(self.seed)
+        lq = rng.integers(self.new_lo, self.new_hi, size=self.n_seq, endpoint=True)
+        cached = rng.integers(self.cached_lo, self.cached_hi, size=self.n_seq, endpoint=True)
+        return lq.astype(np.int32), (lq + cached).astype(np.int32)
+
+
+# Continuous batching of chunked prefills against the cache, at the decode batch's head shape.
+VARLEN = {
+    "chunked_prefill_bf16": VarlenConfig("chunked_prefill_bf16", 16, 32, 8, 128, 512, 2048, 0, 14336, 1007),
+}
+
+
 def normal(shape, gen: torch.Generator, device, dtype) -> torch.Tensor:
     """float32 N(0, 1) from ``gen``, then rounded to ``dtype``."""
     x = torch.randn(*shape, generator=gen, device=device, dtype=torch.float32)
@@ -211,6 +246,26 @@ def paged_decode_inputs(n_seq, Hq, Hkv, d, lens, page_size, *, seed, device="cpu
     table = torch.from_numpy(layout.table).to(device)
     lens_t = torch.from_numpy(layout.lens).to(device)
     return q, k_pool, v_pool, table, lens_t, layout
+
+
+def varlen_inputs(lq, lk, Hq, Hkv, d, *, seed, device="cpu", dtype=torch.bfloat16, max_gap=37,
+                  poison=float("nan")):
+    """Ragged prefill inputs: q [sum(lq), Hq, d] packed by cu_seqlens; k_pool, v_pool [T, Hkv, d]
+    holding sequence s's lk[s] keys at rows offsets[s] .. (placed by pool_layout: seeded order,
+    ``poison`` in the gaps).  Returns q, k_pool, v_pool, cu_seqlens (int32), offsets (int64),
+    kv_lens (int32) and the layout."""
+    layout = pool_layout(np.asarray(lk), seed, max_gap=max_gap)
+    g = make_generator(seed, device)
+    q = normal((int(sum(lq)), Hq, d), g, device, dtype)
+    k_pool = normal((layout.total_rows, Hkv, d), g, device, dtype)
+    v_pool = normal((layout.total_rows, Hkv, d), g, device, dtype)
+    for start, length in layout.gaps:
+        k_pool[start:start + length] = poison
+        v_pool[start:start + length] = poison
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)).to(device)
+    offsets = torch.from_numpy(layout.offsets).to(device)
+    lens_t = torch.from_numpy(layout.lens).to(device)
+    return q, k_pool, v_pool, cu, offsets, lens_t, layout
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:
