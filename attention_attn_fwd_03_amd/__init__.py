@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libattnfwd.so")
 ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(6)
 
 EXPORTS = ["attn_fwd", "attn_fwd_f32", "attn_fwd_varlen", "attn_decode_workspace_size", "attn_decode",
-           "attn_decode_paged", "attn_status_str", "attn_fwd_plan", "attn_fwd_schedule", "attn_decode_plan"]
+           "attn_decode_paged", "attn_status_str", "attn_fwd_plan", "attn_fwd_schedule", "attn_fwd_varlen_schedule",
+           "attn_decode_plan"]
 
 
 class FwdPlanInfo(ctypes.Structure):
@@ -59,6 +60,8 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_plan.restype = i32
     L.attn_fwd_schedule.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, i64]
     L.attn_fwd_schedule.restype = i32
+    L.attn_fwd_varlen_schedule.argtypes = [i32, i32, i32, i32, vp, i64, ctypes.POINTER(ctypes.c_int64)]
+    L.attn_fwd_varlen_schedule.restype = i32
     L.attn_decode_plan.argtypes = [i32, i32, i32, i32] + [ctypes.POINTER(ctypes.c_int32)] * 3
     L.attn_decode_plan.restype = i32
     _lib = L
@@ -240,6 +243,16 @@ def fwd_schedule(B, Hq, Hkv, Lq, Lk, d, causal=False, window=0, f32=False) -> np
     out = np.zeros((n, 3), dtype=np.int32)
     _check(lib().attn_fwd_schedule(B, Hq, Hkv, Lq, Lk, d, int(bool(causal)), int(window), int(bool(f32)),
                                    out.ctypes.data, out.size))
+    return out
+
+
+def fwd_varlen_schedule(n_seq, Hq, Hkv, max_seqlen_q) -> np.ndarray:
+    """[num_blocks, 3] (sequence, query head, query tile) per block of attn_fwd_varlen; sequence
+    n_seq marks a block without work."""
+    n = ctypes.c_int64()
+    _check(lib().attn_fwd_varlen_schedule(n_seq, Hq, Hkv, max_seqlen_q, None, 0, ctypes.byref(n)))
+    out = np.zeros((n.value, 3), dtype=np.int32)
+    _check(lib().attn_fwd_varlen_schedule(n_seq, Hq, Hkv, max_seqlen_q, out.ctypes.data, out.size, ctypes.byref(n)))
     return out
 
 

@@ -282,6 +282,25 @@ int attn_fwd_schedule(int B, int Hq, int Hkv, int Lq, int Lk, int d, int causal,
   return ATTN_OK;
 }
 
+int attn_fwd_varlen_schedule(int n_seq, int Hq, int Hkv, int max_seqlen_q, int32_t* out, int64_t out_len,
+                             int64_t* num_blocks) {
+  if (!num_blocks) return ATTN_ERR_NULL;
+  if (n_seq <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_seqlen_q <= 0) return ATTN_ERR_SHAPE;
+  const int bq = prefill_block_q(false);
+  const int n_qt = (max_seqlen_q + bq - 1) / bq;
+  const int64_t n = prefill_grouped_blocks(n_seq, Hq, Hkv, n_qt);
+  *num_blocks = n;
+  if (!out) return ATTN_OK;  // size query
+  if (out_len < 3 * n) return ATTN_ERR_SHAPE;
+  for (int64_t bid = 0; bid < n; ++bid) {
+    const PrefillTile t = prefill_tile_grouped((int)bid, n_seq, Hq, Hkv, n_qt);
+    out[3 * bid + 0] = t.b;  // n_seq: a block without work
+    out[3 * bid + 1] = t.hq;
+    out[3 * bid + 2] = t.qt;
+  }
+  return ATTN_OK;
+}
+
 int attn_decode_plan(int n_seq, int Hq, int Hkv, int d, int32_t* teams, int32_t* rows_per_seq,
                      int32_t* tokens_per_block) {
   if (!teams || !rows_per_seq || !tokens_per_block) return ATTN_ERR_NULL;

@@ -101,6 +101,48 @@ ATTN_HD PrefillTile prefill_tile(int bid, int B, int Hq, int group, int n_qt, in
 
 ATTN_HD int prefill_heads_per_xcd(int B, int Hq) { return (B * Hq) % 8 == 0 ? (B * Hq) / 8 : 0; }
 
+// Block index -> work item for ragged batches, whose sequences' keys (a cached prefix of up to
+// tens of thousands of rows) outgrow one XCD's L2.  All workgroups of one (sequence, KV head) --
+// its g query heads times its query tiles -- go to the same XCD (bid % 8) in consecutive slots,
+// so they stream the same keys together through that L2; groups g = b * Hkv + hkv are dealt to
+// the XCDs round-robin (with Hkv a multiple of 8 every XCD gets one KV head of every sequence,
+// hence equal work), and inside a group query tiles come heaviest first.  With fewer than 32
+// groups each is cut into `parts` contiguous pieces dealt out the same way, so that every XCD
+// has work.  The launch holds prefill_grouped_blocks(...) blocks; b >= B marks a block without
+// work.
+struct GroupedOrder {
+  int g_heads, items, parts, part_size, per_xcd;
+};
+ATTN_HD GroupedOrder prefill_grouped_order(int B, int Hq, int Hkv, int n_qt) {
+  GroupedOrder o;
+  o.g_heads = Hq / Hkv;
+  o.items = o.g_heads * n_qt;
+  const int groups = B * Hkv;
+  int parts = groups >= 32 ? 1 : (32 + groups - 1) / groups;
+  if (parts > o.items) parts = o.items;
+  o.parts = parts;
+  o.part_size = (o.items + parts - 1) / parts;
+  o.per_xcd = (groups * parts + 7) / 8;
+  return o;
+}
+ATTN_HD int prefill_grouped_blocks(int B, int Hq, int Hkv, int n_qt) {
+  const GroupedOrder o = prefill_grouped_order(B, Hq, Hkv, n_qt);
+  return 8 * o.per_xcd * o.part_size;
+}
+ATTN_HD PrefillTile prefill_tile_grouped(int bid, int B, int Hq, int Hkv, int n_qt) {
+  const GroupedOrder o = prefill_grouped_order(B, Hq, Hkv, n_qt);
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int piece = xcd + 8 * (slot / o.part_size);  // (group, part)
+  const int g = piece / o.parts;
+  const int within = (piece % o.parts) * o.part_size + slot % o.part_size;
+  PrefillTile t;
+  t.b = within < o.items ? g / Hkv : B;  // >= B: no work
+  t.hkv = g % Hkv;
+  t.qt = n_qt - 1 - within / o.g_heads;
+  t.hq = t.hkv * o.g_heads + within % o.g_heads;
+  return t;
+}
+
 // Decode work decomposition.  A block is 32 K (and V) rows, the M dimension of one MFMA tile.
 //  * Packed layout (Hq <= 32 and Hkv divides 32): a block holds P = Hkv heads of 32 / Hkv
 //    consecutive tokens, i.e. 32 consecutive pool rows, and a worker serves every query head of

@@ -132,7 +132,9 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(FwdArgs a) {
   // Uniform (kept in an SGPR), and visibly below WAVES, so load guards that always hold fold away.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (C::WAVES - 1);
   const int h = lane >> 5, col = lane & 31;
-  const PrefillTile t = prefill_tile(blockIdx.x, a.B, a.Hq, a.group, a.n_qt, a.causal, a.heads_per_xcd);
+  const PrefillTile t = VARLEN ? prefill_tile_grouped(blockIdx.x, a.B, a.Hq, a.Hkv, a.n_qt)
+                               : prefill_tile(blockIdx.x, a.B, a.Hq, a.group, a.n_qt, a.causal, a.heads_per_xcd);
+  if (VARLEN && t.b >= a.B) return;  // padding block of the grouped order
   const int q_start = t.qt * C::BQ;
   const int q = q_start + wave * 32 + col;  // query row of this lane
 
@@ -514,7 +516,7 @@ hipError_t launch_prefill(const FwdArgs& a, bool f32, int d, hipStream_t stream)
 }
 
 hipError_t launch_prefill_varlen(const FwdArgs& a, int d, hipStream_t stream) {
-  const int64_t grid = (int64_t)a.n_qt * a.B * a.Hq;
+  const int64_t grid = prefill_grouped_blocks(a.B, a.Hq, a.Hkv, a.n_qt);
   const dim3 g((unsigned)grid), b(256);
   if (d == 64) hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, true>), g, b, 0, stream, a);
   else hipLaunchKernelGGL((fwd_bf16_kernel<128, 32, true>), g, b, 0, stream, a);

@@ -155,6 +155,13 @@ int attn_fwd_plan(int B, int Hq, int Hkv, int Lq, int Lk, int d, int causal, int
 int attn_fwd_schedule(int B, int Hq, int Hkv, int Lq, int Lk, int d, int causal, int window,
                       int dtype_f32, int32_t* out, int64_t out_len);
 
+/* Block order of attn_fwd_varlen for these sizes: *num_blocks blocks, and (if out is not NULL)
+ * out[3*i .. 3*i+2] = (sequence, query head, query tile) of block i; sequence = n_seq marks a
+ * block without work.  The blocks of one (sequence, KV head) share an XCD (i % 8) and
+ * consecutive slots. */
+int attn_fwd_varlen_schedule(int n_seq, int Hq, int Hkv, int max_seqlen_q, int32_t* out, int64_t out_len,
+                             int64_t* num_blocks);
+
 /* Decode work split on the current device.  A block is 32 rows of K/V: when Hq <= 32 and Hkv
  * divides 32 it holds all Hkv heads of 32/Hkv consecutive tokens (one contiguous stretch of the
  * pool; *rows_per_seq = 1 and one worker serves every query head), otherwise 32 tokens of one KV

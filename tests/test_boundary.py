@@ -92,6 +92,29 @@ def test_fwd_varlen_rejects_bad_arguments(kw, status):
     assert fv(**kw) == status
 
 
+@pytest.mark.parametrize("n_seq,Hq,Hkv,max_q", [(16, 32, 8, 1888), (3, 8, 2, 500), (5, 12, 4, 100), (1, 4, 1, 900),
+                                                (10, 8, 2, 1000), (2, 64, 1, 300), (40, 8, 8, 128)])
+def test_varlen_schedule_groups_keys_per_xcd(n_seq, Hq, Hkv, max_q):
+    """Every (sequence, head, query tile) appears once; the blocks of one (sequence, KV head) that
+    lie on one XCD are consecutive there; with Hkv a multiple of 8 every XCD gets the same work."""
+    sched = af.fwd_varlen_schedule(n_seq, Hq, Hkv, max_q)
+    n_qt = -(-max_q // 128)
+    real = sched[sched[:, 0] < n_seq]
+    keys = {tuple(r) for r in real.tolist()}
+    assert len(keys) == len(real) == n_seq * Hq * n_qt
+    assert np.all((real[:, 1] >= 0) & (real[:, 1] < Hq) & (real[:, 2] >= 0) & (real[:, 2] < n_qt))
+    g = Hq // Hkv
+    xcd = np.arange(len(sched)) % 8
+    for x in range(8):
+        mine = sched[xcd == x]
+        groups = [(int(b), int(hq) // g) for b, hq, _ in mine.tolist() if b < n_seq]
+        runs = [k for i, k in enumerate(groups) if i == 0 or groups[i - 1] != k]
+        assert len(runs) == len(set(runs)), x  # a group's blocks on this XCD are contiguous
+    if Hkv % 8 == 0:
+        per = [int(np.sum(sched[xcd == x][:, 0] < n_seq)) for x in range(8)]
+        assert len(set(per)) == 1, per
+
+
 def dec(**kw):
     a = dict(q=P, kp=P, vp=P, offs=P, lens=P, o=P, lse=None, N=4, Hq=8, Hkv=2, d=128, T=1000, max_len=100, window=0,
              scale=0.1, ws=P, ws_bytes=1 << 30)
