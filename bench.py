@@ -326,7 +326,7 @@ def main():
         },
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "fwd_bf16_kernel<128,32>",
+                     "kernel": "fwd_bf16_kernel<128,32,false>",
                      "per_launch": f"{pflops / 1e9:.1f} GFLOP useful (4*d per visible pair, 64 heads)"},
         "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None,
@@ -335,7 +335,7 @@ def main():
     }
     traffic = load_traffic()
     if traffic is not None:
-        kp = traffic["kernels"].get("fwd_bf16_kernel<128, 32>")
+        kp = traffic["kernels"].get("fwd_bf16_kernel<128, 32, false>")
         ks = traffic["kernels"].get("decode_split_kernel<128, false>")
         km = traffic["kernels"].get("decode_merge_kernel<128>")
         if kp:
