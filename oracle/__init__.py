@@ -3,10 +3,10 @@
 Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import this
 package.  It shares no code with the GPU path and imports nothing from it.
 """
-from .attention import (attention, attention_head, attention_rows, decode, decode_paged, host_cores, kv_head,
+from .attention import (attention, attention_backward, attention_head, attention_rows, decode, decode_paged, host_cores, kv_head,
                         masked_softmax, merge_partials, paged_rows, prefill_varlen, scores, useful_flops,
                         visibility, visible_pairs)
 
-__all__ = ["attention", "attention_head", "attention_rows", "decode", "decode_paged", "host_cores", "kv_head",
+__all__ = ["attention", "attention_backward", "attention_head", "attention_rows", "decode", "decode_paged", "host_cores", "kv_head",
            "masked_softmax", "merge_partials", "paged_rows", "prefill_varlen", "scores", "useful_flops",
            "visibility", "visible_pairs"]

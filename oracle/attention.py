@@ -327,6 +327,64 @@ def prefill_varlen(q, k_pool, v_pool, cu_seqlens_q, offsets, lens_k, scale: floa
     return O, LSE
 
 
+def _softmax_backward(P, dP, O, dO):
+    """dS = P * (dP - rowsum(dO * O)): the row-wise softmax Jacobian applied to dP (rowsum(dO * O)
+    equals rowsum(P * dP), since O = P V and dP = dO V^T)."""
+    D = (dO * O).sum(axis=1)
+    return P * (dP - D[:, None])
+
+
+def _key_grads(dS, P, q, dO, scale):
+    """dK = scale * dS^T q and dV = P^T dO for one query head's rows."""
+    return scale * (dS.T @ q), P.T @ dO
+
+
+def attention_backward(q, k, v, dout, scale: float | None = None, causal: bool = False, window: int = 0,
+                       threads: int | None = None, block: int = 512):
+    """Gradients of attention() with respect to q, k and v, for an upstream gradient dout = dL/dO.
+
+    [MQA-GQA §4]: FlashAttention's backward pass recomputes the forward results rather than
+    keeping the score matrix ([DS-Attn §一]: the softmax matrix would otherwise have to be stored
+    for back-propagation).  Here the plain definition is differentiated, everything materialised
+    in fp64 (query rows ``block`` at a time):
+        S = scale * q k^T on the visible entries, P = row softmax of S, O = P v
+        dV = P^T dO,   dP = dO v^T,   dS = P * (dP - rowsum(dO * O))
+        dQ = scale * dS k,   dK = scale * dS^T q
+    With GQA the gradient of a KV head is the sum over the query heads sharing it ([LLM-Attn]
+    repeat_kv: the copies' gradients flow back to the shared head).  Rows that see no key have
+    P = 0 and contribute nothing.  Returns dQ, dK, dV shaped like q, k, v."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, Hq, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if window and not causal:
+        raise ValueError("a sliding window is defined only together with causal masking")
+    dQ = np.zeros_like(q)
+    dK = np.zeros_like(k)
+    dV = np.zeros_like(v)
+
+    def one(b_kh):
+        b, kh = b_kh
+        for h in range(Hq):
+            if kv_head(h, Hq, Hkv) != kh:
+                continue
+            for s0 in range(0, Lq, block):
+                r = np.arange(s0, min(s0 + block, Lq))
+                S = scores(q[b, h, r], k[b, kh], scale)
+                P, _ = masked_softmax(S, _visibility_rows(r, Lq, Lk, causal, window))
+                O = P @ v[b, kh]
+                dO = dout[b, h, r]
+                dS = _softmax_backward(P, dO @ v[b, kh].T, O, dO)
+                dQ[b, h, r] = scale * (dS @ k[b, kh])
+                gk, gv = _key_grads(dS, P, q[b, h, r], dO, scale)
+                dK[b, kh] += gk
+                dV[b, kh] += gv
+
+    _run([(b, kh) for b in range(B) for kh in range(Hkv)], one, threads)
+    return dQ, dK, dV
+
+
 def merge_partials(outs, lses):
     """Combine attention results taken over disjoint key subsets into the result over their
     union.  outs [C, ..., d] are the per-subset normalised outputs, lses [C, ...] their

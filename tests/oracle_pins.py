@@ -488,6 +488,98 @@ def check_varlen_chunks(seed=26):
     assert np.max(np.abs(Ov - Od)) <= 1e-14 and np.max(np.abs(Lv - Ld)) <= 1e-14
 
 
+def _vis_by_distance(Lq, Lk, causal, window):
+    """Visibility spelled as distance back from the query's position (independent of the oracle)."""
+    dist = (np.arange(Lq)[:, None] + (Lk - Lq)) - np.arange(Lk)[None, :]
+    vis = np.ones((Lq, Lk), bool)
+    if causal:
+        vis &= dist >= 0
+    if window:
+        vis &= dist < window
+    return vis
+
+
+def check_backward_autograd(seed=27):
+    """The backward oracle ([MQA-GQA §4]: the backward pass recomputes the forward) against torch's
+    float64 autograd through the plain formula softmax(scale q k^T + mask) v, GQA by repeating K/V
+    (whose gradients autograd sums back)."""
+    import torch
+    rng = _rng(seed)
+    for (Hq, Hkv, Lq, Lk, d, causal, W) in [(4, 2, 7, 9, 5, True, 0), (2, 2, 6, 6, 3, False, 0),
+                                            (4, 1, 5, 8, 4, True, 3), (3, 3, 8, 8, 2, True, 1)]:
+        q = rng.standard_normal((1, Hq, Lq, d))
+        k = rng.standard_normal((1, Hkv, Lk, d))
+        v = rng.standard_normal((1, Hkv, Lk, d))
+        do = rng.standard_normal((1, Hq, Lq, d))
+        scale = 0.6
+        qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        g = Hq // Hkv
+        kk, vv = kt.repeat_interleave(g, dim=1), vt.repeat_interleave(g, dim=1)
+        vis = torch.from_numpy(_vis_by_distance(Lq, Lk, causal, W))
+        S = (scale * qt @ kk.transpose(-1, -2)).masked_fill(~vis, -math.inf)
+        O = torch.softmax(S, dim=-1) @ vv
+        (O * torch.from_numpy(do)).sum().backward()
+        dQ, dK, dV = oracle.attention_backward(q, k, v, do, scale=scale, causal=causal, window=W)
+        for got, ref, nm in ((dQ, qt.grad, "dq"), (dK, kt.grad, "dk"), (dV, vt.grad, "dv")):
+            assert np.max(np.abs(got - ref.numpy())) <= 1e-12, (nm, Hq, Hkv, Lq, Lk, causal, W)
+
+
+def check_backward_finite_differences(seed=28):
+    """Central differences of L = sum(attention(q, k, v) * dO), taken with the forward oracle, match
+    the backward oracle's gradients for every input element of a tiny causal GQA window case."""
+    rng = _rng(seed)
+    Hq, Hkv, Lq, Lk, d, W, scale = 2, 1, 3, 4, 2, 3, 0.9
+    q = rng.standard_normal((1, Hq, Lq, d))
+    k = rng.standard_normal((1, Hkv, Lk, d))
+    v = rng.standard_normal((1, Hkv, Lk, d))
+    do = rng.standard_normal((1, Hq, Lq, d))
+    dQ, dK, dV = oracle.attention_backward(q, k, v, do, scale=scale, causal=True, window=W)
+    eps = 1e-6
+
+    def loss(q_, k_, v_):
+        return float(np.sum(oracle.attention(q_, k_, v_, scale=scale, causal=True, window=W)[0] * do))
+
+    for which, x, grad in ((0, q, dQ), (1, k, dK), (2, v, dV)):
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[which], args_m[which] = xp, xm
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-7 * max(1.0, abs(fd)), (which, idx, fd, grad[idx])
+
+
+def check_backward_closed_forms(seed=29):
+    """Equal value rows make the output constant in q and k: dQ = dK = 0.  Equal key rows give
+    uniform rows of P whose dS sums to zero per row: dQ = 0.  Rows that see no key (Lq > Lk,
+    causal) get dQ = 0 and their dO does not reach dK or dV."""
+    rng = _rng(seed)
+    Hq, Hkv, Lq, Lk, d = 2, 1, 5, 6, 3
+    q = rng.standard_normal((1, Hq, Lq, d))
+    k = rng.standard_normal((1, Hkv, Lk, d))
+    v = np.repeat(rng.standard_normal((1, Hkv, 1, d)), Lk, axis=2)
+    do = rng.standard_normal((1, Hq, Lq, d))
+    dQ, dK, _ = oracle.attention_backward(q, k, v, do, scale=0.8, causal=True)
+    assert np.max(np.abs(dQ)) <= 1e-13 and np.max(np.abs(dK)) <= 1e-13
+    k_eq = np.repeat(rng.standard_normal((1, Hkv, 1, d)), Lk, axis=2)
+    v2 = rng.standard_normal((1, Hkv, Lk, d))
+    dQ, _, _ = oracle.attention_backward(q, k_eq, v2, do, scale=0.8)
+    assert np.max(np.abs(dQ)) <= 1e-13
+    Lq2, Lk2 = 6, 3                              # rows 0..2 see no key
+    q2 = rng.standard_normal((1, Hq, Lq2, d))
+    k2 = rng.standard_normal((1, Hkv, Lk2, d))
+    v3 = rng.standard_normal((1, Hkv, Lk2, d))
+    do2 = rng.standard_normal((1, Hq, Lq2, d))
+    dQa, dKa, dVa = oracle.attention_backward(q2, k2, v3, do2, scale=0.8, causal=True)
+    assert np.all(dQa[:, :, :3] == 0)
+    do3 = do2.copy()
+    do3[:, :, :3] = rng.standard_normal((1, Hq, 3, d))
+    _, dKb, dVb = oracle.attention_backward(q2, k2, v3, do3, scale=0.8, causal=True)
+    assert np.array_equal(dKa, dKb) and np.array_equal(dVa, dVb)
+
+
 def check_golden():
     """Hand-derived exact values (tests/golden/worked_example.json)."""
     g = json.load(open(GOLDEN))
@@ -523,4 +615,5 @@ ALL_CHECKS = [check_golden, check_brute_force, check_torch_sdpa, check_softmax_r
               check_causal_boundary, check_window_convention, check_gqa_mapping, check_pv_invariants,
               check_lse_identity, check_split_merge, check_decode_is_last_row, check_pool_addressing,
               check_paged_matches_contiguous, check_paged_brute_force, check_varlen_brute_force,
-              check_varlen_chunks, check_visible_pairs]
+              check_varlen_chunks, check_backward_autograd, check_backward_finite_differences,
+              check_backward_closed_forms, check_visible_pairs]

@@ -105,6 +105,16 @@ def _seq_rows_from_zero(pool, start, n):
     return np.asarray(pool[:n], np.float64)
 
 
+def _softmax_backward_no_rowsum(P, dP, O, dO):
+    # the rowsum(dO * O) term of the softmax Jacobian dropped
+    return P * dP
+
+
+def _key_grads_unscaled(dS, P, q, dO, scale):
+    # dK without the score scale
+    return dS.T @ q, P.T @ dO
+
+
 MUTANTS = {
     "gqa_interleaved": ("kv_head", _interleaved_kv_head),
     "window_off_by_one": ("_visibility_rows", _window_one_too_wide),
@@ -119,6 +129,8 @@ MUTANTS = {
     "paged_rows_unscaled": ("paged_rows", _paged_rows_unscaled),
     "paged_rows_swapped": ("paged_rows", _paged_rows_swapped),
     "varlen_offsets_ignored": ("_seq_rows", _seq_rows_from_zero),
+    "backward_no_rowsum": ("_softmax_backward", _softmax_backward_no_rowsum),
+    "backward_dk_unscaled": ("_key_grads", _key_grads_unscaled),
 }
 
 
