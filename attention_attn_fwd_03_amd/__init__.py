@@ -19,7 +19,7 @@ ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE
 
 EXPORTS = ["attn_fwd", "attn_fwd_f32", "attn_fwd_varlen", "attn_decode_workspace_size", "attn_decode",
            "attn_decode_paged", "attn_status_str", "attn_fwd_plan", "attn_fwd_schedule", "attn_fwd_varlen_schedule",
-           "attn_decode_plan"]
+           "attn_decode_plan", "attn_bwd_workspace_size", "attn_bwd"]
 
 
 class FwdPlanInfo(ctypes.Structure):
@@ -54,6 +54,10 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_paged.argtypes = [vp, vp, vp, vp, i32, i32, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                                     vp, sz, vp]
     L.attn_decode_paged.restype = i32
+    L.attn_bwd_workspace_size.argtypes = [i32, i32, i32]
+    L.attn_bwd_workspace_size.restype = sz
+    L.attn_bwd.argtypes = [vp] * 9 + [i32] * 8 + [f32, vp, sz, vp]
+    L.attn_bwd.restype = i32
     L.attn_status_str.argtypes = [i32]
     L.attn_status_str.restype = ctypes.c_char_p
     L.attn_fwd_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(FwdPlanInfo)]
@@ -118,6 +122,42 @@ def attn_fwd(q, k, v, *, causal: bool = False, window: int = 0, scale: float | N
     _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr() if lse is not None else None,
               B, Hq, Hkv, Lq, Lk, d, int(bool(causal)), int(window), float(scale), _stream()))
     return (o, lse) if return_lse else o
+
+
+def bwd_workspace_size(B: int, Hq: int, Lq: int) -> int:
+    return int(lib().attn_bwd_workspace_size(B, Hq, Lq))
+
+
+def attn_bwd(q, k, v, o, dout, lse, *, causal: bool = False, window: int = 0, scale: float | None = None,
+             workspace=None, out=None):
+    """Gradients (dq, dk, dv) of attn_fwd for an upstream gradient ``dout`` [B, Hq, Lq, d], given
+    the forward's output ``o`` and row log-sum-exp ``lse`` [B, Hq, Lq] fp32 (same q, k, v, mask
+    and scale).  bf16.  ``workspace``: optional uint8 device tensor of bwd_workspace_size bytes;
+    ``out``: optional (dq, dk, dv) tensors to write."""
+    import torch
+    _require_gpu(q, k, v, o, dout, lse)
+    if any(t.dtype != torch.bfloat16 for t in (q, k, v, o, dout)) or lse.dtype != torch.float32:
+        raise ValueError("attn_bwd takes bfloat16 q, k, v, o, dout and float32 lse")
+    B, Hq, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    if (tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != d or tuple(o.shape) != tuple(q.shape)
+            or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, Lq)):
+        raise ValueError("shape mismatch between q, k, v, o, dout and lse")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = bwd_workspace_size(B, Hq, Lq)
+    if workspace is None:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    _require_gpu(workspace)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = out
+    _require_gpu(dq, dk, dv)
+    _check(lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                          dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Lq, Lk, d, int(bool(causal)),
+                          int(window), float(scale), workspace.data_ptr(),
+                          workspace.numel() * workspace.element_size(), _stream()))
+    return dq, dk, dv
 
 
 def decode_workspace_size(n_seq: int, Hq: int, Hkv: int, d: int, max_len: int) -> int:

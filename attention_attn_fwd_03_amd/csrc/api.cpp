@@ -222,6 +222,54 @@ int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool, con
                        workspace_bytes, stream, a);
 }
 
+size_t attn_bwd_workspace_size(int B, int Hq, int Lq) {
+  if (B <= 0 || Hq <= 0 || Lq <= 0) return 0;
+  const size_t bytes = (size_t)B * Hq * Lq * sizeof(float);
+  return (bytes + 255) / 256 * 256;
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
+             void* dk, void* dv, int B, int Hq, int Hkv, int Lq, int Lk, int d, int causal, int window, float scale,
+             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dout || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
+  const int st = check_fwd(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d, causal, window, scale);
+  if (st != ATTN_OK) return st;
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(lse))
+    return ATTN_ERR_UNSUPPORTED;
+  // query rows of one head are addressed with 32-bit byte offsets; block counts fit the grid
+  if ((int64_t)Lq * d * 4 >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
+  if ((int64_t)B * Hkv * ((Lk + 127) / 128) >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
+  if ((int64_t)B * Hq * Lq / 16 >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
+  const size_t need = attn_bwd_workspace_size(B, Hq, Lq);
+  if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_ERR_UNSUPPORTED;
+  BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dvec = static_cast<float*>(workspace);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Lq = Lq;
+  a.Lk = Lk;
+  a.group = Hq / Hkv;
+  a.causal = causal;
+  a.window = window;
+  a.scale = scale;
+  a.c2 = scale * kLog2eHost;
+  a.n_qt = (Lq + 127) / 128;
+  a.n_kt = (Lk + 127) / 128;
+  const hipError_t e = launch_backward(a, d, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 const char* attn_status_str(int status) {
   switch (status) {
     case ATTN_OK: return "ATTN_OK";
@@ -230,7 +278,7 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_UNSUPPORTED:
       return "ATTN_ERR_UNSUPPORTED: unsupported head size, window without causal, non-finite scale or "
              "misaligned pointer";
-    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: decode workspace missing or too small";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace missing or too small";
     case ATTN_ERR_HIP: return "ATTN_ERR_HIP: kernel launch failed";
     default: return "unknown attn status";
   }

@@ -58,6 +58,29 @@ struct DecArgs {
   int qmode;
 };
 
+// Backward (bf16): q, o, dout, dq are [B, Hq, Lq, d]; k, v, dk, dv are [B, Hkv, Lk, d]; lse is
+// the forward's natural-log row sum [B, Hq, Lq]; dvec is [B, Hq, Lq] fp32 scratch for
+// D = rowsum(dO * O).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* dvec;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, Hq, Hkv, Lq, Lk;
+  int group;  // Hq / Hkv
+  int causal, window;
+  float scale;
+  float c2;   // scale * log2(e), signed
+  int n_qt;   // 128-row query tiles per head
+  int n_kt;   // 128-row key tiles per KV head
+};
+
 struct DecWorkspaceLayout {
   size_t share, prefix, ml, o, total;  // byte offsets of each region, and the size
 };
@@ -72,5 +95,7 @@ hipError_t launch_prefill_varlen(const FwdArgs& a, int d, hipStream_t stream);
 
 int decode_workers(int d);  // one resident round of split workers on the current device, or < 0
 hipError_t launch_decode(const DecArgs& a, int d, hipStream_t stream);
+
+hipError_t launch_backward(const BwdArgs& a, int d, hipStream_t stream);
 
 }  // namespace attnfwd

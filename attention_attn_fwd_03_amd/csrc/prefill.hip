@@ -64,32 +64,6 @@ __device__ __forceinline__ void edge_limits(int k0, int h, int q, const FwdArgs&
   hi = hk - kbase;
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// N wave-wide global->LDS loads of one tile: load i writes LDS bytes [j*1024, +1024) of `stage`,
-// j = wave + waves*i (loads with j >= total are skipped; j is uniform), from byte offset voff[i]
-// of the buffer `rs`.  The buffer covers exactly the tile's valid rows, so rows past the end of
-// the sequence read as zeros; lanes that land on pad slots carry an offset past any buffer and
-// write zeros there, which nothing reads.  No lane needs its own branch.  (The scalar offset
-// is kept 0: only the per-lane offset is range-checked.)
-template <int N>
-__device__ __forceinline__ void issue_loads(__amdgpu_buffer_rsrc_t rs, unsigned char* stage, int wave, int waves,
-                                            int total, const unsigned (&voff)[N]) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const int j = wave + waves * i;
-    if (j < total) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(stage + j * 1024), 16, voff[i], 0, 0, 0);
-  }
-}
-
-// Buffer descriptor over rows [row0, nrows) of a row-major [nrows, D] bf16 matrix at `base`.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const unsigned short* base, int row0, int nrows,
-                                                            int row_bytes) {
-  const int left = nrows - row0 > 0 ? nrows - row0 : 0;
-  return __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned char*)base + (size_t)row0 * row_bytes), 0,
-                                           left * row_bytes, 0x00020000);
-}
-
 // Buffer descriptor over at most max_rows rows, from row0 on, of nrows rows stride_bytes apart
 // (each row_bytes long) at `base`: the rows of one head of a token-major pool.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t strided_rows_rsrc(const unsigned short* base, int row0, int nrows,

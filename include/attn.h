@@ -44,7 +44,7 @@ typedef enum {
                                Lk*d*4 and max_len*Hkv*d*2 must stay below 2^31 bytes) */
   ATTN_ERR_UNSUPPORTED = 3, /* d not in {64, 128}; window > 0 without causal; scale not finite;
                                a pointer not 16-byte aligned */
-  ATTN_ERR_WORKSPACE = 4,   /* decode workspace NULL or smaller than attn_decode_workspace_size */
+  ATTN_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than attn_decode_workspace_size / attn_bwd_workspace_size */
   ATTN_ERR_HIP = 5          /* the HIP runtime refused a launch */
 } attn_status;
 
@@ -127,6 +127,28 @@ int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                       const int32_t* lens, void* o, float* lse,
                       int n_seq, int Hq, int Hkv, int d, int max_len, int window,
                       float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace attn_bwd needs: B * Hq * Lq fp32 values (rounded up to 256). */
+size_t attn_bwd_workspace_size(int B, int Hq, int Lq);
+
+/* Backward of attn_fwd (bf16): the gradients of O = softmax(scale * Q K^T + mask) V with respect
+ * to q, k and v for an upstream gradient dout = dL/dO.  FlashAttention's backward pass recomputes
+ * the probabilities tile by tile from the forward's row log-sum-exp instead of storing them (the
+ * tqpw.cn MQA/GQA article, §4; the stored softmax matrix is what "003-注意力机制详解…" §一 says
+ * back-propagation would otherwise need).  With P = exp(scale * S - lse) on the visible entries:
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(dO * O)),  dQ = scale * dS K,
+ *   dK = scale * dS^T Q;  with GQA a KV head's gradient sums its query heads' contributions.
+ *   q, o, dout, dq [B, Hq, Lq, d]; k, v, dk, dv [B, Hkv, Lk, d] (bf16, results rounded to nearest
+ *   even); lse [B, Hq, Lq] fp32 as written by attn_fwd with the same q, k, v, mask and scale.
+ *   dq, dk and dv are fully overwritten (not accumulated into).  Masking, scale and status codes
+ *   as attn_fwd; rows with lse = -inf contribute nothing and get dq = 0.
+ * P and dS enter the products rounded to bf16; everything accumulates in fp32.  The result does
+ * not depend on scheduling (no atomics).  workspace: caller-owned device memory of at least
+ * attn_bwd_workspace_size(B, Hq, Lq) bytes, 16-byte aligned, overwritten by each call; calls that
+ * share a workspace must not overlap in time (ATTN_ERR_WORKSPACE if NULL or too small). */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Lq, int Lk, int d,
+             int causal, int window, float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* attn_status_str(int status);

@@ -12,7 +12,16 @@ The bounds are stated for the specified workloads, whose scores have unit varian
 (scale = 1/sqrt(d), N(0, 1) inputs).  Rounding error in fp32 scores is proportional to their
 magnitude, so a stress test that multiplies the scores by a factor f passes ``magnitude=f`` and
 the O bound grows by f (the bf16 bounds are dominated by the bf16 rounding of P and O and do
-not change)."""
+not change).
+
+Gradients (attn_bwd, bf16) have no specified bar; it is derived the same way.  The inputs are
+exact in both paths; the GPU rounds P and dS = P (dP - D) to bf16 before the products that use
+them, takes D = rowsum(dO * O) from the forward's bf16 O, and rounds the results to bf16.  Each
+rounding has a relative RMS of about 2^-8 / sqrt(3) ~ 2.3e-3 and the products sum many such
+terms with independent errors, so a gradient's relative RMS error is about 2.5e-3 (the output
+rounding dominates).  The bar is relative RMS <= 5e-3 per gradient tensor and
+max |g - g_ref| <= 1e-2 * max(1, max |g_ref|) (the largest entries carry the largest rounding,
+u * |g| with u = 2^-8, plus the accumulated share)."""
 import sys
 
 import numpy as np
@@ -20,6 +29,8 @@ import numpy as np
 O_TOL = {"f32": 1e-5, "bf16": 2e-2}
 RMS_TOL = {"bf16": 5e-3}
 LSE_TOL = {"f32": 1e-5, "bf16": 1e-4}
+GRAD_RMS_TOL = 5e-3
+GRAD_MAX_TOL = 1e-2
 
 
 def say(*args):
@@ -56,4 +67,24 @@ def check(o, o_ref, lse, lse_ref, dtype: str, label: str = "", magnitude: float 
             rms = float(np.linalg.norm(o - o_ref)) / nref
             stats["rel_rms"] = rms
             assert rms <= RMS_TOL[dtype], (label, "relative RMS", rms)
+    return stats
+
+
+def check_grad(g, g_ref, label: str = ""):
+    """A bf16 gradient tensor against the fp64 oracle's (see the module docstring for the bar)."""
+    g = np.asarray(g, np.float64)
+    g_ref = np.asarray(g_ref, np.float64)
+    assert g.shape == g_ref.shape, (label, g.shape, g_ref.shape)
+    assert np.all(np.isfinite(g)), (label, "non-finite gradient")
+    err = float(np.max(np.abs(g - g_ref), initial=0.0))
+    bound = GRAD_MAX_TOL * max(1.0, float(np.max(np.abs(g_ref), initial=0.0)))
+    stats = {"max_abs": err}
+    assert err <= bound, (label, "max abs error", err, bound)
+    # An exactly zero reference (one key per row: dP = D, so dS = 0) leaves the fp32 rounding of
+    # dP - D, which only the absolute bound covers.
+    nref = float(np.linalg.norm(g_ref))
+    if nref > 0:
+        rms = float(np.linalg.norm(g - g_ref)) / nref
+        stats["rel_rms"] = rms
+        assert rms <= GRAD_RMS_TOL, (label, "relative RMS", rms)
     return stats

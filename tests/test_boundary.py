@@ -69,6 +69,38 @@ def test_fwd_rejects_bad_arguments(kw, status):
                                  a["Lk"], a["d"], a["causal"], a["window"], a["scale"], None) == status
 
 
+def bwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, Hq=4, Hkv=2, Lq=64, Lk=64, d=128, causal=1,
+             window=0, scale=0.125, ws=P, ws_bytes=1 << 20)
+    a.update(kw)
+    return af.lib().attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["B"],
+                             a["Hq"], a["Hkv"], a["Lq"], a["Lk"], a["d"], a["causal"], a["window"], a["scale"],
+                             a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), af.ATTN_ERR_NULL), (dict(k=None), af.ATTN_ERR_NULL), (dict(v=None), af.ATTN_ERR_NULL),
+    (dict(o=None), af.ATTN_ERR_NULL), (dict(do=None), af.ATTN_ERR_NULL), (dict(lse=None), af.ATTN_ERR_NULL),
+    (dict(dq=None), af.ATTN_ERR_NULL), (dict(dk=None), af.ATTN_ERR_NULL), (dict(dv=None), af.ATTN_ERR_NULL),
+    (dict(B=0), af.ATTN_ERR_SHAPE), (dict(Lq=0), af.ATTN_ERR_SHAPE), (dict(Lk=-3), af.ATTN_ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), af.ATTN_ERR_SHAPE), (dict(window=-1), af.ATTN_ERR_SHAPE), (dict(causal=3), af.ATTN_ERR_SHAPE),
+    (dict(Lq=1 << 22), af.ATTN_ERR_SHAPE), (dict(Lk=1 << 23), af.ATTN_ERR_SHAPE),
+    (dict(d=96), af.ATTN_ERR_UNSUPPORTED), (dict(causal=0, window=8), af.ATTN_ERR_UNSUPPORTED),
+    (dict(scale=math.nan), af.ATTN_ERR_UNSUPPORTED), (dict(do=MISALIGNED), af.ATTN_ERR_UNSUPPORTED),
+    (dict(dk=MISALIGNED), af.ATTN_ERR_UNSUPPORTED), (dict(ws=MISALIGNED), af.ATTN_ERR_UNSUPPORTED),
+    (dict(ws=None), af.ATTN_ERR_WORKSPACE), (dict(ws_bytes=4 * 4 * 64 - 1), af.ATTN_ERR_WORKSPACE),
+])
+def test_bwd_rejects_bad_arguments(kw, status):
+    assert bwd(**kw) == status
+
+
+@pytest.mark.parametrize("B,Hq,Lq", [(1, 1, 1), (2, 32, 4096), (3, 5, 77)])
+def test_bwd_workspace_size(B, Hq, Lq):
+    # one fp32 value per query row, rounded up to 256 bytes
+    assert af.bwd_workspace_size(B, Hq, Lq) == -(-(B * Hq * Lq * 4) // 256) * 256
+    assert af.bwd_workspace_size(0, Hq, Lq) == 0 and af.bwd_workspace_size(B, Hq, 0) == 0
+
+
 def fv(**kw):
     a = dict(q=P, kp=P, vp=P, o=P, lse=None, cu=P, offs=P, lens=P, N=4, Hq=8, Hkv=2, d=128, maxq=100, total=300,
              T=1000, causal=1, window=0, scale=0.1)

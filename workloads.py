@@ -133,6 +133,16 @@ def prefill_inputs(B, Hq, Hkv, Lq, Lk, d, *, seed, dtype=torch.bfloat16, device=
     return q, k, v
 
 
+def backward_inputs(B, Hq, Hkv, Lq, Lk, d, *, seed, dtype=torch.bfloat16, device="cpu"):
+    """prefill_inputs plus an upstream gradient dout [B, Hq, Lq, d] ~ N(0, 1), drawn after them."""
+    g = make_generator(seed, device)
+    q = normal((B, Hq, Lq, d), g, device, dtype)
+    k = normal((B, Hkv, Lk, d), g, device, dtype)
+    v = normal((B, Hkv, Lk, d), g, device, dtype)
+    dout = normal((B, Hq, Lq, d), g, device, dtype)
+    return q, k, v, dout
+
+
 def prefill_inputs_for(cfg: PrefillConfig, device="cpu"):
     return prefill_inputs(cfg.B, cfg.Hq, cfg.Hkv, cfg.Lq, cfg.Lk, cfg.d, seed=cfg.seed,
                           dtype=cfg.torch_dtype, device=device)
