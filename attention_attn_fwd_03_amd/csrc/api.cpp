@@ -266,6 +266,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   a.c2 = scale * kLog2eHost;
   a.n_qt = (Lq + 127) / 128;
   a.n_kt = (Lk + 127) / 128;
+  a.heads_per_xcd = prefill_heads_per_xcd(B, Hq);
   const hipError_t e = launch_backward(a, d, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }

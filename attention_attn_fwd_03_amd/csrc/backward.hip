@@ -37,10 +37,28 @@ struct BwdCfg {
   static constexpr int ROWB = D * 2;    // bytes of one row
   static constexpr int CH = D / 8;      // 16-byte chunks per row
   static constexpr int NPB = ROWB + 16; // LDS pitch of tiles read only as the A operand
-  static constexpr int TPB = ROWB + 64; // LDS pitch of tiles also read transposed
 };
 
+// Query rows per step of the dK/dV kernel (64 measured about 10% faster than 32: half the
+// barriers and step-ahead loads per product).
+constexpr int kBwdQStep = 64;
+
 constexpr int round1k(int x) { return (x + 1023) / 1024 * 1024; }
+
+// Tiles read both as the MFMA A operand (16 consecutive rows, one 16-byte chunk each, per
+// quarter-wave) and transposed (4 consecutive rows, 64 contiguous bytes each, per half-wave) are
+// stored unpadded with their 16-byte chunks permuted per row: chunk c of row r sits at chunk
+// c ^ swz(r).  The LDS bank space is 256 bytes.  At d = 128 a row fills it and swz(r) =
+// 4 (r mod 4) + (r / 4 mod 4): the 16 rows of an A read land on 16 distinct chunks, and the 4 rows
+// of a transposed read on 4 distinct 64-byte quarters.  At d = 64 two rows share it (r mod 2 picks
+// the half) and swz(r) = 4 (r / 2 mod 2) + (r / 4 mod 4), which gives the same two properties.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128)
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  else
+    return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
 
 // Per-lane byte offsets of the wave-wide loads that fill a tile of `rows` rows at LDS pitch
 // `pitch`: load j (of those given to this wave) fills LDS bytes [j*1024, +1024); lane slot
@@ -57,19 +75,43 @@ __device__ __forceinline__ void tile_offsets(unsigned (&voff)[N], int wave, int 
   }
 }
 
-// The MFMA A operand "row r, 16*ks + 8*(lane/32) .. +7" of a tile at pitch `pitch`, for the 32
-// rows starting at `row0`: lane reads row row0 + lane%32.
+// The same for a swizzled tile (pitch = row bytes): LDS chunk p of row r receives memory chunk
+// p ^ swz(r).
+template <int D, int N>
+__device__ __forceinline__ void tile_offsets_swz(unsigned (&voff)[N], int wave, int waves, int lane, int rows) {
+  constexpr int ROWB = D * 2;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int o = (wave + waves * i) * 1024 + 16 * lane;
+    const int row = o / ROWB, chunk = (o % ROWB) / 16;
+    voff[i] = row < rows ? (unsigned)(row * ROWB + (chunk ^ swz<D>(row)) * 16) : 0x80000000u;
+  }
+}
+
+// The MFMA A operand "row r, 16*ks + 8*(lane/32) .. +7" of a padded tile at pitch `pitch`, for
+// the 32 rows starting at `row0`: lane reads row row0 + lane%32.
 __device__ __forceinline__ bf16x8 a_frag(const unsigned char* tile, int row0, int pitch, int ks, int lane) {
   return __builtin_bit_cast(bf16x8, *(const u32x4*)(tile + (row0 + (lane & 31)) * pitch + ks * 32 + (lane >> 5) * 16));
 }
 
-// Transposed A operand (columns 32*dt .. +31 of the tile as rows, 16 tile rows 16*j .. as the
-// k dimension, in the row order that matches an accumulator block used as the B operand).
-__device__ __forceinline__ bf16x8 at_frag(const unsigned char* tile, int pitch, int j, int dt, int lane) {
-  const unsigned char* base = tile + (4 * (lane >> 5) + ((lane & 15) >> 2)) * pitch + ((lane >> 4) & 1) * 32 +
-                              (lane & 3) * 8;
-  const u32x2 r0 = lds_read_tr16(base + 16 * j * pitch + dt * 64);
-  const u32x2 r1 = lds_read_tr16(base + (16 * j + 8) * pitch + dt * 64);
+// The same from a swizzled tile (row0 a multiple of 16).
+template <int D>
+__device__ __forceinline__ bf16x8 a_frag_swz(const unsigned char* tile, int row0, int ks, int lane) {
+  const int row = row0 + (lane & 31);
+  const int chunk = (2 * ks + (lane >> 5)) ^ swz<D>(row);
+  return __builtin_bit_cast(bf16x8, *(const u32x4*)(tile + row * (2 * D) + chunk * 16));
+}
+
+// Transposed A operand from a swizzled tile: columns 32*dt .. +31 of the tile as rows, tile rows
+// 16*j .. 16*j + 15 as the k dimension, in the row order that matches an accumulator block used
+// as the B operand (see the lane layout of ds_read_b64_tr_b16 in attn_device.hpp).
+template <int D>
+__device__ __forceinline__ bf16x8 at_frag_swz(const unsigned char* tile, int j, int dt, int lane) {
+  const int r = 16 * j + 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int chunk = 4 * dt + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int byte = (lane & 1) * 8;
+  const u32x2 r0 = lds_read_tr16(tile + r * (2 * D) + (chunk ^ swz<D>(r)) * 16 + byte);
+  const u32x2 r1 = lds_read_tr16(tile + (r + 8) * (2 * D) + (chunk ^ swz<D>(r + 8)) * 16 + byte);
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3));
 }
 
@@ -154,30 +196,32 @@ __device__ __forceinline__ void key_limits(const BwdArgs& a, int k0, int h, int 
 
 // ---------------------------------------------------------------------------------------------
 // 2. dQ.  One workgroup = 4 waves = 128 query rows of one (batch, query head); keys in tiles of BK.
+// Blocks are ordered as the forward's (plan.hpp prefill_tile): heaviest query tiles first, query
+// heads that share a KV head banded onto one XCD.
 
 template <int D, int BK>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
   constexpr int NB = BK / 32;
-  constexpr int K_TILE = round1k(BK * C::TPB), V_TILE = round1k(BK * C::NPB);
+  constexpr int K_TILE = BK * C::ROWB;                  // swizzled, read both ways
+  constexpr int V_TILE = round1k(BK * C::NPB);          // padded, read as the A operand
   constexpr int K_LOADS = K_TILE / 1024, V_LOADS = V_TILE / 1024;
   constexpr int KLW = (K_LOADS + 3) / 4, VLW = (V_LOADS + 3) / 4;
-  __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[K_TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[K_TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[V_TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[V_TILE];
+  constexpr int OPB = 2 * D + 8;                        // epilogue scratch pitch
+  static_assert(K_TILE % 1024 == 0, "whole wave-wide loads");
+  static_assert(4 * 32 * OPB <= 2 * (K_TILE + V_TILE), "the stages hold the epilogue scratch");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * (K_TILE + V_TILE)];
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  auto k_stage = [&](auto st) -> unsigned char* { if constexpr (decltype(st)::value == 0) return k_lds0; else return k_lds1; };
-  auto v_stage = [&](auto st) -> unsigned char* { if constexpr (decltype(st)::value == 0) return v_lds0; else return v_lds1; };
+  auto k_stage = [&](auto st) -> unsigned char* { return smem + decltype(st)::value * K_TILE; };
+  auto v_stage = [&](auto st) -> unsigned char* { return smem + 2 * K_TILE + decltype(st)::value * V_TILE; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;
   const int h = lane >> 5, col = lane & 31;
-  const int bh = blockIdx.x / a.n_qt;
-  const int qt = a.causal ? a.n_qt - 1 - blockIdx.x % a.n_qt : blockIdx.x % a.n_qt;  // heavy tiles first
-  const int b = bh / a.Hq, hq = bh % a.Hq, hkv = hq / a.group;
-  const int q_start = qt * 128, w_start = q_start + wave * 32;
+  const PrefillTile t = prefill_tile(blockIdx.x, a.B, a.Hq, a.group, a.n_qt, a.causal, a.heads_per_xcd);
+  const int b = t.b, hq = t.hq, hkv = t.hkv;
+  const int q_start = t.qt * 128, w_start = q_start + wave * 32;
   const int q = w_start + col;
   const bool q_ok = q < a.Lq;
 
@@ -212,7 +256,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
   unsigned k_voff[KLW], v_voff[VLW];
-  tile_offsets(k_voff, wave, 4, lane, BK, C::TPB, C::CH, C::ROWB);
+  tile_offsets_swz<D>(k_voff, wave, 4, lane, BK);
   tile_offsets(v_voff, wave, 4, lane, BK, C::NPB, C::CH, C::ROWB);
   auto issue = [&](auto st, int kt) {
     issue_loads(rows_rsrc(Kh, kt * BK, a.Lk, C::ROWB), k_stage(st), wave, 4, K_LOADS, k_voff);
@@ -239,7 +283,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
         for (int kb = 0; kb < NB; ++kb) {
-          x[kb] = mfma_32x32x16(a_frag(Ks, kb * 32, C::TPB, ks, lane), qf[ks], x[kb]);
+          x[kb] = mfma_32x32x16(a_frag_swz<D>(Ks, kb * 32, ks, lane), qf[ks], x[kb]);
           dp[kb] = mfma_32x32x16(a_frag(Vs, kb * 32, C::NPB, ks, lane), df[ks], dp[kb]);
         }
       // Exponent argument c*s - lse2, masked on edge tiles (after scaling: c may be negative).
@@ -264,7 +308,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         for (int half = 0; half < 2; ++half)
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt)
-            acc[dt] = mfma_32x32x16(at_frag(Ks, C::TPB, 2 * kb + half, dt, lane), db[half], acc[dt]);
+            acc[dt] = mfma_32x32x16(at_frag_swz<D>(Ks, 2 * kb + half, dt, lane), db[half], acc[dt]);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -281,38 +325,43 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     }
   }
   // The stages are free (the last step ended with a barrier, no loads in flight): wave w stages
-  // its rows in one of them.
-  unsigned char* scratch = wave == 0 ? k_lds0 : wave == 1 ? k_lds1 : wave == 2 ? v_lds0 : v_lds1;
-  static_assert(32 * (2 * D + 8) <= V_TILE, "a stage holds one wave's rows");
+  // its rows at w * 32 * OPB.
   const int nrows = a.Lq - w_start;
   if (nrows > 0)
-    store_rows_t<D>(acc, a.scale, scratch, (unsigned short*)a.dq + q_off + (size_t)w_start * D, nrows, lane);
+    store_rows_t<D>(acc, a.scale, smem + wave * 32 * OPB, (unsigned short*)a.dq + q_off + (size_t)w_start * D, nrows,
+                    lane);
 }
 
 // ---------------------------------------------------------------------------------------------
-// 3. dK and dV.  One workgroup = 4 waves = 128 keys of one (batch, KV head); a step is 32 query
-// rows of one query head of the group.
+// 3. dK and dV.  One workgroup = 4 waves = 128 keys of one (batch, KV head); a step is BQS query
+// rows of one query head of the group.  Steps run over the query rows from the last down, and
+// over the group's heads inside each stretch of rows, so that the workgroups of one KV head read
+// the same rows at about the same time.  Blocks are ordered key tile first (the first key tiles
+// see the most query rows under a causal mask: heaviest first), KV groups second; with B * Hkv
+// a multiple of 8 all key tiles of a KV group run on one XCD (block index mod 8), sharing its L2.
 
-template <int D>
+template <int D, int BQS>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
-  constexpr int BQS = 32;
-  constexpr int T_TILE = round1k(BQS * C::TPB);
+  constexpr int NQB = BQS / 32;                         // 32-row query blocks per step
+  constexpr int T_TILE = BQS * C::ROWB;                 // swizzled Q or dO rows of one step
   constexpr int T_LOADS = T_TILE / 1024, TLW = (T_LOADS + 3) / 4;
-  __shared__ __attribute__((aligned(1024))) unsigned char q_lds0[T_TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char q_lds1[T_TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char d_lds0[T_TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char d_lds1[T_TILE];
+  constexpr int OPB = 2 * D + 8;
+  static_assert(T_TILE % 1024 == 0, "whole wave-wide loads");
+  // The four stages, which the epilogue reuses as its scratch (32 rows per wave).
+  constexpr int SMEM = 4 * T_TILE > 4 * 32 * OPB ? 4 * T_TILE : 4 * 32 * OPB;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
   __shared__ __attribute__((aligned(16))) float row_lds[2][2][BQS];  // [stage][lse offset, D][row]
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  auto q_stage = [&](auto st) -> unsigned char* { if constexpr (decltype(st)::value == 0) return q_lds0; else return q_lds1; };
-  auto d_stage = [&](auto st) -> unsigned char* { if constexpr (decltype(st)::value == 0) return d_lds0; else return d_lds1; };
+  auto q_stage = [&](auto st) -> unsigned char* { return smem + decltype(st)::value * T_TILE; };
+  auto d_stage = [&](auto st) -> unsigned char* { return smem + (2 + decltype(st)::value) * T_TILE; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;
   const int h = lane >> 5, col = lane & 31;
-  const int bkv = blockIdx.x / a.n_kt, kt = blockIdx.x % a.n_kt;
+  const int n_groups = a.B * a.Hkv;
+  const int kt = blockIdx.x / n_groups, bkv = blockIdx.x % n_groups;
   const int b = bkv / a.Hkv, hkv = bkv % a.Hkv;
   const int k_start = kt * 128, kw = k_start + wave * 32;
   const int key = kw + col;
@@ -361,100 +410,103 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   if (!k_ok) khi = klo - 1;
 
   const int q0_first = qlo > 0 ? qlo / BQS * BQS : 0;
-  const int n_steps_head = qhi > q0_first ? (qhi - q0_first + BQS - 1) / BQS : 0;
-  const int n_steps = n_steps_head * a.group;
+  const int n_qsteps = qhi > q0_first ? (qhi - q0_first + BQS - 1) / BQS : 0;
+  const int n_steps = n_qsteps * a.group;
 
   unsigned t_voff[TLW];
-  tile_offsets(t_voff, wave, 4, lane, BQS, C::TPB, C::CH, C::ROWB);
-  // Step s: query head hkv * group + s / n_steps_head, rows q0 .. q0 + 31.
-  auto step_head = [&](int s) { return hkv * a.group + s / n_steps_head; };
-  auto step_q0 = [&](int s) { return q0_first + (s % n_steps_head) * BQS; };
-  auto issue = [&](auto st, int s) {
-    const int hq = step_head(s), q0 = step_q0(s);
-    const size_t off = ((size_t)(b * a.Hq + hq) * a.Lq) * D;
+  tile_offsets_swz<D>(t_voff, wave, 4, lane, BQS);
+  // Step (qi, hd): query head hkv * group + hd, rows q_top - qi * BQS .. + BQS - 1.
+  const int q_top = q0_first + (n_qsteps - 1) * BQS;
+  auto issue = [&](auto st, int qi, int hd) {
+    const int q0 = q_top - qi * BQS;
+    const size_t off = ((size_t)(b * a.Hq + hkv * a.group + hd) * a.Lq) * D;
     issue_loads(rows_rsrc((const unsigned short*)a.q + off, q0, a.Lq, C::ROWB), q_stage(st), wave, 4, T_LOADS, t_voff);
     issue_loads(rows_rsrc((const unsigned short*)a.dout + off, q0, a.Lq, C::ROWB), d_stage(st), wave, 4, T_LOADS,
                 t_voff);
   };
-  // LSE offsets and D of a step's rows, fetched by the first 64 threads (one value each) a step
-  // ahead and written to LDS before the barrier that precedes their use.
-  auto fetch_rows = [&](int s, float& v) {
-    const int hq = step_head(s), r = step_q0(s) + (tid & 31);
-    const size_t idx = (size_t)(b * a.Hq + hq) * a.Lq + (r < a.Lq ? r : 0);
-    v = tid < 32 ? (r < a.Lq ? lse_offset(a.lse[idx]) : INFINITY) : (r < a.Lq ? a.dvec[idx] : 0.f);
+  // LSE offsets (threads 0 .. BQS-1) and D (threads BQS .. 2*BQS-1) of a step's rows, fetched a
+  // step ahead and written to LDS before the barrier that precedes their use.
+  auto fetch_rows = [&](int qi, int hd, float& v) {
+    const int r = q_top - qi * BQS + (tid % BQS);
+    const size_t idx = (size_t)(b * a.Hq + hkv * a.group + hd) * a.Lq + (r < a.Lq ? r : 0);
+    v = tid < BQS ? (r < a.Lq ? lse_offset(a.lse[idx]) : INFINITY) : (r < a.Lq ? a.dvec[idx] : 0.f);
   };
   const float c = a.c2;
 
+  int qi = 0, hd = 0;  // the current step
   auto step = [&](int s, auto st) {
     using Cur = decltype(st);
     using Oth = std::integral_constant<int, Cur::value ^ 1>;
     float next_row = 0.f;
     const bool more = s + 1 < n_steps;
+    const int nhd = hd + 1 == a.group ? 0 : hd + 1, nqi = hd + 1 == a.group ? qi + 1 : qi;
     if (more) {
-      issue(Oth{}, s + 1);
-      if (tid < 64) fetch_rows(s + 1, next_row);
+      issue(Oth{}, nqi, nhd);
+      if (tid < 2 * BQS) fetch_rows(nqi, nhd, next_row);
     }
-    const int q0 = step_q0(s);
-    if (q0 + BQS > wqlo && q0 < wqhi) {  // some of these rows see this wave's keys
-      const unsigned char* Qs = q_stage(Cur{});
-      const unsigned char* Ds = d_stage(Cur{});
-      f32x16 x, dp;
+    const int q0 = q_top - qi * BQS;
+    const unsigned char* Qs = q_stage(Cur{});
+    const unsigned char* Ds = d_stage(Cur{});
 #pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = dp[i] = 0.f;
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int qb0 = q0 + 32 * qb;
+      if (qb0 + 32 > wqlo && qb0 < wqhi) {  // some of these rows see this wave's keys
+        f32x16 x, dp;
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        x = mfma_32x32x16(a_frag(Qs, 0, C::TPB, ks, lane), kf[ks], x);
-        dp = mfma_32x32x16(a_frag(Ds, 0, C::TPB, ks, lane), vf[ks], dp);
-      }
-      // Rows of the S block are queries q0 + 8*(i/4) + 4h + i%4.
-      const float* lr = row_lds[Cur::value][0] + 4 * h;
-      const float* dr = row_lds[Cur::value][1] + 4 * h;
-      f32x16 l2, dd;
+        for (int i = 0; i < 16; ++i) x[i] = dp[i] = 0.f;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 lv = *(const f32x4*)(lr + 8 * g);
-        const f32x4 dv4 = *(const f32x4*)(dr + 8 * g);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          l2[4 * g + e] = lv[e];
-          dd[4 * g + e] = dv4[e];
+        for (int ks = 0; ks < D / 16; ++ks) {
+          x = mfma_32x32x16(a_frag_swz<D>(Qs, 32 * qb, ks, lane), kf[ks], x);
+          dp = mfma_32x32x16(a_frag_swz<D>(Ds, 32 * qb, ks, lane), vf[ks], dp);
         }
-      }
-      f32x16 xs[1];
+        // Rows of the S block are queries qb0 + 8*(i/4) + 4h + i%4.
+        const float* lr = row_lds[Cur::value][0] + 32 * qb + 4 * h;
+        const float* dr = row_lds[Cur::value][1] + 32 * qb + 4 * h;
+        f32x16 xs[1], dd;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) xs[0][i] = fmaf(x[i], c, -l2[i]);
-      const bool full = k_ok && kw_end == kw + 32 && q0 + BQS <= a.Lq &&
-                        (!a.causal || q0 >= kw + 31 - delta) &&
-                        (a.window <= 0 || q0 + BQS - 1 <= kw - delta + a.window - 1);
-      if (!full) mask_tile(xs, klo - (q0 + 4 * h), khi - (q0 + 4 * h));
-      f32x16 p, ds;
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 lv = *(const f32x4*)(lr + 8 * g);
+          const f32x4 dv4 = *(const f32x4*)(dr + 8 * g);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(xs[0][i]);
-        ds[i] = p[i] * (dp[i] - dd[i]);
-      }
-      bf16x8 pb[2], db[2];
-      to_b_operands(p, pb);
-      to_b_operands(ds, db);
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          dv[dt] = mfma_32x32x16(at_frag(Ds, C::TPB, half, dt, lane), pb[half], dv[dt]);
-          dk[dt] = mfma_32x32x16(at_frag(Qs, C::TPB, half, dt, lane), db[half], dk[dt]);
+          for (int e = 0; e < 4; ++e) {
+            xs[0][4 * g + e] = fmaf(x[4 * g + e], c, -lv[e]);
+            dd[4 * g + e] = dv4[e];
+          }
         }
+        const bool full = k_ok && kw_end == kw + 32 && qb0 + 32 <= a.Lq && (!a.causal || qb0 >= kw + 31 - delta) &&
+                          (a.window <= 0 || qb0 + 31 <= kw - delta + a.window - 1);
+        if (!full) mask_tile(xs, klo - (qb0 + 4 * h), khi - (qb0 + 4 * h));
+        f32x16 p, ds;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          p[i] = __builtin_amdgcn_exp2f(xs[0][i]);
+          ds[i] = p[i] * (dp[i] - dd[i]);
+        }
+        bf16x8 pb[2], db[2];
+        to_b_operands(p, pb);
+        to_b_operands(ds, db);
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) {
+            dv[dt] = mfma_32x32x16(at_frag_swz<D>(Ds, 2 * qb + half, dt, lane), pb[half], dv[dt]);
+            dk[dt] = mfma_32x32x16(at_frag_swz<D>(Qs, 2 * qb + half, dt, lane), db[half], dk[dt]);
+          }
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);
-    if (more && tid < 64) row_lds[Oth::value][tid >> 5][tid & 31] = next_row;
+    if (more && tid < 2 * BQS) row_lds[Oth::value][tid / BQS][tid % BQS] = next_row;
+    qi = nqi;
+    hd = nhd;
     __syncthreads();
   };
 
   if (n_steps > 0) {
-    issue(S0{}, 0);
-    if (tid < 64) {
+    issue(S0{}, 0, 0);
+    if (tid < 2 * BQS) {
       float v;
-      fetch_rows(0, v);
-      row_lds[0][tid >> 5][tid & 31] = v;
+      fetch_rows(0, 0, v);
+      row_lds[0][tid / BQS][tid % BQS] = v;
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -465,9 +517,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   }
   const int nrows = a.Lk - kw;
   if (nrows > 0) {
-    // Wave w stages its rows in q/dO stage w (free after the loop's last barrier).
-    unsigned char* scratch = wave == 0 ? q_lds0 : wave == 1 ? q_lds1 : wave == 2 ? d_lds0 : d_lds1;
-    static_assert(32 * (2 * D + 8) <= T_TILE, "a stage holds one wave's rows");
+    // Wave w stages its rows at w * 32 * OPB (the stages are free after the loop's last barrier).
+    unsigned char* scratch = smem + wave * 32 * OPB;
     store_rows_t<D>(dk, a.scale, scratch, (unsigned short*)a.dk + kv_off + (size_t)kw * D, nrows, lane);
     store_rows_t<D>(dv, 1.f, scratch, (unsigned short*)a.dv + kv_off + (size_t)kw * D, nrows, lane);
   }
@@ -477,8 +528,8 @@ template __global__ void bwd_rowdot_kernel<64>(const unsigned short*, const unsi
 template __global__ void bwd_rowdot_kernel<128>(const unsigned short*, const unsigned short*, float*, int64_t);
 template __global__ void bwd_dq_kernel<64, 64>(BwdArgs);
 template __global__ void bwd_dq_kernel<128, 32>(BwdArgs);
-template __global__ void bwd_dkdv_kernel<64>(BwdArgs);
-template __global__ void bwd_dkdv_kernel<128>(BwdArgs);
+template __global__ void bwd_dkdv_kernel<64, kBwdQStep>(BwdArgs);
+template __global__ void bwd_dkdv_kernel<128, kBwdQStep>(BwdArgs);
 
 hipError_t launch_backward(const BwdArgs& a, int d, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.Hq * a.Lq;
@@ -490,11 +541,11 @@ hipError_t launch_backward(const BwdArgs& a, int d, hipStream_t stream) {
   if (d == 64) {
     hipLaunchKernelGGL(bwd_rowdot_kernel<64>, g1, blk, 0, stream, o, dout, a.dvec, rows);
     hipLaunchKernelGGL((bwd_dq_kernel<64, 64>), g2, blk, 0, stream, a);
-    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, g3, blk, 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<64, kBwdQStep>), g3, blk, 0, stream, a);
   } else {
     hipLaunchKernelGGL(bwd_rowdot_kernel<128>, g1, blk, 0, stream, o, dout, a.dvec, rows);
     hipLaunchKernelGGL((bwd_dq_kernel<128, 32>), g2, blk, 0, stream, a);
-    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, g3, blk, 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<128, kBwdQStep>), g3, blk, 0, stream, a);
   }
   return hipGetLastError();
 }

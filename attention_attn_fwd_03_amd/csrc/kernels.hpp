@@ -79,6 +79,7 @@ struct BwdArgs {
   float c2;   // scale * log2(e), signed
   int n_qt;   // 128-row query tiles per head
   int n_kt;   // 128-row key tiles per KV head
+  int heads_per_xcd;  // dQ block order, as the forward's (plan.hpp)
 };
 
 struct DecWorkspaceLayout {

@@ -12,7 +12,8 @@ reported beside it.  Kernel times come from HIP events recorded on the stream th
 on, over the timed steps.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-  python bench.py --suite        # one JSON line per workload (the five, both decode batches in a
+  python bench.py --suite        # one JSON line per workload (the five, the backward of the dense
+                                 # bf16 ones, both decode batches in a
                                  # paged cache, and a ragged chunked-prefill batch), for the tables
   python bench.py --copy-calib   # a plain device copy of known size, to scale HBM counters
   python bench.py --summarize-counters FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
@@ -66,6 +67,16 @@ def visible_pairs(Lq: int, Lk: int, causal: bool, window: int) -> int:
 
 def prefill_flops(c) -> int:
     return 4 * c.d * c.B * c.Hq * visible_pairs(c.Lq, c.Lk, c.causal, c.window)
+
+
+def backward_flops(c) -> int:
+    """Five products per visible pair and query head (S, dP, dV, dK, dQ), 2*d flops each: 2.5
+    times the forward's; the recomputation of S and dP in the second kernel is not counted."""
+    return 10 * c.d * c.B * c.Hq * visible_pairs(c.Lq, c.Lk, c.causal, c.window)
+
+
+# Backward (training) lines of the suite: the dense bf16 workloads.
+BWD_WORKLOADS = ["mha_bf16_L1024", "gqa_causal_bf16_L4096", "swa_gqa_bf16_L16384_W4096"]
 
 
 def prefill_bytes(c) -> int:
@@ -395,6 +406,23 @@ def run_suite(args):
                           "frac_mfma_peak": round(tf / peak, 4), "peak_TFLOP/s": peak,
                           "GB/s_algorithmic": round(prefill_bytes(c) / (med * 1e-3) / 1e9, 1)}), flush=True)
         del q, k, v, o, lse
+    for name in BWD_WORKLOADS:
+        c = wl.PREFILL[name]
+        if not wanted(name + "_bwd"):
+            continue
+        q, k, v, do = wl.backward_inputs(c.B, c.Hq, c.Hkv, c.Lq, c.Lk, c.d, seed=c.seed, device=dev)
+        o, lse = af.attn_fwd(q, k, v, causal=c.causal, window=c.window, scale=c.scale, return_lse=True)
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        ws = torch.empty(af.bwd_workspace_size(c.B, c.Hq, c.Lq), device=dev, dtype=torch.uint8)
+        med, mn = timeit(lambda: af.attn_bwd(q, k, v, o, do, lse, causal=c.causal, window=c.window, scale=c.scale,
+                                             workspace=ws, out=grads))
+        fl = backward_flops(c)
+        tf = fl / (med * 1e-3) / 1e12
+        print(json.dumps({"workload": name + "_bwd", "kind": "backward", "dtype": "bf16", "median_ms": round(med, 4),
+                          "min_ms": round(mn, 4), "useful_gflop": round(fl / 1e9, 4), "TFLOP/s": round(tf, 2),
+                          "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4), "peak_TFLOP/s": PEAK_BF16_TFLOPS}),
+              flush=True)
+        del q, k, v, do, o, lse, grads, ws
     for name, c in wl.VARLEN.items():
         if not wanted(name):
             continue
