@@ -580,6 +580,61 @@ def check_backward_closed_forms(seed=29):
     assert np.array_equal(dKa, dKb) and np.array_equal(dVa, dVb)
 
 
+def check_fp8_decoders():
+    """The FP8 decoders against the OCP 8-bit float definitions, by hand-worked codes, and against
+    torch's own float8 dtypes (an independent conversion) for all 256 codes of each format."""
+    import torch
+    e4 = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x3C: 1.5,
+          0x40: 2.0, 0x78: 256.0, 0x7E: 448.0, 0xFE: -448.0, 0xB8: -1.0, 0x81: -(2.0 ** -9)}
+    e5 = {0x00: 0.0, 0x01: 2.0 ** -16, 0x03: 3 * 2.0 ** -16, 0x04: 2.0 ** -14, 0x3C: 1.0, 0x3E: 1.5,
+          0x7B: 57344.0, 0x7C: math.inf, 0xFC: -math.inf, 0xBC: -1.0}
+    for table, f in ((e4, oracle.decode_e4m3fn), (e5, oracle.decode_e5m2)):
+        for code, want in table.items():
+            got = float(f(np.array([code], np.uint8))[0])
+            assert got == want, (f.__name__, hex(code), got, want)
+    assert math.copysign(1.0, float(oracle.decode_e4m3fn(np.array([0x80], np.uint8))[0])) == -1.0
+    for code in (0x7F, 0xFF):
+        assert math.isnan(float(oracle.decode_e4m3fn(np.array([code], np.uint8))[0]))
+    for code in (0x7D, 0x7E, 0x7F, 0xFD):
+        assert math.isnan(float(oracle.decode_e5m2(np.array([code], np.uint8))[0]))
+    codes = np.arange(256, dtype=np.uint8)
+    for f, dt in ((oracle.decode_e4m3fn, torch.float8_e4m3fn), (oracle.decode_e5m2, torch.float8_e5m2)):
+        a = f(codes)
+        b = torch.from_numpy(codes).view(dt).to(torch.float64).numpy()
+        assert np.array_equal(np.isnan(a), np.isnan(b)), f.__name__
+        ok = ~np.isnan(a)
+        assert np.array_equal(a[ok], b[ok]), f.__name__
+
+
+def check_fp8kv_decode(seed=30):
+    """Decode over FP8 pools: equal to decode() over the pools that torch's float8 conversion
+    dequantizes (an independent route), for both formats; v_scale scales O and leaves the LSE;
+    k_scale acts as a factor on the scores."""
+    import torch
+    rng = _rng(seed)
+    N, Hq, Hkv, d = 3, 4, 2, 8
+    lens = np.array([5, 1, 9], np.int32)
+    T = 20
+    offsets = np.array([0, 6, 10], np.int64)
+    q = rng.standard_normal((N, Hq, d))
+    for fmt, dt in (("e4m3fn", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)):
+        kc = torch.from_numpy(rng.standard_normal((T, Hkv, d)) * 3).to(dt).view(torch.uint8).numpy()
+        vc = torch.from_numpy(rng.standard_normal((T, Hkv, d)) * 3).to(dt).view(torch.uint8).numpy()
+        ks, vs = 0.37, 1.9
+        O, L = oracle.decode_fp8kv(q, kc, vc, offsets, lens, ks, vs, fmt, scale=0.5)
+        kt = torch.from_numpy(kc).view(dt).to(torch.float64).numpy() * ks
+        vt = torch.from_numpy(vc).view(dt).to(torch.float64).numpy() * vs
+        O2, L2 = oracle.decode(q, kt, vt, offsets, lens, scale=0.5)
+        assert np.allclose(O, O2, rtol=1e-13, atol=1e-13) and np.allclose(L, L2, rtol=1e-13, atol=1e-13), fmt
+        O3, L3 = oracle.decode_fp8kv(q, kc, vc, offsets, lens, ks, 2 * vs, fmt, scale=0.5)
+        assert np.allclose(O3, 2 * O, rtol=1e-13, atol=1e-13) and np.allclose(L3, L, rtol=1e-13, atol=1e-13)
+        O4, L4 = oracle.decode_fp8kv(q, kc, vc, offsets, lens, 1.0, vs, fmt, scale=0.5 * ks)
+        assert np.allclose(O4, O, rtol=1e-12, atol=1e-13) and np.allclose(L4, L, rtol=1e-12, atol=1e-13)
+    # the two formats read the same codes differently
+    Oe4, _ = oracle.decode_fp8kv(q, kc, vc, offsets, lens, 1.0, 1.0, "e4m3fn", scale=0.5)
+    assert not np.allclose(Oe4, oracle.decode_fp8kv(q, kc, vc, offsets, lens, 1.0, 1.0, "e5m2", scale=0.5)[0])
+
+
 def check_golden():
     """Hand-derived exact values (tests/golden/worked_example.json)."""
     g = json.load(open(GOLDEN))
@@ -616,4 +671,4 @@ ALL_CHECKS = [check_golden, check_brute_force, check_torch_sdpa, check_softmax_r
               check_lse_identity, check_split_merge, check_decode_is_last_row, check_pool_addressing,
               check_paged_matches_contiguous, check_paged_brute_force, check_varlen_brute_force,
               check_varlen_chunks, check_backward_autograd, check_backward_finite_differences,
-              check_backward_closed_forms, check_visible_pairs]
+              check_backward_closed_forms, check_visible_pairs, check_fp8_decoders, check_fp8kv_decode]

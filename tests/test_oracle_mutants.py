@@ -163,3 +163,46 @@ def test_decode_window_mutant_is_caught(monkeypatch):
     monkeypatch.setattr(mod, "decode", _decode_window_from_start)
     failed = _run_all_checks()
     assert failed
+
+
+# ---- FP8 KV cache (oracle/fp8.py) -----------------------------------------------------------
+
+fp8mod = importlib.import_module("oracle.fp8")
+
+
+def _e4m3_bias8(codes):
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    val = np.where(e == 0, np.ldexp(m / 8.0, -7), np.ldexp(1.0 + m / 8.0, e - 8))
+    return sign * np.where((e == 15) & ((c & 0x7) == 7), np.nan, val)
+
+
+def _e4m3_flush_subnormals(codes):
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.where(((c >> 3) & 0xF) == 0, 0.0, fp8mod.__dict__["_orig_e4m3"](codes))
+
+
+def _fp8kv_scales_swapped(q, k_codes, v_codes, offsets, lens, k_scale, v_scale, fmt, **kw):
+    return fp8mod.decode(q, fp8mod.dequantize(k_codes, v_scale, fmt), fp8mod.dequantize(v_codes, k_scale, fmt),
+                         offsets, lens, **kw)
+
+
+FP8_MUTANTS = {
+    "e4m3_bias_8": ("decode_e4m3fn", _e4m3_bias8),
+    "e4m3_subnormals_flushed": ("decode_e4m3fn", _e4m3_flush_subnormals),
+    "e5m2_read_as_e4m3": ("decode_e5m2", fp8mod.decode_e4m3fn),
+    "fp8kv_scales_swapped": ("decode_fp8kv", _fp8kv_scales_swapped),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTANTS))
+def test_planted_fp8_mistake_is_caught(name, monkeypatch):
+    import oracle
+    attr, repl = FP8_MUTANTS[name]
+    monkeypatch.setitem(fp8mod.__dict__, "_orig_e4m3", fp8mod.decode_e4m3fn)
+    monkeypatch.setattr(fp8mod, attr, repl)
+    monkeypatch.setattr(oracle, attr, repl)
+    failed = _run_all_checks()
+    assert failed, f"mutant {name} passed every pin"

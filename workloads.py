@@ -258,6 +258,48 @@ def paged_decode_inputs(n_seq, Hq, Hkv, d, lens, page_size, *, seed, device="cpu
     return q, k_pool, v_pool, table, lens_t, layout
 
 
+# FP8 KV cache: the two formats and their largest finite values (OCP 8-bit floating point).
+FP8_DTYPES = {"e4m3fn": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+FP8_MAX = {"e4m3fn": 448.0, "e5m2": 57344.0}
+
+
+def to_fp8_codes(x: torch.Tensor, fmt: str, scale: float | None = None):
+    """Quantise a float tensor to FP8 codes (uint8) with one per-tensor scale: torch's conversion
+    (round to nearest even) of x / scale.  The scale defaults to max |x| over the finite entries
+    divided by the format's largest finite value, so the largest entry maps to it; NaN stays NaN.
+    Returns (codes, scale)."""
+    xf = x.to(torch.float32)
+    if scale is None:
+        fin = torch.isfinite(xf)
+        amax = float(xf[fin].abs().max()) if bool(fin.any()) else 1.0
+        scale = amax / FP8_MAX[fmt] if amax > 0 else 1.0
+    codes = (xf / scale).to(FP8_DTYPES[fmt]).view(torch.uint8)
+    return codes, float(scale)
+
+
+def fp8_decode_inputs(n_seq, Hq, Hkv, d, lens, fmt, *, seed, device="cpu", max_gap=255, shuffle=True):
+    """decode_inputs with the pools held as FP8 codes: the same draws in fp32, q rounded to bf16,
+    K and V quantised per pool (to_fp8_codes; NaN gap rows become NaN codes).  Returns q,
+    k_codes, v_codes, offsets, lens, layout, k_scale, v_scale."""
+    q, kp, vp, offs, lens_t, layout = decode_inputs(n_seq, Hq, Hkv, d, lens, seed=seed, device=device,
+                                                    dtype=torch.float32, max_gap=max_gap, shuffle=shuffle)
+    kc, ks = to_fp8_codes(kp, fmt)
+    vc, vs = to_fp8_codes(vp, fmt)
+    return q.to(torch.bfloat16), kc, vc, offs, lens_t, layout, ks, vs
+
+
+def fp8_paged_decode_inputs(n_seq, Hq, Hkv, d, lens, page_size, fmt, *, seed, device="cpu", extra_pages=0,
+                            stride=None):
+    """paged_decode_inputs with FP8 pools, as fp8_decode_inputs.  Returns q, k_codes, v_codes,
+    block table, lens, layout, k_scale, v_scale."""
+    q, kp, vp, table, lens_t, layout = paged_decode_inputs(n_seq, Hq, Hkv, d, lens, page_size, seed=seed,
+                                                           device=device, dtype=torch.float32,
+                                                           extra_pages=extra_pages, stride=stride)
+    kc, ks = to_fp8_codes(kp, fmt)
+    vc, vs = to_fp8_codes(vp, fmt)
+    return q.to(torch.bfloat16), kc, vc, table, lens_t, layout, ks, vs
+
+
 def varlen_inputs(lq, lk, Hq, Hkv, d, *, seed, device="cpu", dtype=torch.bfloat16, max_gap=37,
                   poison=float("nan")):
     """Ragged prefill inputs: q [sum(lq), Hq, d] packed by cu_seqlens; k_pool, v_pool [T, Hkv, d]
