@@ -16,10 +16,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattnfwd.so")
 
 ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(6)
+KV_FORMATS = {"e4m3fn": 1, "e5m2": 2}  # attn_kv_format
 
 EXPORTS = ["attn_fwd", "attn_fwd_f32", "attn_fwd_varlen", "attn_decode_workspace_size", "attn_decode",
            "attn_decode_paged", "attn_status_str", "attn_fwd_plan", "attn_fwd_schedule", "attn_fwd_varlen_schedule",
-           "attn_decode_plan", "attn_bwd_workspace_size", "attn_bwd"]
+           "attn_decode_plan", "attn_bwd_workspace_size", "attn_bwd", "attn_decode_fp8", "attn_decode_paged_fp8"]
 
 
 class FwdPlanInfo(ctypes.Structure):
@@ -54,6 +55,12 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_paged.argtypes = [vp, vp, vp, vp, i32, i32, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                                     vp, sz, vp]
     L.attn_decode_paged.restype = i32
+    L.attn_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, i32, f32, i32, f32, f32,
+                                  vp, sz, vp]
+    L.attn_decode_fp8.restype = i32
+    L.attn_decode_paged_fp8.argtypes = [vp, vp, vp, vp, i32, i32, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+                                        i32, f32, f32, vp, sz, vp]
+    L.attn_decode_paged_fp8.restype = i32
     L.attn_bwd_workspace_size.argtypes = [i32, i32, i32]
     L.attn_bwd_workspace_size.restype = sz
     L.attn_bwd.argtypes = [vp] * 9 + [i32] * 8 + [f32, vp, sz, vp]
@@ -196,17 +203,34 @@ def attn_fwd_varlen(q, k_pool, v_pool, cu_seqlens_q, kv_offsets, kv_lens, *, max
     return (o, lse) if return_lse else o
 
 
+def _kv_format(q, k_pool, v_pool, kv_format, k_scale, v_scale):
+    """0 for bf16 pools; the attn_kv_format code for uint8 (FP8 code) pools."""
+    import torch
+    if q.dtype != torch.bfloat16:
+        raise ValueError("decode takes a bfloat16 q")
+    if k_pool.dtype == torch.bfloat16 and v_pool.dtype == torch.bfloat16:
+        if kv_format is not None:
+            raise ValueError("kv_format applies to uint8 (FP8 code) pools")
+        return 0
+    if k_pool.dtype == torch.uint8 and v_pool.dtype == torch.uint8:
+        if kv_format not in KV_FORMATS or k_scale is None or v_scale is None:
+            raise ValueError("FP8 pools need kv_format ('e4m3fn' or 'e5m2'), k_scale and v_scale")
+        return KV_FORMATS[kv_format]
+    raise ValueError("pools must both be bfloat16, or both uint8 FP8 codes")
+
+
 def attn_decode(q, k_pool, v_pool, offsets, lens, *, max_len: int, window: int = 0, scale: float | None = None,
-                return_lse: bool = False, workspace=None, out=None, lse_out=None):
+                return_lse: bool = False, workspace=None, out=None, lse_out=None, kv_format: str | None = None,
+                k_scale: float | None = None, v_scale: float | None = None):
     """Decode one query token per sequence against a pooled KV cache.
 
-    q [N, Hq, d] bf16; k_pool, v_pool [T, Hkv, d] bf16; offsets int64 [N] (first pool row of
-    each sequence); lens int32 [N]; max_len >= max(lens).  Returns O [N, Hq, d] bf16 and,
-    when ``return_lse``, LSE [N, Hq] fp32."""
+    q [N, Hq, d] bf16; k_pool, v_pool [T, Hkv, d] bf16, or uint8 FP8 codes with ``kv_format``
+    ('e4m3fn' / 'e5m2') and per-pool ``k_scale`` / ``v_scale`` (real value = scale * code value);
+    offsets int64 [N] (first pool row of each sequence); lens int32 [N]; max_len >= max(lens).
+    Returns O [N, Hq, d] bf16 and, when ``return_lse``, LSE [N, Hq] fp32."""
     import torch
     _require_gpu(q, k_pool, v_pool, offsets, lens)
-    if q.dtype != torch.bfloat16 or k_pool.dtype != torch.bfloat16 or v_pool.dtype != torch.bfloat16:
-        raise ValueError("decode takes bfloat16 q and pools")
+    fmt = _kv_format(q, k_pool, v_pool, kv_format, k_scale, v_scale)
     if offsets.dtype != torch.int64 or lens.dtype != torch.int32:
         raise ValueError("offsets must be int64 and lens int32")
     N, Hq, d = q.shape
@@ -222,26 +246,30 @@ def attn_decode(q, k_pool, v_pool, offsets, lens, *, max_len: int, window: int =
     lse = None
     if return_lse:
         lse = torch.empty((N, Hq), device=q.device, dtype=torch.float32) if lse_out is None else lse_out
-    _check(lib().attn_decode(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), offsets.data_ptr(), lens.data_ptr(),
-                             o.data_ptr(), lse.data_ptr() if lse is not None else None, N, Hq, Hkv, d, T,
-                             int(max_len), int(window), float(scale), workspace.data_ptr(),
-                             workspace.numel() * workspace.element_size(), _stream()))
+    args = (q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), offsets.data_ptr(), lens.data_ptr(), o.data_ptr(),
+            lse.data_ptr() if lse is not None else None, N, Hq, Hkv, d, T, int(max_len), int(window), float(scale))
+    tail = (workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream())
+    if fmt == 0:
+        _check(lib().attn_decode(*args, *tail))
+    else:
+        _check(lib().attn_decode_fp8(*args, fmt, float(k_scale), float(v_scale), *tail))
     return (o, lse) if return_lse else o
 
 
 def attn_decode_paged(q, k_pool, v_pool, block_table, lens, *, page_size: int, max_len: int, window: int = 0,
                       scale: float | None = None, return_lse: bool = False, workspace=None, out=None,
-                      lse_out=None):
+                      lse_out=None, kv_format: str | None = None, k_scale: float | None = None,
+                      v_scale: float | None = None):
     """Decode one query token per sequence against a paged KV cache.
 
     q [N, Hq, d] bf16; k_pool, v_pool [pool_pages * page_size, Hkv, d] bf16 (physical page p
     is rows p * page_size .. + page_size - 1); block_table int32 [N, table_stride] (entry j of
     sequence s: the page holding its tokens j * page_size .. + page_size - 1); lens int32 [N];
-    max_len >= max(lens).  Returns O [N, Hq, d] bf16 and, when ``return_lse``, LSE [N, Hq]."""
+    max_len >= max(lens).  FP8 pools as attn_decode.  Returns O [N, Hq, d] bf16 and, when
+    ``return_lse``, LSE [N, Hq]."""
     import torch
     _require_gpu(q, k_pool, v_pool, block_table, lens)
-    if q.dtype != torch.bfloat16 or k_pool.dtype != torch.bfloat16 or v_pool.dtype != torch.bfloat16:
-        raise ValueError("decode takes bfloat16 q and pools")
+    fmt = _kv_format(q, k_pool, v_pool, kv_format, k_scale, v_scale)
     if block_table.dtype != torch.int32 or lens.dtype != torch.int32:
         raise ValueError("block_table and lens must be int32")
     if block_table.dim() != 2 or not block_table.is_contiguous():
@@ -262,11 +290,14 @@ def attn_decode_paged(q, k_pool, v_pool, block_table, lens, *, page_size: int, m
     lse = None
     if return_lse:
         lse = torch.empty((N, Hq), device=q.device, dtype=torch.float32) if lse_out is None else lse_out
-    _check(lib().attn_decode_paged(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), block_table.data_ptr(),
-                                   int(block_table.shape[1]), int(page_size), T // page_size, lens.data_ptr(),
-                                   o.data_ptr(), lse.data_ptr() if lse is not None else None, N, Hq, Hkv, d,
-                                   int(max_len), int(window), float(scale), workspace.data_ptr(),
-                                   workspace.numel() * workspace.element_size(), _stream()))
+    args = (q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), block_table.data_ptr(), int(block_table.shape[1]),
+            int(page_size), T // page_size, lens.data_ptr(), o.data_ptr(), lse.data_ptr() if lse is not None else None,
+            N, Hq, Hkv, d, int(max_len), int(window), float(scale))
+    tail = (workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream())
+    if fmt == 0:
+        _check(lib().attn_decode_paged(*args, *tail))
+    else:
+        _check(lib().attn_decode_paged_fp8(*args, fmt, float(k_scale), float(v_scale), *tail))
     return (o, lse) if return_lse else o
 
 

@@ -128,14 +128,18 @@ size_t attn_decode_workspace_size(int n_seq, int Hq, int Hkv, int d, int max_len
 namespace {
 
 // Shared by the contiguous and the paged entry points: everything but the addressing of the pool.
+// a.kv_fmt selects the pool's element format; k_scale and v_scale apply to fp8 pools only.
 int decode_common(const void* q, const void* k_pool, const void* v_pool, const int32_t* lens, void* o,
                   float* lse, int n_seq, int Hq, int Hkv, int d, int max_len, int window, float scale,
-                  void* workspace, size_t workspace_bytes, void* stream, DecArgs& a) {
+                  float k_scale, float v_scale, void* workspace, size_t workspace_bytes, void* stream, DecArgs& a) {
   if (!q || !k_pool || !v_pool || !lens || !o) return ATTN_ERR_NULL;
   if (n_seq <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_len < 1 || window < 0) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
+  if (a.kv_fmt < 0 || a.kv_fmt > 2) return ATTN_ERR_UNSUPPORTED;
+  if (a.kv_fmt != 0 && !(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+    return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
   if (n_seq > 65535) return ATTN_ERR_SHAPE;
   const int group = Hq / Hkv;
@@ -151,7 +155,7 @@ int decode_common(const void* q, const void* k_pool, const void* v_pool, const i
   const DecWorkspaceLayout lay = decode_workspace_layout(n_seq, Hq, Hkv, d);
   if (workspace == nullptr || workspace_bytes < lay.total) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_UNSUPPORTED;
-  const int workers = decode_workers(d);
+  const int workers = decode_workers(d, a.kv_fmt != 0);
   if (workers <= 0) return ATTN_ERR_HIP;
 
   a.q = q;
@@ -178,6 +182,12 @@ int decode_common(const void* q, const void* k_pool, const void* v_pool, const i
   a.nh = decode_heads_per_slot(Hq, Hkv);
   a.teams = decode_teams(workers, rows);
   set_scale(scale, a.c, a.qmode);
+  if (a.kv_fmt != 0) {
+    if (a.qmode != 2) a.c *= k_scale;  // scores of an fp8 pool: scale * k_scale * (q . code values)
+    a.v_scale = v_scale;
+  } else {
+    a.v_scale = 1.f;
+  }
   const hipError_t e = launch_decode(a, d, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
@@ -195,14 +205,34 @@ int attn_decode(const void* q, const void* k_pool, const void* v_pool, const int
   a.offsets = offsets;
   a.pool_rows = pool_rows;
   a.paged = 0;
-  return decode_common(q, k_pool, v_pool, lens, o, lse, n_seq, Hq, Hkv, d, max_len, window, scale, workspace,
-                       workspace_bytes, stream, a);
+  return decode_common(q, k_pool, v_pool, lens, o, lse, n_seq, Hq, Hkv, d, max_len, window, scale, 1.f, 1.f,
+                       workspace, workspace_bytes, stream, a);
 }
 
-int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
-                      int table_stride, int page_size, int64_t pool_pages, const int32_t* lens, void* o, float* lse,
-                      int n_seq, int Hq, int Hkv, int d, int max_len, int window, float scale, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+int attn_decode_fp8(const void* q, const void* k_pool, const void* v_pool, const int64_t* offsets,
+                    const int32_t* lens, void* o, float* lse, int n_seq, int Hq, int Hkv, int d, int64_t pool_rows,
+                    int max_len, int window, float scale, int kv_format, float k_scale, float v_scale,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!offsets) return ATTN_ERR_NULL;
+  if (pool_rows < 0) return ATTN_ERR_SHAPE;
+  if (kv_format != ATTN_KV_E4M3 && kv_format != ATTN_KV_E5M2) return ATTN_ERR_UNSUPPORTED;
+  DecArgs a{};
+  a.offsets = offsets;
+  a.pool_rows = pool_rows;
+  a.paged = 0;
+  a.kv_fmt = kv_format;
+  return decode_common(q, k_pool, v_pool, lens, o, lse, n_seq, Hq, Hkv, d, max_len, window, scale, k_scale,
+                       v_scale, workspace, workspace_bytes, stream, a);
+}
+
+}  // extern "C"
+
+namespace {
+
+int decode_paged_common(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                        int table_stride, int page_size, int64_t pool_pages, const int32_t* lens, void* o, float* lse,
+                        int n_seq, int Hq, int Hkv, int d, int max_len, int window, float scale, int kv_format,
+                        float k_scale, float v_scale, void* workspace, size_t workspace_bytes, void* stream) {
   if (!block_table) return ATTN_ERR_NULL;
   if (page_size < 1 || pool_pages < 0 || max_len < 1 || table_stride < 1) return ATTN_ERR_SHAPE;
   // every token a valid sequence may hold has a table entry
@@ -218,8 +248,33 @@ int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool, con
   a.pool_pages = pool_pages;
   a.pool_rows = pool_pages * page_size;
   a.paged = 1;
-  return decode_common(q, k_pool, v_pool, lens, o, lse, n_seq, Hq, Hkv, d, max_len, window, scale, workspace,
-                       workspace_bytes, stream, a);
+  a.kv_fmt = kv_format;
+  return decode_common(q, k_pool, v_pool, lens, o, lse, n_seq, Hq, Hkv, d, max_len, window, scale, k_scale,
+                       v_scale, workspace, workspace_bytes, stream, a);
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                      int table_stride, int page_size, int64_t pool_pages, const int32_t* lens, void* o, float* lse,
+                      int n_seq, int Hq, int Hkv, int d, int max_len, int window, float scale, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return decode_paged_common(q, k_pool, v_pool, block_table, table_stride, page_size, pool_pages, lens, o, lse,
+                             n_seq, Hq, Hkv, d, max_len, window, scale, 0, 1.f, 1.f, workspace, workspace_bytes,
+                             stream);
+}
+
+int attn_decode_paged_fp8(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                          int table_stride, int page_size, int64_t pool_pages, const int32_t* lens, void* o,
+                          float* lse, int n_seq, int Hq, int Hkv, int d, int max_len, int window, float scale,
+                          int kv_format, float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (kv_format != ATTN_KV_E4M3 && kv_format != ATTN_KV_E5M2) return ATTN_ERR_UNSUPPORTED;
+  return decode_paged_common(q, k_pool, v_pool, block_table, table_stride, page_size, pool_pages, lens, o, lse,
+                             n_seq, Hq, Hkv, d, max_len, window, scale, kv_format, k_scale, v_scale, workspace,
+                             workspace_bytes, stream);
 }
 
 size_t attn_bwd_workspace_size(int B, int Hq, int Lq) {

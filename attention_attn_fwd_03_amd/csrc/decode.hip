@@ -36,12 +36,23 @@ namespace attnfwd {
 
 typedef __attribute__((address_space(3))) void lds_void_d;
 
-template <int D>
+// KV element formats of the pool: bf16, or an 8-bit float code (OCP E4M3 / E5M2) with one scale
+// per pool.
+enum KvFormat : int { kKvBf16 = 0, kKvE4M3 = 1, kKvE5M2 = 2 };
+
+template <int D, int KV = kKvBf16>
 struct DecCfg {
-  static constexpr int ROWB = D * 2;            // bytes of one head's K or V row
-  static constexpr int CH = D / 8;              // 16-byte chunks per row
-  static constexpr int KPB = ROWB + 16;         // K row pitch in LDS: A-operand reads of 16 rows hit distinct banks
-  static constexpr int VPB = ROWB + 64;         // V row pitch: transposed reads of 4 rows hit distinct banks
+  static constexpr bool FP8 = KV != kKvBf16;
+  static constexpr int ROWB = FP8 ? D : D * 2;  // bytes of one head's K or V row
+  static constexpr int CH = ROWB / 16;          // 16-byte chunks per row
+  // Row pitches in LDS are whole 16-byte chunks (each lane of a wave-wide load fills one chunk).
+  // K: the bf16 A-operand reads of 16 rows x 16 bytes hit distinct banks (the fp8 reads of 32 rows
+  // x 8 bytes meet in pairs, rows r and r + 16; K is a small share of the LDS reads).  V: the
+  // transposed reads of a half-wave (bf16: 4 rows x 64 bytes; fp8: 8 rows x 32 bytes) cover the
+  // 256-byte bank space once.
+  static constexpr int KPB = ROWB + 16;
+  static constexpr int VPB = FP8 ? ROWB + 32 : ROWB + 64;
+  static_assert(KPB % 16 == 0 && VPB % 16 == 0, "whole chunks per LDS row");
   static constexpr int K_STAGE = (kDecodeBlockRows * KPB + 1023) / 1024 * 1024;
   static constexpr int V_STAGE = kDecodeBlockRows * VPB;
   static constexpr int K_LOADS = K_STAGE / 1024;  // wave-wide 16-byte-per-lane loads per stage
@@ -122,25 +133,60 @@ __device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t rs, unsigned 
 // token r / pack, KV head r % pack, i.e. byte (r / pack) * token_bytes + (r % pack) * ROWB of the
 // block's buffer.  Pad slots take an offset past any buffer (the hardware returns zeros and
 // reads nothing).
-template <int N, int PITCH, int CH, int ROWB>
+// With SWAP23, LDS row r holds block row r with bits 2 and 3 exchanged (the fp8 V stage: an
+// 8-row transposed read then returns the rows in the order of the P operand, see below).
+template <int N, int PITCH, int CH, int ROWB, bool SWAP23 = false>
 __device__ __forceinline__ void stage_offsets(unsigned (&voff)[N], int lane, int pack, int token_bytes) {
 #pragma unroll
   for (int j = 0; j < N; ++j) {
     const int o = j * 1024 + 16 * lane;
     const int r = o / PITCH, ch = (o % PITCH) / 16;
+    const int src = SWAP23 ? (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1) : r;
     voff[j] = (r < kDecodeBlockRows && ch < CH)
-                  ? (unsigned)((r / pack) * token_bytes + (r % pack) * ROWB + ch * 16)
+                  ? (unsigned)((src / pack) * token_bytes + (src % pack) * ROWB + ch * 16)
                   : 0x80000000u;
   }
 }
 
-// PAGED selects the pool addressing at compile time, so the contiguous kernel carries none of the
-// page-table code.
-template <int D, bool PAGED>
+// Eight 8-bit float codes (bytes 0..7 of w) as eight bf16 values; exact for both formats.
+template <int KV>
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 w) {
+  bf16x2 p0, p1, p2, p3;
+  if constexpr (KV == kKvE4M3) {
+    p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false);
+    p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true);
+    p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false);
+    p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true);
+  } else {
+    p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w[0], 1.0f, false);
+    p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w[0], 1.0f, true);
+    p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w[1], 1.0f, false);
+    p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w[1], 1.0f, true);
+  }
+  const u32x4 r = {__builtin_bit_cast(unsigned, p0), __builtin_bit_cast(unsigned, p1), __builtin_bit_cast(unsigned, p2),
+                   __builtin_bit_cast(unsigned, p3)};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+// ds_read_b64_tr_b8: inside each 16-lane group, lane i receives byte i%8 of the 8-byte pieces
+// addressed by lanes i/8 + 2c, c = 0..7 (checked on the hardware with a lane-layout probe).  If
+// lane j of the group addresses row r0 + j/2, bytes c0 + 8*(j%2) .. +7 of a row-major byte
+// matrix, lane i receives rows r0 .. r0+7 of column c0 + i.
+__device__ __forceinline__ u32x2 lds_read_tr8(const void* lds_generic_ptr) {
+  const lds_i32x2* p = (const lds_i32x2*)(__attribute__((address_space(3))) unsigned char*)lds_generic_ptr;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(const_cast<lds_i32x2*>(p)));
+}
+
+// PAGED selects the pool addressing and KV the pool's element format at compile time, so the
+// contiguous bf16 kernel carries none of the page-table or conversion code.
+template <int D, bool PAGED, int KV>
 // At d = 128 the two LDS stages (38 KB) allow four waves per CU, one per SIMD, so the wave may use
 // the whole register file; at d = 64 two waves per SIMD fit.
 __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecArgs a) {
-  using C = DecCfg<D>;
+  using C = DecCfg<D, KV>;
   // Each pipeline stage is its own LDS object, so reading one does not wait for loads into the other.
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[C::K_STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[C::K_STAGE];
@@ -226,11 +272,17 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
   const int token_bytes = a.Hkv * C::ROWB;  // bytes between consecutive tokens of the pool
   unsigned k_voff[C::K_LOADS], v_voff[C::V_LOADS];
   stage_offsets<C::K_LOADS, C::KPB, C::CH, C::ROWB>(k_voff, lane, pack, token_bytes);
-  stage_offsets<C::V_LOADS, C::VPB, C::CH, C::ROWB>(v_voff, lane, pack, token_bytes);
-  // K A operand: lane holds K[row = col][16*ks + 8*h .. +7] at LDS byte col*KPB + 32*ks + 16*h.
-  const int k_lane = col * C::KPB + h * 16;
-  // ds_read_b64_tr_b16 addressing of the V^T operand (see attn_device.hpp).
-  const int v_lane = (4 * h + ((lane & 15) >> 2)) * C::VPB + ((lane >> 4) & 1) * 32 + (lane & 3) * 8;
+  stage_offsets<C::V_LOADS, C::VPB, C::CH, C::ROWB, C::FP8>(v_voff, lane, pack, token_bytes);
+  // K A operand: lane holds K[row = col][16*ks + 8*h .. +7], at LDS byte col*KPB + 32*ks + 16*h
+  // (bf16) or col*KPB + 16*ks + 8*h (fp8 codes, converted in registers).
+  const int k_lane = col * C::KPB + h * (C::FP8 ? 8 : 16);
+  // V^T operand.  bf16: ds_read_b64_tr_b16 addressing (see attn_device.hpp).  fp8: one
+  // ds_read_b64_tr_b8 per operand, group g = lane/16 reading rows 8*(g/2) .. +7 and columns
+  // 16*(g%2) .. +15 of the 32-column slice: lane l gets rows 16*j + 8*h .. +7 of column l%32.  The
+  // stage holds block row swap23(r) at LDS row r, so these are block rows 16*j + 8*(e/4) + 4*h +
+  // e%4 for byte e -- the rows the P operand holds at k = 8*h + e.
+  const int v_lane = C::FP8 ? (8 * (lane >> 5) + ((lane & 15) >> 1)) * C::VPB + ((lane >> 4) & 1) * 16 + (lane & 1) * 8
+                            : (4 * h + ((lane & 15) >> 2)) * C::VPB + ((lane >> 4) & 1) * 32 + (lane & 3) * 8;
   // S^T register i of this lane holds block row r(i) = 8*(i/4) + 4*h + i%4 against query head
   // qbase + col.  In the packed layout only rows of the head's own KV group count.
   unsigned head_ok = 0xFFFFu;
@@ -333,8 +385,14 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
 #pragma unroll
       for (int i = 0; i < 16; ++i) sv[0][i] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < QL; ++ks)
-        sv[0] = mfma_32x32x16(__builtin_bit_cast(bf16x8, *(const u32x4*)(Ks + ks * 32)), qf[ks], sv[0]);
+      for (int ks = 0; ks < QL; ++ks) {
+        bf16x8 kf;
+        if constexpr (C::FP8)
+          kf = fp8x8_to_bf16<KV>(*(const u32x2*)(Ks + ks * 16));
+        else
+          kf = __builtin_bit_cast(bf16x8, *(const u32x4*)(Ks + ks * 32));
+        sv[0] = mfma_32x32x16(kf, qf[ks], sv[0]);
+      }
       // The piece ends inside this block (only at the sequence's end), or the block starts
       // before the first visible key (only a paged cache under a window).
       if (t0 + tpb > t_end || (PAGED && t0 < vis_lo)) {
@@ -359,10 +417,15 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
         const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          const u32x2 r0 = lds_read_tr16(Vs + 16 * j * C::VPB + dt * 64);
-          const u32x2 r1 = lds_read_tr16(Vs + (16 * j + 8) * C::VPB + dt * 64);
-          const u32x4 vw = __builtin_shufflevector(r0, r1, 0, 1, 2, 3);
-          o[dt] = mfma_32x32x16(__builtin_bit_cast(bf16x8, vw), pb, o[dt]);
+          bf16x8 vf;
+          if constexpr (C::FP8) {
+            vf = fp8x8_to_bf16<KV>(lds_read_tr8(Vs + 16 * j * C::VPB + dt * 32));
+          } else {
+            const u32x2 r0 = lds_read_tr16(Vs + 16 * j * C::VPB + dt * 64);
+            const u32x2 r1 = lds_read_tr16(Vs + (16 * j + 8) * C::VPB + dt * 64);
+            vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3));
+          }
+          o[dt] = mfma_32x32x16(vf, pb, o[dt]);
         }
       }
     };
@@ -385,17 +448,19 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));  // no load may still target LDS past this point
 
-    // Partial of this (team, sequence, row): unnormalised O relative to m, plus (m, l).
+    // Partial of this (team, sequence, row): unnormalised O relative to m, plus (m, l).  An fp8
+    // pool's V scale is applied here (the K scale is folded into c).
     const float l_tot = pair_sum(st.l);
     if (q_ok) {
       const size_t idx = ((size_t)(team + s) * a.rows + u) * a.nh + col;
       float* wo = a.ws_o + idx * D;
+      const float vs = C::FP8 ? a.v_scale : 1.f;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           *(f32x4*)(wo + dt * 32 + g * 8 + h * 4) =
-              f32x4{o[dt][4 * g], o[dt][4 * g + 1], o[dt][4 * g + 2], o[dt][4 * g + 3]};
+              f32x4{o[dt][4 * g] * vs, o[dt][4 * g + 1] * vs, o[dt][4 * g + 2] * vs, o[dt][4 * g + 3] * vs};
       if (h == 0) {  // a piece that met a bad page entry is marked with NaN for the merge
         a.ws_ml[2 * idx] = bad ? NAN : st.m;
         a.ws_ml[2 * idx + 1] = bad ? NAN : l_tot;
@@ -514,10 +579,18 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
     a.lse[(size_t)s * a.Hq + hq] = bad ? NAN : L > 0.f ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
 }
 
-template __global__ void decode_split_kernel<64, false>(DecArgs);
-template __global__ void decode_split_kernel<128, false>(DecArgs);
-template __global__ void decode_split_kernel<64, true>(DecArgs);
-template __global__ void decode_split_kernel<128, true>(DecArgs);
+template __global__ void decode_split_kernel<64, false, kKvBf16>(DecArgs);
+template __global__ void decode_split_kernel<128, false, kKvBf16>(DecArgs);
+template __global__ void decode_split_kernel<64, true, kKvBf16>(DecArgs);
+template __global__ void decode_split_kernel<128, true, kKvBf16>(DecArgs);
+template __global__ void decode_split_kernel<64, false, kKvE4M3>(DecArgs);
+template __global__ void decode_split_kernel<128, false, kKvE4M3>(DecArgs);
+template __global__ void decode_split_kernel<64, true, kKvE4M3>(DecArgs);
+template __global__ void decode_split_kernel<128, true, kKvE4M3>(DecArgs);
+template __global__ void decode_split_kernel<64, false, kKvE5M2>(DecArgs);
+template __global__ void decode_split_kernel<128, false, kKvE5M2>(DecArgs);
+template __global__ void decode_split_kernel<64, true, kKvE5M2>(DecArgs);
+template __global__ void decode_split_kernel<128, true, kKvE5M2>(DecArgs);
 template __global__ void decode_merge_kernel<64>(DecArgs);
 template __global__ void decode_merge_kernel<128>(DecArgs);
 
@@ -534,37 +607,56 @@ DecWorkspaceLayout decode_workspace_layout(int n_seq, int Hq, int Hkv, int d) {
   return l;
 }
 
-int decode_workers(int d) {
-  static std::atomic<int> cache[2][64];
+int decode_workers(int d, bool fp8) {
+  static std::atomic<int> cache[2][2][64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
-  std::atomic<int>& slot = cache[d == 128 ? 1 : 0][dev];
+  std::atomic<int>& slot = cache[d == 128 ? 1 : 0][fp8 ? 1 : 0][dev];
   int w = slot.load(std::memory_order_relaxed);
   if (w > 0) return w;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-  const hipError_t e =
-      d == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<128, false>, 64, 0)
-               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<64, false>, 64, 0);
+  hipError_t e;
+  if (fp8)
+    e = d == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<128, false, kKvE4M3>, 64, 0)
+                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<64, false, kKvE4M3>, 64, 0);
+  else
+    e = d == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<128, false, kKvBf16>, 64, 0)
+                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<64, false, kKvBf16>, 64, 0);
   if (e != hipSuccess || cus <= 0 || per_cu <= 0) return -1;
-  if (per_cu > kDecodeWorkersPerCu) per_cu = kDecodeWorkersPerCu;
+  const int cap = fp8 ? kDecodeWorkersPerCuFp8 : kDecodeWorkersPerCu;
+  if (per_cu > cap) per_cu = cap;
   w = cus * per_cu < kDecodeMaxWorkers ? cus * per_cu : kDecodeMaxWorkers;
   slot.store(w, std::memory_order_relaxed);
   return w;
 }
 
-hipError_t launch_decode(const DecArgs& a, int d, hipStream_t stream) {
+template <int D, int KV>
+void launch_split(const DecArgs& a, dim3 grid, hipStream_t stream) {
+  if (a.paged)
+    hipLaunchKernelGGL((decode_split_kernel<D, true, KV>), grid, dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<D, false, KV>), grid, dim3(64), 0, stream, a);
+}
+
+template <int D>
+void launch_decode_d(const DecArgs& a, hipStream_t stream) {
   const dim3 g1((unsigned)(a.teams * a.rows));
   const dim3 g2((unsigned)a.Hq, (unsigned)a.n_seq);
-  if (d == 64) {
-    if (a.paged) hipLaunchKernelGGL((decode_split_kernel<64, true>), g1, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL((decode_split_kernel<64, false>), g1, dim3(64), 0, stream, a);
-    hipLaunchKernelGGL(decode_merge_kernel<64>, g2, dim3(64), 0, stream, a);
-  } else {
-    if (a.paged) hipLaunchKernelGGL((decode_split_kernel<128, true>), g1, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL((decode_split_kernel<128, false>), g1, dim3(64), 0, stream, a);
-    hipLaunchKernelGGL(decode_merge_kernel<128>, g2, dim3(64), 0, stream, a);
-  }
+  if (a.kv_fmt == kKvE4M3)
+    launch_split<D, kKvE4M3>(a, g1, stream);
+  else if (a.kv_fmt == kKvE5M2)
+    launch_split<D, kKvE5M2>(a, g1, stream);
+  else
+    launch_split<D, kKvBf16>(a, g1, stream);
+  hipLaunchKernelGGL(decode_merge_kernel<D>, g2, dim3(64), 0, stream, a);
+}
+
+hipError_t launch_decode(const DecArgs& a, int d, hipStream_t stream) {
+  if (d == 64)
+    launch_decode_d<64>(a, stream);
+  else
+    launch_decode_d<128>(a, stream);
   return hipGetLastError();
 }
 

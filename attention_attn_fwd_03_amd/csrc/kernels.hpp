@@ -54,8 +54,10 @@ struct DecArgs {
   int rows;   // rows per sequence (1 in the packed layout, else Hkv * hblocks)
   int nh;     // query heads per partial slot
   int teams;  // teams of `rows` workers in the split launch
-  float c;
+  float c;       // |scale| * log2(e) (times an fp8 pool's K scale), or 1 when scale = 0
   int qmode;
+  int kv_fmt;    // pool element format: 0 bf16, 1 E4M3, 2 E5M2
+  float v_scale; // fp8 pools: V scale (real value = v_scale * code value)
 };
 
 // Backward (bf16): q, o, dout, dq are [B, Hq, Lq, d]; k, v, dk, dv are [B, Hkv, Lk, d]; lse is
@@ -94,7 +96,8 @@ int prefill_lds_bytes(bool f32, int d);
 hipError_t launch_prefill(const FwdArgs& a, bool f32, int d, hipStream_t stream);
 hipError_t launch_prefill_varlen(const FwdArgs& a, int d, hipStream_t stream);
 
-int decode_workers(int d);  // one resident round of split workers on the current device, or < 0
+// One resident round of split workers on the current device (bf16 or fp8 pool), or < 0.
+int decode_workers(int d, bool fp8 = false);
 hipError_t launch_decode(const DecArgs& a, int d, hipStream_t stream);
 
 hipError_t launch_backward(const BwdArgs& a, int d, hipStream_t stream);

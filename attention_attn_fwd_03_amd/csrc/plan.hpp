@@ -163,6 +163,10 @@ constexpr int kDecodeMaxWorkers = 2048;  // workers per launch, at most (one res
 // four (measured at d = 128, GQA and MQA batches; 2 and 3 per CU both beat 4, and counts that are
 // not a multiple of the CU count load the CUs unevenly and are slower still).
 constexpr int kDecodeWorkersPerCu = 3;
+// An FP8 pool halves the bytes per block while the per-block work grows (the codes are converted
+// to bf16 in registers): four workers per CU, one per SIMD, are about 9% faster than three on the
+// GQA batch (equal on MQA).
+constexpr int kDecodeWorkersPerCuFp8 = 4;
 
 ATTN_HD int decode_head_blocks(int group) { return (group + 31) / 32; }
 // KV heads per block: Hkv in the packed layout, 1 in the row layout.

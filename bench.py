@@ -84,10 +84,10 @@ def prefill_bytes(c) -> int:
     return (2 * c.B * c.Hq * c.Lq * c.d + 2 * c.B * c.Hkv * c.Lk * c.d) * esz + 4 * c.B * c.Hq * c.Lq
 
 
-def decode_bytes(n_tokens: int, n_seq: int, Hq: int, Hkv: int, d: int) -> int:
-    """One read of every live K and V row, one read of q, one write of O (bf16) and LSE (fp32),
-    plus offsets and lens."""
-    return 2 * n_tokens * Hkv * d * 2 + 2 * n_seq * Hq * d * 2 + 4 * n_seq * Hq + 12 * n_seq
+def decode_bytes(n_tokens: int, n_seq: int, Hq: int, Hkv: int, d: int, kv_bytes: int = 2) -> int:
+    """One read of every live K and V row (kv_bytes per element: 2 for bf16, 1 for an FP8 cache),
+    one read of q, one write of O (bf16) and LSE (fp32), plus offsets and lens."""
+    return 2 * n_tokens * Hkv * d * kv_bytes + 2 * n_seq * Hq * d * 2 + 4 * n_seq * Hq + 12 * n_seq
 
 
 def decode_flops(n_tokens: int, Hq: int, Hkv: int, d: int) -> int:
@@ -341,13 +341,13 @@ def main():
                      "per_launch": f"{pflops / 1e9:.1f} GFLOP useful (4*d per visible pair, 64 heads)"},
         "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                            "kernels": "decode_split_kernel<128, false> + decode_merge_kernel<128>",
+                            "kernels": "decode_split_kernel<128, false, 0> + decode_merge_kernel<128>",
                             "per_launch": f"{dbytes / 1e9:.3f} GB (one read of live K/V rows + q, O, LSE)"},
     }
     traffic = load_traffic()
     if traffic is not None:
         kp = traffic["kernels"].get("fwd_bf16_kernel<128, 32, false>")
-        ks = traffic["kernels"].get("decode_split_kernel<128, false>")
+        ks = traffic["kernels"].get("decode_split_kernel<128, false, 0>")
         km = traffic["kernels"].get("decode_merge_kernel<128>")
         if kp:
             line["roofline"]["traffic"] = kp["traffic_bytes"]
@@ -364,6 +364,7 @@ def main():
 
 
 PAGE_SIZE = 64  # tokens per page of the paged-cache suite lines
+FP8_FORMATS = ("e4m3fn", "e5m2")  # FP8 KV-cache suite lines
 
 
 def run_suite(args):
@@ -443,7 +444,8 @@ def run_suite(args):
         del q, kp, vp, o, lse
     for name, c in wl.DECODE.items():
         paged_name = f"{name}_paged_P{PAGE_SIZE}"
-        if not wanted(name) and not wanted(paged_name):
+        fp8_names = {fmt: name.replace("_bf16", "") + f"_fp8_{fmt}" for fmt in FP8_FORMATS}
+        if not wanted(name) and not wanted(paged_name) and not any(wanted(n) for n in fp8_names.values()):
             continue
         lens = wl.decode_lens(c.n_seq, c.len_lo, c.len_hi, c.lens_seed)
         max_len = int(lens.max())
@@ -470,10 +472,10 @@ def run_suite(args):
         n_tok = int(lens.sum())
         by = decode_bytes(n_tok, c.n_seq, c.Hq, c.Hkv, c.d)
 
-        def report(wname, med, mn, extra):
+        def report(wname, med, mn, extra, by=by, dtype="bf16", reps=n_rep):
             gbs = by / (med * 1e-3) / 1e9
-            print(json.dumps({"workload": wname, "kind": "decode", "dtype": "bf16", "median_ms": round(med, 4),
-                              "min_ms": round(mn, 4), "kv_tokens": n_tok, "pool_replicas": n_rep, **extra,
+            print(json.dumps({"workload": wname, "kind": "decode", "dtype": dtype, "median_ms": round(med, 4),
+                              "min_ms": round(mn, 4), "kv_tokens": n_tok, "pool_replicas": reps, **extra,
                               "algorithmic_gb": round(by / 1e9, 4), "GB/s": round(gbs, 1),
                               "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
                               "useful_gflop": round(decode_flops(n_tok, c.Hq, c.Hkv, c.d) / 1e9, 3)}), flush=True)
@@ -496,6 +498,23 @@ def run_suite(args):
             med, mn = timeit(call_paged)
             report(paged_name, med, mn, {"page_size": PAGE_SIZE})
             del paged
+        for fmt, fp8_name in fp8_names.items():
+            if not wanted(fp8_name):
+                continue
+            # The same batch with an FP8 cache (per-pool scales); half the bytes, so more replicas.
+            n_rep8 = max(1, min(16, math.ceil(2.0e9 / (pool_bytes / 2))))
+            reps8 = [wl.fp8_decode_inputs(c.n_seq, c.Hq, c.Hkv, c.d, lens, fmt, seed=c.value_seed + 100 * r,
+                                          device=dev, max_gap=c.max_gap) for r in range(n_rep8)]
+
+            def call_fp8():
+                qd, kc, vc, offs, lens_t, _, ks, vs = reps8[it[0] % n_rep8]
+                it[0] += 1
+                af.attn_decode(qd, kc, vc, offs, lens_t, max_len=max_len, scale=c.scale, return_lse=True,
+                               workspace=ws, out=od, lse_out=lsed, kv_format=fmt, k_scale=ks, v_scale=vs)
+            med, mn = timeit(call_fp8)
+            by8 = decode_bytes(n_tok, c.n_seq, c.Hq, c.Hkv, c.d, kv_bytes=1)
+            report(fp8_name, med, mn, {"kv_format": fmt}, by=by8, dtype=f"bf16 (kv {fmt})", reps=n_rep8)
+            del reps8
 
 
 if __name__ == "__main__":

@@ -43,10 +43,19 @@ typedef enum {
                                max_len < 1, pool_rows < 0, or a size too large to index (per head,
                                Lk*d*4 and max_len*Hkv*d*2 must stay below 2^31 bytes) */
   ATTN_ERR_UNSUPPORTED = 3, /* d not in {64, 128}; window > 0 without causal; scale not finite;
-                               a pointer not 16-byte aligned */
+                               a pointer not 16-byte aligned; an unknown FP8 format or an FP8
+                               pool scale that is not finite and > 0 */
   ATTN_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than attn_decode_workspace_size / attn_bwd_workspace_size */
   ATTN_ERR_HIP = 5          /* the HIP runtime refused a launch */
 } attn_status;
+
+/* Element formats of an FP8 KV cache (attn_decode_fp8, attn_decode_paged_fp8): the OCP 8-bit
+ * floating point formats that "注意力机制深度优化" (§一.1 and its FP8 tensor-core item) loads
+ * models in, torch.float8_e4m3fn and torch.float8_e5m2. */
+typedef enum {
+  ATTN_KV_E4M3 = 1,  /* 1 sign, 4 exponent (bias 7), 3 mantissa bits; no infinities, max 448 */
+  ATTN_KV_E5M2 = 2   /* 1 sign, 5 exponent (bias 15), 2 mantissa bits; IEEE-style inf / NaN */
+} attn_kv_format;
 
 /* Prefill / full attention, bfloat16 tensors (uint16 storage, round-to-nearest-even results).
  *   q [B, Hq, Lq, d], k and v [B, Hkv, Lk, d], o [B, Hq, Lq, d]  (bf16)
@@ -150,6 +159,28 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Lq, int Lk, int d,
              int causal, int window, float scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/* attn_decode over an FP8 KV cache: k_pool and v_pool [pool_rows, Hkv, d] hold 8-bit codes of
+ * format kv_format (one byte per element, same layout as the bf16 pools), with one scale per pool:
+ * the key is k_scale * K(code), the value v_scale * V(code) (k_scale, v_scale finite and > 0).
+ * q, o, lse and every other argument as attn_decode; the same workspace.  Codes convert exactly to
+ * bf16, so the arithmetic is attn_decode's: scores in fp32 (k_scale folded into the score scale),
+ * P rounded to bf16 for P.V, fp32 accumulation, v_scale applied to the fp32 result.  NaN codes
+ * propagate like NaN values. */
+int attn_decode_fp8(const void* q, const void* k_pool, const void* v_pool,
+                    const int64_t* offsets, const int32_t* lens, void* o, float* lse,
+                    int n_seq, int Hq, int Hkv, int d, int64_t pool_rows, int max_len, int window,
+                    float scale, int kv_format, float k_scale, float v_scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* attn_decode_paged over an FP8 KV cache (pools [pool_pages * page_size, Hkv, d] of 8-bit codes),
+ * with kv_format, k_scale and v_scale as attn_decode_fp8. */
+int attn_decode_paged_fp8(const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_table, int table_stride, int page_size, int64_t pool_pages,
+                          const int32_t* lens, void* o, float* lse,
+                          int n_seq, int Hq, int Hkv, int d, int max_len, int window,
+                          float scale, int kv_format, float k_scale, float v_scale,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* attn_status_str(int status);
 
@@ -192,7 +223,8 @@ int attn_fwd_varlen_schedule(int n_seq, int Hq, int Hkv, int max_seqlen_q, int32
  * workers launched.  With nb(s) = ceil(visible keys of s / tokens_per_block) blocks per row (0
  * for a sequence that is not read) and T = sum of nb(s), the blocks of all sequences laid end
  * to end are cut into shares of ceil(T / teams) blocks; team t computes share t for every row,
- * one partial per (row, sequence) it meets.  ATTN_ERR_HIP without a usable device. */
+ * one partial per (row, sequence) it meets.  ATTN_ERR_HIP without a usable device.  The plan is
+ * that of bf16 pools (three workers per CU); FP8 pools (attn_decode_fp8) run four per CU. */
 int attn_decode_plan(int n_seq, int Hq, int Hkv, int d, int32_t* teams, int32_t* rows_per_seq,
                      int32_t* tokens_per_block);
 

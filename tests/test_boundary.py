@@ -69,6 +69,51 @@ def test_fwd_rejects_bad_arguments(kw, status):
                                  a["Lk"], a["d"], a["causal"], a["window"], a["scale"], None) == status
 
 
+def dec8(**kw):
+    a = dict(q=P, kp=P, vp=P, offs=P, lens=P, o=P, lse=None, N=4, Hq=32, Hkv=8, d=128, T=1000, max_len=100,
+             window=0, scale=0.1, fmt=1, ks=0.5, vs=0.25, ws=P, ws_bytes=1 << 30)
+    a.update(kw)
+    return af.lib().attn_decode_fp8(a["q"], a["kp"], a["vp"], a["offs"], a["lens"], a["o"], a["lse"], a["N"], a["Hq"],
+                                    a["Hkv"], a["d"], a["T"], a["max_len"], a["window"], a["scale"], a["fmt"], a["ks"],
+                                    a["vs"], a["ws"], a["ws_bytes"], None)
+
+
+def dec8p(**kw):
+    a = dict(q=P, kp=P, vp=P, table=P, stride=7, page=16, pages=50, lens=P, o=P, lse=None, N=4, Hq=32, Hkv=8,
+             d=128, max_len=100, window=0, scale=0.1, fmt=2, ks=0.5, vs=0.25, ws=P, ws_bytes=1 << 30)
+    a.update(kw)
+    return af.lib().attn_decode_paged_fp8(a["q"], a["kp"], a["vp"], a["table"], a["stride"], a["page"], a["pages"],
+                                          a["lens"], a["o"], a["lse"], a["N"], a["Hq"], a["Hkv"], a["d"], a["max_len"],
+                                          a["window"], a["scale"], a["fmt"], a["ks"], a["vs"], a["ws"], a["ws_bytes"],
+                                          None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(fmt=0), af.ATTN_ERR_UNSUPPORTED), (dict(fmt=3), af.ATTN_ERR_UNSUPPORTED), (dict(fmt=-1), af.ATTN_ERR_UNSUPPORTED),
+    (dict(ks=0.0), af.ATTN_ERR_UNSUPPORTED), (dict(ks=-1.0), af.ATTN_ERR_UNSUPPORTED),
+    (dict(vs=0.0), af.ATTN_ERR_UNSUPPORTED), (dict(vs=math.inf), af.ATTN_ERR_UNSUPPORTED),
+    (dict(ks=math.nan), af.ATTN_ERR_UNSUPPORTED),
+    (dict(q=None), af.ATTN_ERR_NULL), (dict(offs=None), af.ATTN_ERR_NULL), (dict(kp=None), af.ATTN_ERR_NULL),
+    (dict(N=0), af.ATTN_ERR_SHAPE), (dict(Hq=8, Hkv=3), af.ATTN_ERR_SHAPE), (dict(T=-1), af.ATTN_ERR_SHAPE),
+    (dict(d=96), af.ATTN_ERR_UNSUPPORTED), (dict(scale=math.nan), af.ATTN_ERR_UNSUPPORTED),
+    (dict(kp=MISALIGNED), af.ATTN_ERR_UNSUPPORTED),
+    (dict(ws=None), af.ATTN_ERR_WORKSPACE), (dict(ws_bytes=16), af.ATTN_ERR_WORKSPACE),
+])
+def test_decode_fp8_rejects_bad_arguments(kw, status):
+    assert dec8(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(fmt=0), af.ATTN_ERR_UNSUPPORTED), (dict(fmt=7), af.ATTN_ERR_UNSUPPORTED),
+    (dict(vs=-0.5), af.ATTN_ERR_UNSUPPORTED), (dict(ks=math.inf), af.ATTN_ERR_UNSUPPORTED),
+    (dict(table=None), af.ATTN_ERR_NULL), (dict(page=0), af.ATTN_ERR_SHAPE), (dict(stride=6), af.ATTN_ERR_SHAPE),
+    (dict(page=6, stride=17), af.ATTN_ERR_UNSUPPORTED),     # not a multiple of the 4-token block
+    (dict(ws=None), af.ATTN_ERR_WORKSPACE),
+])
+def test_decode_paged_fp8_rejects_bad_arguments(kw, status):
+    assert dec8p(**kw) == status
+
+
 def bwd(**kw):
     a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, Hq=4, Hkv=2, Lq=64, Lk=64, d=128, causal=1,
              window=0, scale=0.125, ws=P, ws_bytes=1 << 20)

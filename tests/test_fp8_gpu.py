@@ -1,0 +1,160 @@
+"""Decode over an FP8 KV cache (attn_decode_fp8, attn_decode_paged_fp8) against the fp64 oracle.
+
+Pools hold E4M3 or E5M2 codes with one scale per pool (workloads.to_fp8_codes); the oracle decodes
+the same codes itself (oracle.fp8) and attends exactly.  Codes convert exactly to bf16, so the bar
+is the bf16 decode bar (parity.check).  With power-of-two scales the FP8 path must also equal the
+bf16 path bit for bit on the same values, since every scaling is then exact."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attention_attn_fwd_03_amd as af
+import oracle
+import workloads as wl
+from parity import check, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+FMTS = ["e4m3fn", "e5m2"]
+
+
+def gather_codes(kc, vc, offsets, lens, seqs):
+    ks, vs, offs, ls, pos = [], [], [], [], 0
+    for s in seqs:
+        a, n = int(offsets[s]), int(lens[s])
+        ks.append(kc[a:a + n].cpu().numpy())
+        vs.append(vc[a:a + n].cpu().numpy())
+        offs.append(pos)
+        ls.append(n)
+        pos += n
+    return np.concatenate(ks), np.concatenate(vs), np.array(offs, np.int64), np.array(ls, np.int32)
+
+
+def run(q, kc, vc, offs, lens, max_len, window, scale, fmt, ks, vs):
+    N, Hq, d = q.shape
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((N, Hq), float("nan"), device=q.device, dtype=torch.float32)
+    af.attn_decode(q, kc, vc, offs, lens, max_len=max_len, window=window, scale=scale, return_lse=True, out=o,
+                   lse_out=lse, kv_format=fmt, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def fp8_case(lens, Hq, Hkv, d, fmt, window=0, seed=0, scale=None, seqs=None, scale_mult=None, max_gap=37):
+    """scale_mult = (a, b) multiplies the pools' quantisation scales (the keys by a, the values by
+    b); O grows by b and is compared after dividing by b, so the unit-scale bar applies."""
+    lens = np.asarray(lens, np.int32)
+    label = f"fp8 decode {fmt} N{len(lens)} Hq{Hq} Hkv{Hkv} d{d} W{window} seed{seed} lens[:8]={lens[:8].tolist()}"
+    say(label)
+    q, kc, vc, offs, lens_t, layout, ks, vs = wl.fp8_decode_inputs(len(lens), Hq, Hkv, d, lens, fmt, seed=seed,
+                                                                   max_gap=max_gap)
+    vmul = 1.0
+    if scale_mult is not None:
+        ks, vs, vmul = ks * scale_mult[0], vs * scale_mult[1], scale_mult[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    o, lse = run(q.to(DEV), kc.to(DEV), vc.to(DEV), offs.to(DEV), lens_t.to(DEV), int(max(lens.max(), 1)), window,
+                 scale, fmt, ks, vs)
+    seqs = list(range(len(lens))) if seqs is None else seqs
+    kg, vg, po, pl = gather_codes(kc, vc, layout.offsets, layout.lens, seqs)
+    O_ref, L_ref = oracle.decode_fp8kv(wl.to_f64(q)[seqs], kg, vg, po, pl, ks, vs, fmt, scale=scale, window=window)
+    return check(wl.to_f64(o)[seqs] / vmul, O_ref / vmul, lse.cpu().numpy()[seqs], L_ref, "bf16", label)
+
+
+MIXED = [1, 31, 32, 33, 0, 64, 5, 100, 1000, 2049, 3, 777]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (32, 1), (8, 8), (40, 8)])
+def test_fp8_decode_shapes(fmt, d, Hq, Hkv):
+    fp8_case(MIXED, Hq, Hkv, d, fmt, seed=Hq + Hkv + d)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("W", [1, 33, 500])
+def test_fp8_decode_window(fmt, W):
+    fp8_case(MIXED, 32, 8, 128, fmt, window=W, seed=W)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("mult", [(0.37, 2.9), (2.0 ** -2, 2.0 ** 3), (1.7, 0.011)])
+def test_fp8_decode_scales(fmt, mult):
+    fp8_case(MIXED, 32, 4, 128, fmt, seed=9, scale_mult=mult)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("Hkv", [8, 1])
+def test_fp8_equals_bf16_path_with_power_of_two_scales(fmt, Hkv):
+    """Codes convert exactly to bf16 and power-of-two scales are exact, so the FP8 kernel and the
+    bf16 kernel on the dequantized pool (exact in bf16) produce the same bits."""
+    lens = np.array(MIXED, np.int32)
+    q, kc, vc, offs, lens_t, layout, _, _ = wl.fp8_decode_inputs(len(lens), 32, Hkv, 128, lens, fmt, seed=4)
+    ks, vs = 2.0 ** -3, 2.0 ** 2
+    dt = wl.FP8_DTYPES[fmt]
+    kb = (kc.view(dt).to(torch.float32) * ks).to(torch.bfloat16)
+    vb = (vc.view(dt).to(torch.float32) * vs).to(torch.bfloat16)
+    kb = torch.where(torch.isnan(kb), torch.zeros_like(kb), kb)  # NaN gap rows: never read by either path
+    vb = torch.where(torch.isnan(vb), torch.zeros_like(vb), vb)
+    max_len = int(lens.max())
+    o8, l8 = run(q.to(DEV), kc.to(DEV), vc.to(DEV), offs.to(DEV), lens_t.to(DEV), max_len, 0, 0.0884, fmt, ks, vs)
+    o = torch.full_like(o8, float("nan"))
+    lse = torch.full_like(l8, float("nan"))
+    af.attn_decode(q.to(DEV), kb.to(DEV), vb.to(DEV), offs.to(DEV), lens_t.to(DEV), max_len=max_len, scale=0.0884,
+                   return_lse=True, out=o, lse_out=lse)
+    torch.cuda.synchronize()
+    assert torch.equal(o8.view(torch.int16), o.view(torch.int16)) and torch.equal(l8, lse)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("name", ["gqa_decode_bf16", "mqa_decode_bf16"])
+def test_fp8_named_decode(fmt, name):
+    """The full decode batch (64 sequences, lengths 1k..32k, NaN codes in the pool's gaps) with an
+    FP8 cache: every output finite, 16+ sequences against the oracle."""
+    c = wl.DECODE[name]
+    lens = wl.decode_lens(c.n_seq, c.len_lo, c.len_hi, c.lens_seed)
+    say(f"fp8 decode {fmt} {name} full size on device")
+    q, kc, vc, offs, lens_t, layout, ks, vs = wl.fp8_decode_inputs(c.n_seq, c.Hq, c.Hkv, c.d, lens, fmt,
+                                                                   seed=c.value_seed, device=DEV, max_gap=c.max_gap)
+    o, lse = run(q, kc, vc, offs, lens_t, int(lens.max()), 0, c.scale, fmt, ks, vs)
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+    seqs = sorted(set(np.random.default_rng(c.value_seed).choice(c.n_seq, 16, replace=False).tolist())
+                  | {int(np.argmax(lens)), int(np.argmin(lens))})
+    kg, vg, po, pl = gather_codes(kc, vc, layout.offsets, layout.lens, seqs)
+    O_ref, L_ref = oracle.decode_fp8kv(wl.to_f64(q)[seqs], kg, vg, po, pl, ks, vs, fmt, scale=c.scale)
+    say(name, fmt, check(wl.to_f64(o)[seqs], O_ref, lse.cpu().numpy()[seqs], L_ref, "bf16", name + " " + fmt))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("Hkv,P", [(8, 16), (8, 64), (1, 32), (2, 48)])
+def test_fp8_decode_paged(fmt, Hkv, P):
+    lens = np.array(MIXED, np.int32)
+    label = f"fp8 paged {fmt} Hkv{Hkv} P{P}"
+    say(label)
+    q, kc, vc, table, lens_t, layout, ks, vs = wl.fp8_paged_decode_inputs(len(lens), 32, Hkv, 128, lens, P, fmt,
+                                                                          seed=P + Hkv, extra_pages=3)
+    o = torch.full((len(lens), 32, 128), float("nan"), device=DEV, dtype=torch.bfloat16)
+    lse = torch.full((len(lens), 32), float("nan"), device=DEV, dtype=torch.float32)
+    af.attn_decode_paged(q.to(DEV), kc.to(DEV), vc.to(DEV), table.to(DEV), lens_t.to(DEV), page_size=P,
+                         max_len=int(lens.max()), scale=0.0884, return_lse=True, out=o, lse_out=lse, kv_format=fmt,
+                         k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.decode_paged_fp8kv(wl.to_f64(q), kc.numpy(), vc.numpy(), layout.table, layout.lens, P, ks,
+                                             vs, fmt, scale=0.0884)
+    check(wl.to_f64(o), O_ref, lse.cpu().numpy(), L_ref, "bf16", label)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_fp8_invalid_sequences_report_nan(fmt):
+    """A sequence whose range leaves the pool is not read and reports NaN; the others are exact."""
+    lens = np.array([40, 70, 5, 33], np.int32)
+    q, kc, vc, offs, lens_t, layout, ks, vs = wl.fp8_decode_inputs(4, 16, 4, 64, lens, fmt, seed=3)
+    bad = offs.clone()
+    bad[1] = layout.total_rows - 10  # runs past the end of the pool
+    o, lse = run(q.to(DEV), kc.to(DEV), vc.to(DEV), bad.to(DEV), lens_t.to(DEV), 70, 0, 0.125, fmt, ks, vs)
+    assert torch.isnan(o[1]).all().item() and torch.isnan(lse[1]).all().item()
+    good = [0, 2, 3]
+    kg, vg, po, pl = gather_codes(kc, vc, layout.offsets, layout.lens, good)
+    O_ref, L_ref = oracle.decode_fp8kv(wl.to_f64(q)[good], kg, vg, po, pl, ks, vs, fmt, scale=0.125)
+    check(wl.to_f64(o)[good], O_ref, lse.cpu().numpy()[good], L_ref, "bf16", "fp8 invalid")
