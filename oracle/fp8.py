@@ -16,13 +16,14 @@ OCP 8-bit floating point definitions (OFP8, Open Compute Project, 2023):
 
 Reading taken for the scaling the pages leave open: one fp32 scale per pool, real value =
 scale * decoded code (k_scale for K, v_scale for V), as a per-tensor-scaled FP8 cache stores it.
-The attention itself is decode() / decode_paged() of attention.py on the dequantized pools.
+The attention itself is decode() / decode_paged() / attention() of attention.py on the
+dequantized tensors.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .attention import decode, decode_paged
+from .attention import attention, decode, decode_paged
 
 FORMATS = ("e4m3fn", "e5m2")
 
@@ -72,3 +73,16 @@ def decode_paged_fp8kv(q, k_codes, v_codes, block_table, lens, page_size: int, k
     """decode_paged() with FP8 pools, as decode_fp8kv()."""
     return decode_paged(q, dequantize(k_codes, k_scale, fmt), dequantize(v_codes, v_scale, fmt), block_table,
                         lens, page_size, scale=scale, window=window, threads=threads, seqs=seqs)
+
+
+def attention_fp8(q_codes, k_codes, v_codes, q_scale: float, k_scale: float, v_scale: float, fmt: str,
+                  scale: float | None = None, causal: bool = False, window: int = 0, threads: int | None = None):
+    """attention() of Q, K and V given as FP8 codes [B, H, L, d] (uint8) with one scale per tensor
+    ("注意力机制深度优化" §一.1 runs FlashAttention on float8_e4m3fn tensors): the exact attention
+    of the dequantized tensors.  Returns O, LSE as attention()."""
+    q = dequantize(q_codes, q_scale, fmt)
+    k = dequantize(k_codes, k_scale, fmt)
+    v = dequantize(v_codes, v_scale, fmt)
+    if scale is None:
+        scale = 1.0 / np.sqrt(q.shape[-1])
+    return attention(q, k, v, scale=scale, causal=causal, window=window, threads=threads)

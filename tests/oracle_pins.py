@@ -635,6 +635,25 @@ def check_fp8kv_decode(seed=30):
     assert not np.allclose(Oe4, oracle.decode_fp8kv(q, kc, vc, offsets, lens, 1.0, 1.0, "e5m2", scale=0.5)[0])
 
 
+def check_fp8_attention(seed=31):
+    """Attention over FP8 Q, K, V: equal to attention() of the tensors torch's float8 conversion
+    dequantizes (an independent route), for both formats; q_scale * k_scale act as one factor on
+    the scores and v_scale scales O."""
+    import torch
+    rng = _rng(seed)
+    B, Hq, Hkv, L, d = 1, 4, 2, 9, 8
+    for fmt, dt in (("e4m3fn", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)):
+        codes = [torch.from_numpy(rng.standard_normal(shape) * 4).to(dt).view(torch.uint8).numpy()
+                 for shape in ((B, Hq, L, d), (B, Hkv, L, d), (B, Hkv, L, d))]
+        qs, ks, vs = 0.21, 0.7, 1.3
+        O, L_ = oracle.attention_fp8(*codes, qs, ks, vs, fmt, scale=0.4, causal=True, window=5)
+        ref = [torch.from_numpy(c).view(dt).to(torch.float64).numpy() * s_ for c, s_ in zip(codes, (qs, ks, vs))]
+        O2, L2 = oracle.attention(*ref, scale=0.4, causal=True, window=5)
+        assert np.allclose(O, O2, rtol=1e-13, atol=1e-13) and np.allclose(L_, L2, rtol=1e-13, atol=1e-13), fmt
+        O3, L3 = oracle.attention_fp8(*codes, 1.0, qs * ks, 2 * vs, fmt, scale=0.4, causal=True, window=5)
+        assert np.allclose(O3, 2 * O, rtol=1e-12, atol=1e-13) and np.allclose(L3, L_, rtol=1e-12, atol=1e-13)
+
+
 def check_golden():
     """Hand-derived exact values (tests/golden/worked_example.json)."""
     g = json.load(open(GOLDEN))
@@ -671,4 +690,5 @@ ALL_CHECKS = [check_golden, check_brute_force, check_torch_sdpa, check_softmax_r
               check_lse_identity, check_split_merge, check_decode_is_last_row, check_pool_addressing,
               check_paged_matches_contiguous, check_paged_brute_force, check_varlen_brute_force,
               check_varlen_chunks, check_backward_autograd, check_backward_finite_differences,
-              check_backward_closed_forms, check_visible_pairs, check_fp8_decoders, check_fp8kv_decode]
+              check_backward_closed_forms, check_visible_pairs, check_fp8_decoders, check_fp8kv_decode,
+              check_fp8_attention]

@@ -189,7 +189,13 @@ def _fp8kv_scales_swapped(q, k_codes, v_codes, offsets, lens, k_scale, v_scale, 
                          offsets, lens, **kw)
 
 
+def _fp8_attention_v_unscaled(q_codes, k_codes, v_codes, q_scale, k_scale, v_scale, fmt, **kw):
+    return fp8mod.attention(fp8mod.dequantize(q_codes, q_scale, fmt), fp8mod.dequantize(k_codes, k_scale, fmt),
+                            fp8mod.dequantize(v_codes, 1.0, fmt), **kw)
+
+
 FP8_MUTANTS = {
+    "fp8_attention_v_scale_dropped": ("attention_fp8", _fp8_attention_v_unscaled),
     "e4m3_bias_8": ("decode_e4m3fn", _e4m3_bias8),
     "e4m3_subnormals_flushed": ("decode_e4m3fn", _e4m3_flush_subnormals),
     "e5m2_read_as_e4m3": ("decode_e5m2", fp8mod.decode_e4m3fn),

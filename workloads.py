@@ -288,6 +288,14 @@ def fp8_decode_inputs(n_seq, Hq, Hkv, d, lens, fmt, *, seed, device="cpu", max_g
     return q.to(torch.bfloat16), kc, vc, offs, lens_t, layout, ks, vs
 
 
+def fp8_prefill_inputs(B, Hq, Hkv, Lq, Lk, d, fmt, *, seed, device="cpu"):
+    """prefill_inputs drawn in fp32 and quantised per tensor (to_fp8_codes): q, k, v codes
+    [B, H, L, d] uint8 and their scales (q_scale, k_scale, v_scale)."""
+    q, k, v = prefill_inputs(B, Hq, Hkv, Lq, Lk, d, seed=seed, dtype=torch.float32, device=device)
+    (qc, qs), (kc, ks), (vc, vs) = (to_fp8_codes(x, fmt) for x in (q, k, v))
+    return qc, kc, vc, qs, ks, vs
+
+
 def fp8_paged_decode_inputs(n_seq, Hq, Hkv, d, lens, page_size, fmt, *, seed, device="cpu", extra_pages=0,
                             stride=None):
     """paged_decode_inputs with FP8 pools, as fp8_decode_inputs.  Returns q, k_codes, v_codes,
