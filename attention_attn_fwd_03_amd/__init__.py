@@ -20,7 +20,8 @@ KV_FORMATS = {"e4m3fn": 1, "e5m2": 2}  # attn_kv_format
 
 EXPORTS = ["attn_fwd", "attn_fwd_f32", "attn_fwd_varlen", "attn_decode_workspace_size", "attn_decode",
            "attn_decode_paged", "attn_status_str", "attn_fwd_plan", "attn_fwd_schedule", "attn_fwd_varlen_schedule",
-           "attn_decode_plan", "attn_bwd_workspace_size", "attn_bwd", "attn_decode_fp8", "attn_decode_paged_fp8"]
+           "attn_decode_plan", "attn_bwd_workspace_size", "attn_bwd", "attn_decode_fp8", "attn_decode_paged_fp8",
+           "attn_fwd_fp8"]
 
 
 class FwdPlanInfo(ctypes.Structure):
@@ -55,6 +56,8 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_paged.argtypes = [vp, vp, vp, vp, i32, i32, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                                     vp, sz, vp]
     L.attn_decode_paged.restype = i32
+    L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, f32, f32, f32, vp]
+    L.attn_fwd_fp8.restype = i32
     L.attn_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, i32, f32, i32, f32, f32,
                                   vp, sz, vp]
     L.attn_decode_fp8.restype = i32
@@ -165,6 +168,35 @@ def attn_bwd(q, k, v, o, dout, lse, *, causal: bool = False, window: int = 0, sc
                           int(window), float(scale), workspace.data_ptr(),
                           workspace.numel() * workspace.element_size(), _stream()))
     return dq, dk, dv
+
+
+def attn_fwd_fp8(q, k, v, *, qkv_format: str, q_scale: float, k_scale: float, v_scale: float, causal: bool = False,
+                 window: int = 0, scale: float | None = None, return_lse: bool = False, out=None, lse_out=None):
+    """Exact attention over FP8 inputs: q [B, Hq, Lq, d], k, v [B, Hkv, Lk, d] uint8 codes of
+    ``qkv_format`` ('e4m3fn' / 'e5m2') with per-tensor scales (real value = scale * code value).
+    Returns O [B, Hq, Lq, d] bf16 and, when ``return_lse``, LSE [B, Hq, Lq] fp32."""
+    import torch
+    _require_gpu(q, k, v)
+    if q.dtype != torch.uint8 or k.dtype != torch.uint8 or v.dtype != torch.uint8:
+        raise ValueError("attn_fwd_fp8 takes uint8 FP8 codes")
+    if qkv_format not in KV_FORMATS:
+        raise ValueError("qkv_format must be 'e4m3fn' or 'e5m2'")
+    B, Hq, Lq, d = q.shape
+    Bk, Hkv, Lk, dk = k.shape
+    if Bk != B or dk != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch between q, k and v")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty((B, Hq, Lq, d), device=q.device, dtype=torch.bfloat16) if out is None else out
+    _require_gpu(o)
+    lse = None
+    if return_lse:
+        lse = torch.empty((B, Hq, Lq), device=q.device, dtype=torch.float32) if lse_out is None else lse_out
+    _check(lib().attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr() if lse is not None else None, B, Hq, Hkv, Lq, Lk, d, int(bool(causal)),
+                              int(window), float(scale), KV_FORMATS[qkv_format], float(q_scale), float(k_scale),
+                              float(v_scale), _stream()))
+    return (o, lse) if return_lse else o
 
 
 def decode_workspace_size(n_seq: int, Hq: int, Hkv: int, d: int, max_len: int) -> int:

@@ -10,8 +10,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattnfwd.so")
-SOURCES = ["api.cpp", "prefill.hip", "decode.hip", "backward.hip"]
-HEADERS = ["attn_device.hpp", "kernels.hpp", "plan.hpp"]
+SOURCES = ["api.cpp", "prefill.hip", "prefill_fp8.hip", "decode.hip", "backward.hip"]
+HEADERS = ["attn_device.hpp", "fp8_device.hpp", "kernels.hpp", "plan.hpp"]
 
 
 def hipcc() -> str:

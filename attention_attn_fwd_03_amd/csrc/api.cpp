@@ -95,6 +95,22 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
   return fwd_common(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d, causal, window, scale, stream, true);
 }
 
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Lq,
+                 int Lk, int d, int causal, int window, float scale, int qkv_format, float q_scale, float k_scale,
+                 float v_scale, void* stream) {
+  const int st = check_fwd(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d, causal, window, scale);
+  if (st != ATTN_OK) return st;
+  if (qkv_format != ATTN_KV_E4M3 && qkv_format != ATTN_KV_E5M2) return ATTN_ERR_UNSUPPORTED;
+  if (!(std::isfinite(q_scale) && q_scale > 0.f && std::isfinite(k_scale) && k_scale > 0.f &&
+        std::isfinite(v_scale) && v_scale > 0.f))
+    return ATTN_ERR_UNSUPPORTED;
+  FwdArgs a = make_fwd_args(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d, causal, window, scale, false);
+  if (a.qmode != 2) a.c *= q_scale * k_scale;  // scores: scale * q_scale * k_scale * (q . k codes); 2: zero scale
+  a.v_scale = v_scale;
+  const hipError_t e = launch_prefill_fp8(a, d, qkv_format, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 int attn_fwd_varlen(const void* q, const void* k_pool, const void* v_pool, void* o, float* lse,
                     const int32_t* cu_seqlens_q, const int64_t* kv_offsets, const int32_t* kv_lens, int n_seq, int Hq,
                     int Hkv, int d, int max_seqlen_q, int64_t total_q, int64_t pool_rows, int causal, int window,

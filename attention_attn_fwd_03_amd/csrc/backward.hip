@@ -181,19 +181,6 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const unsigned short* o
   if (row < rows && part == 0) dvec[row] = acc;
 }
 
-// Per-lane visible range of an S^T tile's keys (rows) for query q: keys kbase + lo .. kbase + hi,
-// kbase = k0 + 4*(lane/32); bottom-right causal, window and key tail as in the forward.
-__device__ __forceinline__ void key_limits(const BwdArgs& a, int k0, int h, int q, int& lo, int& hi) {
-  const int pos = q + (a.Lk - a.Lq);
-  int hk = a.Lk - 1;
-  if (a.causal && pos < hk) hk = pos;
-  int lk = 0;
-  if (a.window > 0 && pos - a.window + 1 > lk) lk = pos - a.window + 1;
-  const int kbase = k0 + 4 * h;
-  lo = lk - kbase;
-  hi = hk - kbase;
-}
-
 // ---------------------------------------------------------------------------------------------
 // 2. dQ.  One workgroup = 4 waves = 128 query rows of one (batch, query head); keys in tiles of BK.
 // Blocks are ordered as the forward's (plan.hpp prefill_tile): heaviest query tiles first, query
@@ -294,7 +281,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       const int k0 = kt * BK;
       if (!tile_full(k0, w_start, 32, a.Lq, a.Lk, BK, a.causal, a.window)) {
         int elo, ehi;
-        key_limits(a, k0, h, q, elo, ehi);
+        edge_key_limits(k0, h, q, a.Lq, a.Lk, a.causal, a.window, elo, ehi);
         mask_tile(x, elo, ehi);
       }
 #pragma unroll

@@ -29,16 +29,13 @@
 #include <type_traits>
 
 #include "attn_device.hpp"
+#include "fp8_device.hpp"
 #include "kernels.hpp"
 #include "plan.hpp"
 
 namespace attnfwd {
 
 typedef __attribute__((address_space(3))) void lds_void_d;
-
-// KV element formats of the pool: bf16, or an 8-bit float code (OCP E4M3 / E5M2) with one scale
-// per pool.
-enum KvFormat : int { kKvBf16 = 0, kKvE4M3 = 1, kKvE5M2 = 2 };
 
 template <int D, int KV = kKvBf16>
 struct DecCfg {
@@ -141,43 +138,11 @@ __device__ __forceinline__ void stage_offsets(unsigned (&voff)[N], int lane, int
   for (int j = 0; j < N; ++j) {
     const int o = j * 1024 + 16 * lane;
     const int r = o / PITCH, ch = (o % PITCH) / 16;
-    const int src = SWAP23 ? (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1) : r;
+    const int src = SWAP23 ? fp8_v_row(r) : r;
     voff[j] = (r < kDecodeBlockRows && ch < CH)
                   ? (unsigned)((src / pack) * token_bytes + (src % pack) * ROWB + ch * 16)
                   : 0x80000000u;
   }
-}
-
-// Eight 8-bit float codes (bytes 0..7 of w) as eight bf16 values; exact for both formats.
-template <int KV>
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 w) {
-  bf16x2 p0, p1, p2, p3;
-  if constexpr (KV == kKvE4M3) {
-    p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false);
-    p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true);
-    p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false);
-    p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true);
-  } else {
-    p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w[0], 1.0f, false);
-    p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w[0], 1.0f, true);
-    p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w[1], 1.0f, false);
-    p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w[1], 1.0f, true);
-  }
-  const u32x4 r = {__builtin_bit_cast(unsigned, p0), __builtin_bit_cast(unsigned, p1), __builtin_bit_cast(unsigned, p2),
-                   __builtin_bit_cast(unsigned, p3)};
-  return __builtin_bit_cast(bf16x8, r);
-}
-
-typedef __attribute__((ext_vector_type(2))) int i32x2;
-typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
-
-// ds_read_b64_tr_b8: inside each 16-lane group, lane i receives byte i%8 of the 8-byte pieces
-// addressed by lanes i/8 + 2c, c = 0..7 (checked on the hardware with a lane-layout probe).  If
-// lane j of the group addresses row r0 + j/2, bytes c0 + 8*(j%2) .. +7 of a row-major byte
-// matrix, lane i receives rows r0 .. r0+7 of column c0 + i.
-__device__ __forceinline__ u32x2 lds_read_tr8(const void* lds_generic_ptr) {
-  const lds_i32x2* p = (const lds_i32x2*)(__attribute__((address_space(3))) unsigned char*)lds_generic_ptr;
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(const_cast<lds_i32x2*>(p)));
 }
 
 // PAGED selects the pool addressing and KV the pool's element format at compile time, so the

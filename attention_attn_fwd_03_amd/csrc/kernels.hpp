@@ -26,6 +26,9 @@ struct FwdArgs {
   const int64_t* kv_offs;
   const int32_t* kv_lens;
   int64_t total_q, pool_rows;
+  // FP8 inputs (fwd_fp8_kernel): the V scale, applied to the result (the Q and K scales are folded
+  // into c).
+  float v_scale;
 };
 
 struct DecArgs {
@@ -95,6 +98,7 @@ int prefill_threads(bool f32);
 int prefill_lds_bytes(bool f32, int d);
 hipError_t launch_prefill(const FwdArgs& a, bool f32, int d, hipStream_t stream);
 hipError_t launch_prefill_varlen(const FwdArgs& a, int d, hipStream_t stream);
+hipError_t launch_prefill_fp8(const FwdArgs& a, int d, int fmt, hipStream_t stream);
 
 // One resident round of split workers on the current device (bf16 or fp8 pool), or < 0.
 int decode_workers(int d, bool fp8 = false);

@@ -63,6 +63,21 @@ ATTN_HD bool tile_full(int k0, int q_start, int bq, int Lq, int Lk, int bk, int 
   return true;
 }
 
+// Keys a query row sees, relative to kbase = k0 + 4*(lane/32) (the first key of the lane's rows in
+// an S^T accumulator block): key kbase + ci is visible iff lo <= ci <= hi.  Query q sits at
+// position q + Lk - Lq (bottom-right), sees keys up to it under causal masking, the last `window`
+// positions under a window, and nothing past Lk - 1.
+ATTN_HD void edge_key_limits(int k0, int h, int q, int Lq, int Lk, int causal, int window, int& lo, int& hi) {
+  const int pos = q + (Lk - Lq);
+  int hk = Lk - 1;
+  if (causal && pos < hk) hk = pos;
+  int lk = 0;
+  if (window > 0 && pos - window + 1 > lk) lk = pos - window + 1;
+  const int kbase = k0 + 4 * h;
+  lo = lk - kbase;
+  hi = hk - kbase;
+}
+
 // Per-pair visibility, used inside masked tiles.
 ATTN_HD bool visible(int key, int q, int Lq, int Lk, int causal, int window) {
   const int p = q + (Lk - Lq);

@@ -51,19 +51,6 @@ struct Bf16Cfg {
   static_assert(K_TILE % 1024 == 0 && V_TILE % 1024 == 0, "stages must be whole wave-wide loads");
 };
 
-// Per-lane key window of an edge tile, relative to kbase = k0 + 4*(lane/32): key kbase + ci is
-// visible iff lo <= ci <= hi.
-__device__ __forceinline__ void edge_limits(int k0, int h, int q, const FwdArgs& a, int& lo, int& hi) {
-  const int pos = q + (a.Lk - a.Lq);
-  int hk = a.Lk - 1;
-  if (a.causal && pos < hk) hk = pos;
-  int lk = 0;
-  if (a.window > 0 && pos - a.window + 1 > lk) lk = pos - a.window + 1;
-  const int kbase = k0 + 4 * h;
-  lo = lk - kbase;
-  hi = hk - kbase;
-}
-
 // Buffer descriptor over at most max_rows rows, from row0 on, of nrows rows stride_bytes apart
 // (each row_bytes long) at `base`: the rows of one head of a token-major pool.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t strided_rows_rsrc(const unsigned short* base, int row0, int nrows,
@@ -264,7 +251,7 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(FwdArgs a) {
       const int k0 = kt * BK;
       if (!tile_full(k0, w_start, 32, a.Lq, a.Lk, BK, a.causal, a.window)) {
         int elo, ehi;
-        edge_limits(k0, h, q, a, elo, ehi);
+        edge_key_limits(k0, h, q, a.Lq, a.Lk, a.causal, a.window, elo, ehi);
         mask_tile(sc, elo, ehi);
       }
       const float mb = update_max(sc, st, o, c);
@@ -427,7 +414,7 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
     const bool full = tile_full(k0, q_start, C::BQ, a.Lq, a.Lk, BK, a.causal, a.window);
     if (!full) {
       int elo, ehi;
-      edge_limits(k0, h, q, a, elo, ehi);
+      edge_key_limits(k0, h, q, a.Lq, a.Lk, a.causal, a.window, elo, ehi);
       mask_tile(s, elo, ehi);
     }
     const float mb = update_max(s, st, o, c);

@@ -40,6 +40,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk/CU)
 PEAK_F32_MFMA_TFLOPS = 157.3
+PEAK_FP8_TFLOPS = 5033.2    # dense fp8 MFMA: twice the bf16 rate
+# The FP8-input prefill runs S = Q K^T on the FP8 matrix cores and P V on the bf16 ones, half the
+# useful FLOPs each: its roofline peak is 1 / (0.5 / 5033.2 + 0.5 / 2516.6) TFLOP/s.
+PEAK_FP8_BF16_MIX_TFLOPS = round(1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS), 1)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
@@ -74,6 +78,9 @@ def backward_flops(c) -> int:
     times the forward's; the recomputation of S and dP in the second kernel is not counted."""
     return 10 * c.d * c.B * c.Hq * visible_pairs(c.Lq, c.Lk, c.causal, c.window)
 
+
+# FP8-input prefill lines of the suite: the two long workloads with FP8 Q, K, V.
+FP8_PREFILL_WORKLOADS = ["gqa_causal_bf16_L4096", "swa_gqa_bf16_L16384_W4096"]
 
 # Backward (training) lines of the suite: the dense bf16 workloads.
 BWD_WORKLOADS = ["mha_bf16_L1024", "gqa_causal_bf16_L4096", "swa_gqa_bf16_L16384_W4096"]
@@ -364,7 +371,7 @@ def main():
 
 
 PAGE_SIZE = 64  # tokens per page of the paged-cache suite lines
-FP8_FORMATS = ("e4m3fn", "e5m2")  # FP8 KV-cache suite lines
+FP8_FORMATS = ("e4m3fn", "e5m2")  # FP8 suite lines (KV cache, prefill inputs)
 
 
 def run_suite(args):
@@ -407,6 +414,27 @@ def run_suite(args):
                           "frac_mfma_peak": round(tf / peak, 4), "peak_TFLOP/s": peak,
                           "GB/s_algorithmic": round(prefill_bytes(c) / (med * 1e-3) / 1e9, 1)}), flush=True)
         del q, k, v, o, lse
+    for name in FP8_PREFILL_WORKLOADS:
+        c = wl.PREFILL[name]
+        for fmt in FP8_FORMATS:
+            fname = name.replace("_bf16_", f"_fp8_{fmt}_")
+            if not wanted(fname):
+                continue
+            qc, kc, vc, qs, ks, vs = wl.fp8_prefill_inputs(c.B, c.Hq, c.Hkv, c.Lq, c.Lk, c.d, fmt, seed=c.seed,
+                                                           device=dev)
+            o = torch.empty(qc.shape, device=dev, dtype=torch.bfloat16)
+            lse = torch.empty(qc.shape[:3], device=dev, dtype=torch.float32)
+            med, mn = timeit(lambda: af.attn_fwd_fp8(qc, kc, vc, qkv_format=fmt, q_scale=qs, k_scale=ks, v_scale=vs,
+                                                     causal=c.causal, window=c.window, scale=c.scale,
+                                                     return_lse=True, out=o, lse_out=lse))
+            fl = prefill_flops(c)
+            tf = fl / (med * 1e-3) / 1e12
+            print(json.dumps({"workload": fname, "kind": "prefill", "dtype": f"fp8 {fmt} q/k/v, bf16 P",
+                              "median_ms": round(med, 4), "min_ms": round(mn, 4), "useful_gflop": round(fl / 1e9, 4),
+                              "TFLOP/s": round(tf, 2), "frac_mfma_peak": round(tf / PEAK_FP8_BF16_MIX_TFLOPS, 4),
+                              "peak_TFLOP/s": PEAK_FP8_BF16_MIX_TFLOPS,
+                              "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}), flush=True)
+            del qc, kc, vc, o, lse
     for name in BWD_WORKLOADS:
         c = wl.PREFILL[name]
         if not wanted(name + "_bwd"):

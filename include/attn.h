@@ -72,6 +72,18 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
                  int B, int Hq, int Hkv, int Lq, int Lk, int d,
                  int causal, int window, float scale, void* stream);
 
+/* attn_fwd over 8-bit float inputs ("注意力机制深度优化" §一.1 runs FlashAttention on float8_e4m3fn
+ * tensors, its FP8 tensor-core item on float8_e5m2): q [B, Hq, Lq, d], k and v [B, Hkv, Lk, d] hold
+ * codes of format qkv_format (attn_kv_format, one byte per element), with one scale per tensor
+ * (real value = scale * code value; finite and > 0).  o [B, Hq, Lq, d] is bf16, lse as attn_fwd.
+ * S = Q K^T runs on the FP8 matrix cores (v_mfma_f32_32x32x64_f8f6f4, fp32 accumulation, the Q and
+ * K scales folded into the score scale); the softmax is fp32, P is rounded to bf16 and P V runs on
+ * the bf16 matrix cores with V's codes converted exactly.  The result is attn_fwd's arithmetic on
+ * the dequantized tensors.  Masking, scale, rules and status codes as attn_fwd. */
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Hq, int Hkv, int Lq, int Lk, int d, int causal, int window, float scale,
+                 int qkv_format, float q_scale, float k_scale, float v_scale, void* stream);
+
 /* Ragged prefill against a pooled KV cache (continuous batching: "注意力机制深度优化" §二.1;
  * variable-length sequences processed in chunks against their history: "高效多头潜在注意力解码技术：
  * Flash MLA深度解析" §一, §2.2).  bf16.

@@ -38,7 +38,16 @@ def say(*args):
     sys.stdout.flush()
 
 
-def check(o, o_ref, lse, lse_ref, dtype: str, label: str = "", magnitude: float = 1.0):
+# FP8 inputs (attn_fwd_fp8): v_mfma_f32_32x32x64_f8f6f4 adds its 64 exact products with about 13
+# bits of precision, not fp32's 24: over 65,536 outputs of full-range random E4M3 codes the error was
+# at most 1.05e-4 of the sum of |products| (about 2^-13).  A score therefore carries up to
+# FP8_MFMA_EPS * |scale| * sum_i |q_i k_i| of error (bound taken at twice the largest measured), and
+# so may the LSE; check() takes that per row as ``lse_abs_extra``.  O is not affected beyond the
+# bf16 bar (the score error stays below the bf16 rounding of P).
+FP8_MFMA_EPS = 2.0 ** -12
+
+
+def check(o, o_ref, lse, lse_ref, dtype: str, label: str = "", magnitude: float = 1.0, lse_abs_extra=None):
     o = np.asarray(o, np.float64)
     o_ref = np.asarray(o_ref, np.float64)
     assert o.shape == o_ref.shape, (label, o.shape, o_ref.shape)
@@ -51,7 +60,10 @@ def check(o, o_ref, lse, lse_ref, dtype: str, label: str = "", magnitude: float 
             assert np.all(np.isneginf(lse[empty])), (label, "rows that see no key need LSE = -inf")
             fin = ~empty
             assert np.all(np.isfinite(lse[fin])), (label, "non-finite LSE")
-            rel = np.abs(lse[fin] - lse_ref[fin]) / np.maximum(1.0, np.abs(lse_ref[fin]))
+            diff = np.abs(lse[fin] - lse_ref[fin])
+            if lse_abs_extra is not None:
+                diff = np.maximum(0.0, diff - np.broadcast_to(np.asarray(lse_abs_extra, np.float64), lse.shape)[fin])
+            rel = diff / np.maximum(1.0, np.abs(lse_ref[fin]))
             lerr = float(np.max(rel, initial=0.0))
             stats["lse_err"] = lerr
             assert lerr <= LSE_TOL[dtype], (label, "LSE error (relative to max(1, |LSE|))", lerr)

@@ -69,6 +69,27 @@ def test_fwd_rejects_bad_arguments(kw, status):
                                  a["Lk"], a["d"], a["causal"], a["window"], a["scale"], None) == status
 
 
+def fwd8(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, Hq=4, Hkv=2, Lq=64, Lk=64, d=128, causal=1, window=0, scale=0.125,
+             fmt=1, qs=0.5, ks=0.25, vs=2.0)
+    a.update(kw)
+    return af.lib().attn_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Lq"], a["Lk"],
+                                 a["d"], a["causal"], a["window"], a["scale"], a["fmt"], a["qs"], a["ks"], a["vs"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), af.ATTN_ERR_NULL), (dict(o=None), af.ATTN_ERR_NULL),
+    (dict(B=0), af.ATTN_ERR_SHAPE), (dict(Hq=6, Hkv=4), af.ATTN_ERR_SHAPE), (dict(Lk=1 << 23), af.ATTN_ERR_SHAPE),
+    (dict(d=96), af.ATTN_ERR_UNSUPPORTED), (dict(causal=0, window=4), af.ATTN_ERR_UNSUPPORTED),
+    (dict(fmt=0), af.ATTN_ERR_UNSUPPORTED), (dict(fmt=3), af.ATTN_ERR_UNSUPPORTED),
+    (dict(qs=0.0), af.ATTN_ERR_UNSUPPORTED), (dict(ks=-1.0), af.ATTN_ERR_UNSUPPORTED),
+    (dict(vs=math.nan), af.ATTN_ERR_UNSUPPORTED), (dict(scale=math.inf), af.ATTN_ERR_UNSUPPORTED),
+    (dict(k=MISALIGNED), af.ATTN_ERR_UNSUPPORTED),
+])
+def test_fwd_fp8_rejects_bad_arguments(kw, status):
+    assert fwd8(**kw) == status
+
+
 def dec8(**kw):
     a = dict(q=P, kp=P, vp=P, offs=P, lens=P, o=P, lse=None, N=4, Hq=32, Hkv=8, d=128, T=1000, max_len=100,
              window=0, scale=0.1, fmt=1, ks=0.5, vs=0.25, ws=P, ws_bytes=1 << 30)

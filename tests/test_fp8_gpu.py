@@ -13,7 +13,7 @@ import torch
 import attention_attn_fwd_03_amd as af
 import oracle
 import workloads as wl
-from parity import check, say
+from parity import FP8_MFMA_EPS, check, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -158,3 +158,97 @@ def test_fp8_invalid_sequences_report_nan(fmt):
     kg, vg, po, pl = gather_codes(kc, vc, layout.offsets, layout.lens, good)
     O_ref, L_ref = oracle.decode_fp8kv(wl.to_f64(q)[good], kg, vg, po, pl, ks, vs, fmt, scale=0.125)
     check(wl.to_f64(o)[good], O_ref, lse.cpu().numpy()[good], L_ref, "bf16", "fp8 invalid")
+
+
+# ---------------------------------------------------------------------------------------------
+# Prefill over FP8 Q, K, V (attn_fwd_fp8).  The oracle attends exactly over the dequantized
+# tensors; P is rounded to bf16 as in the bf16 kernel, so the bf16 bar applies to O; the LSE bar
+# adds the FP8 matrix cores' accumulation error (parity.FP8_MFMA_EPS).
+
+def fp8_lse_allowance(qd, kd, scale, rows=None):
+    """Per query row: FP8_MFMA_EPS * |scale| * max_j sum_i |q_i k_ji| (every key j, an upper bound)
+    for dequantized q [B, Hq, Lq, d], k [B, Hkv, Lk, d]; ``rows`` picks (b, h, i) samples."""
+    B, Hq, Lq, d = qd.shape
+    g = Hq // kd.shape[1]
+    if rows is None:
+        out = np.empty((B, Hq, Lq))
+        for b in range(B):
+            for h in range(Hq):
+                out[b, h] = (np.abs(qd[b, h]) @ np.abs(kd[b, h // g]).T).max(axis=1)
+    else:
+        out = np.array([(np.abs(qd[b, h, i]) @ np.abs(kd[b, h // g]).T).max() for b, h, i in rows])
+    return FP8_MFMA_EPS * abs(scale) * out
+
+
+def fp8_fwd_case(B, Hq, Hkv, Lq, Lk, d, causal, window, fmt, seed, scale=None, scale_mult=(1.0, 1.0, 1.0)):
+    label = f"fp8 fwd {fmt} B{B} Hq{Hq} Hkv{Hkv} Lq{Lq} Lk{Lk} d{d} causal{int(causal)} W{window} seed{seed} scale{scale}"
+    say(label)
+    qc, kc, vc, qs, ks, vs = wl.fp8_prefill_inputs(B, Hq, Hkv, Lq, Lk, d, fmt, seed=seed)
+    qs, ks, vs = qs * scale_mult[0], ks * scale_mult[1], vs * scale_mult[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    o = torch.full((B, Hq, Lq, d), float("nan"), device=DEV, dtype=torch.bfloat16)
+    lse = torch.full((B, Hq, Lq), float("nan"), device=DEV, dtype=torch.float32)
+    af.attn_fwd_fp8(qc.to(DEV), kc.to(DEV), vc.to(DEV), qkv_format=fmt, q_scale=qs, k_scale=ks, v_scale=vs,
+                    causal=causal, window=window, scale=scale, return_lse=True, out=o, lse_out=lse)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention_fp8(qc.numpy(), kc.numpy(), vc.numpy(), qs, ks, vs, fmt, scale=scale,
+                                        causal=causal, window=window)
+    vm = scale_mult[2]
+    extra = fp8_lse_allowance(oracle.dequantize(qc.numpy(), qs, fmt), oracle.dequantize(kc.numpy(), ks, fmt), scale)
+    stats = check(wl.to_f64(o) / vm, O_ref / vm, lse.cpu().numpy(), L_ref, "bf16", label, lse_abs_extra=extra)
+    say(stats)
+    return stats
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("L,causal", [(1, True), (33, False), (128, True), (129, True), (300, False), (517, True)])
+def test_fp8_fwd_lengths(fmt, d, L, causal):
+    fp8_fwd_case(1, 4, 2, L, L, d, causal, 0, fmt, seed=L + d)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 1), (12, 4)])
+def test_fp8_fwd_head_groups(fmt, Hq, Hkv):
+    fp8_fwd_case(2, Hq, Hkv, 200, 200, 128, True, 0, fmt, seed=Hq * Hkv)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("Lq,Lk", [(100, 333), (333, 100), (1, 700), (257, 64)])
+def test_fp8_fwd_unequal_lengths(fmt, Lq, Lk):
+    fp8_fwd_case(1, 4, 2, Lq, Lk, 128, True, 0, fmt, seed=Lq + Lk)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("W,d", [(1, 64), (37, 128), (64, 128), (500, 64)])
+def test_fp8_fwd_windows(fmt, W, d):
+    fp8_fwd_case(1, 4, 2, 600, 600, d, True, W, fmt, seed=W)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("scale,mult", [(0.0, (1.0, 1.0, 1.0)), (-0.1, (1.0, 1.0, 1.0)), (0.05, (3.0, 0.5, 7.0))])
+def test_fp8_fwd_scales(fmt, scale, mult):
+    fp8_fwd_case(1, 4, 2, 300, 300, 128, True, 0, fmt, seed=11, scale=scale, scale_mult=mult)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_fp8_fwd_named_workload_sampled(fmt):
+    """The causal GQA L4096 workload (B2 Hq32 Hkv8 d128) with FP8 inputs, full-size launch, checked
+    on sampled rows of every head; every output finite."""
+    c = wl.PREFILL["gqa_causal_bf16_L4096"]
+    say(f"fp8 fwd {fmt} gqa_causal L4096 full size on device")
+    qc, kc, vc, qs, ks, vs = wl.fp8_prefill_inputs(c.B, c.Hq, c.Hkv, c.Lq, c.Lk, c.d, fmt, seed=c.seed, device=DEV)
+    o, lse = af.attn_fwd_fp8(qc, kc, vc, qkv_format=fmt, q_scale=qs, k_scale=ks, v_scale=vs, causal=True,
+                             scale=c.scale, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+    rng = np.random.default_rng(c.seed)
+    fixed = [0, 1, 63, 64, 127, 128, 129, c.Lq // 2, c.Lq - 129, c.Lq - 2, c.Lq - 1]
+    rows = sorted(set(fixed) | set(rng.integers(0, c.Lq, 4).tolist()))
+    samples = [(b, h, i) for b in range(c.B) for h in range(c.Hq) for i in rows]
+    qd, kd, vd = (oracle.dequantize(x.cpu().numpy(), s_, fmt) for x, s_ in ((qc, qs), (kc, ks), (vc, vs)))
+    O_ref, L_ref = oracle.attention_rows(qd, kd, vd, samples, scale=c.scale, causal=True)
+    idx = tuple(np.array(samples).T)
+    extra = fp8_lse_allowance(qd, kd, c.scale, rows=samples)
+    say(fmt, check(wl.to_f64(o)[idx], O_ref, lse.cpu().numpy().astype(np.float64)[idx], L_ref, "bf16", "fp8 L4096",
+                   lse_abs_extra=extra))
