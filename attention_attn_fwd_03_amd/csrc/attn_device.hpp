@@ -74,6 +74,10 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_generic_ptr) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory instructions are outstanding and
+// leaves the LDS/scalar and export counters unconstrained (vmcnt split over bits 3:0 and 15:14).
+constexpr unsigned vmcnt_at_most(unsigned n) { return 0x0F70u | (n & 0xFu) | ((n >> 4) << 14); }
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // N wave-wide global->LDS loads of one tile: load i writes LDS bytes [j*1024, +1024) of `stage`,

@@ -335,14 +335,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int T_LOADS = T_TILE / 1024, TLW = (T_LOADS + 3) / 4;
   constexpr int OPB = 2 * D + 8;
   static_assert(T_TILE % 1024 == 0, "whole wave-wide loads");
-  // The four stages, which the epilogue reuses as its scratch (32 rows per wave).
-  constexpr int SMEM = 4 * T_TILE > 4 * 32 * OPB ? 4 * T_TILE : 4 * 32 * OPB;
+  // Three stages of Q and dO rows: the loads of step s + 2 are issued at the start of step s, so
+  // a step's loads have two steps of compute to land (one wave per SIMD hides nothing else).  The
+  // epilogue reuses the stages as its scratch (32 rows per wave).
+  constexpr int NST = 3;
+  constexpr int SMEM = 2 * NST * T_TILE > 4 * 32 * OPB ? 2 * NST * T_TILE : 4 * 32 * OPB;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
-  __shared__ __attribute__((aligned(16))) float row_lds[2][2][BQS];  // [stage][lse offset, D][row]
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  auto q_stage = [&](auto st) -> unsigned char* { return smem + decltype(st)::value * T_TILE; };
-  auto d_stage = [&](auto st) -> unsigned char* { return smem + (2 + decltype(st)::value) * T_TILE; };
+  __shared__ __attribute__((aligned(16))) float row_lds[2][2][BQS];  // [step parity][lse offset, D][row]
+  // The stage index is a runtime (wave-uniform) value: one copy of the loop body, so the per-lane
+  // LDS offsets are held once rather than once per stage.
+  auto q_stage = [&](int st) -> unsigned char* { return smem + st * T_TILE; };
+  auto d_stage = [&](int st) -> unsigned char* { return smem + (NST + st) * T_TILE; };
+  // Every wave issues T_LOADS / 4 loads per tile and two tiles per step; waiting until at most that
+  // many loads are outstanding leaves only the newest step's in flight (loads complete in order).
+  static_assert(T_LOADS % 4 == 0, "every wave issues the same number of loads");
+  constexpr unsigned kWaitAhead = vmcnt_at_most(2 * (T_LOADS / 4));
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;
@@ -404,7 +411,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   tile_offsets_swz<D>(t_voff, wave, 4, lane, BQS);
   // Step (qi, hd): query head hkv * group + hd, rows q_top - qi * BQS .. + BQS - 1.
   const int q_top = q0_first + (n_qsteps - 1) * BQS;
-  auto issue = [&](auto st, int qi, int hd) {
+  auto issue = [&](int st, int qi, int hd) {
     const int q0 = q_top - qi * BQS;
     const size_t off = ((size_t)(b * a.Hq + hkv * a.group + hd) * a.Lq) * D;
     issue_loads(rows_rsrc((const unsigned short*)a.q + off, q0, a.Lq, C::ROWB), q_stage(st), wave, 4, T_LOADS, t_voff);
@@ -420,20 +427,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   };
   const float c = a.c2;
 
-  int qi = 0, hd = 0;  // the current step
-  auto step = [&](int s, auto st) {
-    using Cur = decltype(st);
-    using Oth = std::integral_constant<int, Cur::value ^ 1>;
-    float next_row = 0.f;
-    const bool more = s + 1 < n_steps;
-    const int nhd = hd + 1 == a.group ? 0 : hd + 1, nqi = hd + 1 == a.group ? qi + 1 : qi;
-    if (more) {
-      issue(Oth{}, nqi, nhd);
-      if (tid < 2 * BQS) fetch_rows(nqi, nhd, next_row);
+  // Steps s, s + 1 and s + 2 as (qi, hd): heads inside each stretch of rows.
+  auto advance = [&](int& qi_, int& hd_) {
+    if (++hd_ == a.group) {
+      hd_ = 0;
+      ++qi_;
     }
+  };
+  int qi = 0, hd = 0, qi1 = 0, hd1 = 0;
+  advance(qi1, hd1);
+  int qi2 = qi1, hd2 = hd1;
+  advance(qi2, hd2);
+  int cur = 0;  // stage of step s; step s + 2 loads into stage (cur + 2) % NST
+  auto step = [&](int s) {
+    float next_row = 0.f;
+    const bool more = s + 1 < n_steps, more2 = s + 2 < n_steps;
+    if (more && tid < 2 * BQS) fetch_rows(qi1, hd1, next_row);
+    if (more2) issue(cur == 0 ? 2 : cur - 1, qi2, hd2);
     const int q0 = q_top - qi * BQS;
-    const unsigned char* Qs = q_stage(Cur{});
-    const unsigned char* Ds = d_stage(Cur{});
+    const unsigned char* Qs = q_stage(cur);
+    const unsigned char* Ds = d_stage(cur);
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const int qb0 = q0 + 32 * qb;
@@ -447,8 +460,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
           dp = mfma_32x32x16(a_frag_swz<D>(Ds, 32 * qb, ks, lane), vf[ks], dp);
         }
         // Rows of the S block are queries qb0 + 8*(i/4) + 4h + i%4.
-        const float* lr = row_lds[Cur::value][0] + 32 * qb + 4 * h;
-        const float* dr = row_lds[Cur::value][1] + 32 * qb + 4 * h;
+        const float* lr = row_lds[s & 1][0] + 32 * qb + 4 * h;
+        const float* dr = row_lds[s & 1][1] + 32 * qb + 4 * h;
         f32x16 xs[1], dd;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -481,15 +494,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
           }
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    if (more && tid < 2 * BQS) row_lds[Oth::value][tid / BQS][tid % BQS] = next_row;
-    qi = nqi;
-    hd = nhd;
+    // Step s + 1's tiles have landed (only step s + 2's may still be in flight), and so has its
+    // row fetch, which was issued before them.
+    if (more2)
+      __builtin_amdgcn_s_waitcnt(kWaitAhead);
+    else
+      __builtin_amdgcn_s_waitcnt(0);
+    if (more && tid < 2 * BQS) row_lds[(s + 1) & 1][tid / BQS][tid % BQS] = next_row;
+    qi = qi1;
+    hd = hd1;
+    qi1 = qi2;
+    hd1 = hd2;
+    advance(qi2, hd2);
+    cur = cur == NST - 1 ? 0 : cur + 1;
     __syncthreads();
   };
 
   if (n_steps > 0) {
-    issue(S0{}, 0, 0);
+    issue(0, 0, 0);
+    if (n_steps > 1) issue(1, qi1, hd1);
     if (tid < 2 * BQS) {
       float v;
       fetch_rows(0, 0, v);
@@ -497,10 +520,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int s = 0; s < n_steps; s += 2) {
-      step(s, S0{});
-      if (s + 1 < n_steps) step(s + 1, S1{});
-    }
+    for (int s = 0; s < n_steps; ++s) step(s);
   }
   const int nrows = a.Lk - kw;
   if (nrows > 0) {

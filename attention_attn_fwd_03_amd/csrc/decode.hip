@@ -58,10 +58,6 @@ struct DecCfg {
   static_assert(K_LOADS + V_LOADS <= 63, "one block's loads must fit the vmcnt counter");
 };
 
-// s_waitcnt immediate that waits until at most n vector-memory instructions are outstanding and
-// leaves the LDS/scalar and export counters unconstrained (vmcnt split over bits 3:0 and 15:14).
-constexpr unsigned vmcnt_at_most(unsigned n) { return 0x0F70u | (n & 0xFu) | ((n >> 4) << 14); }
-
 __device__ __forceinline__ bool decode_seq_valid(const DecArgs& a, int n, int64_t base, bool paged) {
   if (paged) return n >= 0 && n <= a.max_len;  // page entries are checked as they are read
   return n >= 0 && n <= a.max_len && base >= 0 && base + n <= a.pool_rows;
