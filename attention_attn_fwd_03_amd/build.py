@@ -51,7 +51,7 @@ def build(verbose: bool = False) -> str:
 
 def check_loadable(path: str) -> None:
     """Refuse a library with unresolved symbols (e.g. a kernel whose host launch stub was not
-    emitted): load it with every symbol bound now, as the GPU machine would at first use."""
+    emitted): load it with every symbol bound now, as its first use on a GPU host would."""
     import ctypes
     try:
         ctypes.CDLL(path, mode=os.RTLD_NOW | os.RTLD_LOCAL)
