@@ -434,7 +434,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       ++qi_;
     }
   };
-  int qi = 0, hd = 0, qi1 = 0, hd1 = 0;
+  int qi = 0, qi1 = 0, hd1 = 0;  // (the current step's head is implicit in its stage)
   advance(qi1, hd1);
   int qi2 = qi1, hd2 = hd1;
   advance(qi2, hd2);
@@ -502,7 +502,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       __builtin_amdgcn_s_waitcnt(0);
     if (more && tid < 2 * BQS) row_lds[(s + 1) & 1][tid / BQS][tid % BQS] = next_row;
     qi = qi1;
-    hd = hd1;
     qi1 = qi2;
     hd1 = hd2;
     advance(qi2, hd2);
