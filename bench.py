@@ -103,7 +103,7 @@ def decode_flops(n_tokens: int, Hq: int, Hkv: int, d: int) -> int:
 
 # ---- HBM traffic from counter runs -------------------------------------------------------------
 
-KERNEL_SOURCES = ["attn_device.hpp", "kernels.hpp", "plan.hpp", "prefill.hip", "decode.hip"]
+KERNEL_SOURCES = ["attn_device.hpp", "fp8_device.hpp", "kernels.hpp", "plan.hpp", "prefill.hip", "decode.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
 
