@@ -232,14 +232,15 @@ def test_fp8_fwd_scales(fmt, scale, mult):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-def test_fp8_fwd_named_workload_sampled(fmt):
-    """The causal GQA L4096 workload (B2 Hq32 Hkv8 d128) with FP8 inputs, full-size launch, checked
-    on sampled rows of every head; every output finite."""
-    c = wl.PREFILL["gqa_causal_bf16_L4096"]
-    say(f"fp8 fwd {fmt} gqa_causal L4096 full size on device")
+@pytest.mark.parametrize("name", ["gqa_causal_bf16_L4096", "swa_gqa_bf16_L16384_W4096"])
+def test_fp8_fwd_named_workload_sampled(fmt, name):
+    """The causal GQA L4096 workload (B2 Hq32 Hkv8 d128) and the window workload (L16384, W4096)
+    with FP8 inputs, full-size launch, checked on sampled rows of every head; every output finite."""
+    c = wl.PREFILL[name]
+    say(f"fp8 fwd {fmt} {name} full size on device")
     qc, kc, vc, qs, ks, vs = wl.fp8_prefill_inputs(c.B, c.Hq, c.Hkv, c.Lq, c.Lk, c.d, fmt, seed=c.seed, device=DEV)
     o, lse = af.attn_fwd_fp8(qc, kc, vc, qkv_format=fmt, q_scale=qs, k_scale=ks, v_scale=vs, causal=True,
-                             scale=c.scale, return_lse=True)
+                             window=c.window, scale=c.scale, return_lse=True)
     torch.cuda.synchronize()
     assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
     rng = np.random.default_rng(c.seed)
@@ -247,8 +248,39 @@ def test_fp8_fwd_named_workload_sampled(fmt):
     rows = sorted(set(fixed) | set(rng.integers(0, c.Lq, 4).tolist()))
     samples = [(b, h, i) for b in range(c.B) for h in range(c.Hq) for i in rows]
     qd, kd, vd = (oracle.dequantize(x.cpu().numpy(), s_, fmt) for x, s_ in ((qc, qs), (kc, ks), (vc, vs)))
-    O_ref, L_ref = oracle.attention_rows(qd, kd, vd, samples, scale=c.scale, causal=True)
+    O_ref, L_ref = oracle.attention_rows(qd, kd, vd, samples, scale=c.scale, causal=True, window=c.window)
     idx = tuple(np.array(samples).T)
     extra = fp8_lse_allowance(qd, kd, c.scale, rows=samples)
-    say(fmt, check(wl.to_f64(o)[idx], O_ref, lse.cpu().numpy().astype(np.float64)[idx], L_ref, "bf16", "fp8 L4096",
+    say(fmt, check(wl.to_f64(o)[idx], O_ref, lse.cpu().numpy().astype(np.float64)[idx], L_ref, "bf16", f"fp8 {name}",
                    lse_abs_extra=extra))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("name", ["gqa_decode_bf16", "mqa_decode_bf16"])
+def test_fp8_named_decode_paged(fmt, name):
+    """The full decode batch with an FP8 cache in 64-token pages scattered over the pool (spare
+    pages and page tails NaN codes): every output finite, 16+ sequences against the oracle."""
+    c = wl.DECODE[name]
+    P = 64
+    lens = wl.decode_lens(c.n_seq, c.len_lo, c.len_hi, c.lens_seed)
+    say(f"fp8 paged decode {fmt} {name} full size on device, P{P}")
+    q, kc, vc, table, lens_t, layout, ks, vs = wl.fp8_paged_decode_inputs(c.n_seq, c.Hq, c.Hkv, c.d, lens, P, fmt,
+                                                                          seed=c.value_seed, device=DEV, extra_pages=97)
+    o, lse = af.attn_decode_paged(q, kc, vc, table, lens_t, page_size=P, max_len=int(lens.max()), scale=c.scale,
+                                  return_lse=True, kv_format=fmt, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+    seqs = sorted(set(np.random.default_rng(c.value_seed).choice(c.n_seq, 16, replace=False).tolist())
+                  | {int(np.argmax(lens)), int(np.argmin(lens))})
+    tab = layout.table
+    used = sorted({int(tab[s_, j]) for s_ in seqs for j in range(-(-int(lens[s_]) // P))})
+    new_id = {p_: i for i, p_ in enumerate(used)}
+    rows = torch.tensor([p_ * P + r for p_ in used for r in range(P)], dtype=torch.int64, device=DEV)
+    kcomp, vcomp = kc.index_select(0, rows).cpu().numpy(), vc.index_select(0, rows).cpu().numpy()
+    sub = np.full((len(seqs), tab.shape[1]), -1, np.int64)
+    for i, s_ in enumerate(seqs):
+        for j in range(-(-int(lens[s_]) // P)):
+            sub[i, j] = new_id[int(tab[s_, j])]
+    O_ref, L_ref = oracle.decode_paged_fp8kv(wl.to_f64(q)[seqs], kcomp, vcomp, sub, lens[seqs], P, ks, vs, fmt,
+                                             scale=c.scale)
+    say(name, fmt, check(wl.to_f64(o)[seqs], O_ref, lse.cpu().numpy()[seqs], L_ref, "bf16", f"{name} {fmt} paged"))
