@@ -29,6 +29,13 @@ void set_scale(float scale, float& c, int& qmode) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// FP8 tensor scales are folded into the kernels' score scale c in fp32 (set_scale, then c *= f);
+// a product that overflows would turn every score into inf or NaN, so it is refused instead.
+bool scale_folds(float scale, float f) {
+  if (scale == 0.f) return true;  // run as Q = 0 with c = 1: nothing is folded
+  return std::isfinite(f) && std::isfinite(std::fabs(scale) * kLog2eHost * f);
+}
+
 int check_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int Hq,
               int Hkv, int Lq, int Lk, int d, int causal, int window, float scale) {
   if (!q || !k || !v || !o) return ATTN_ERR_NULL;
@@ -104,6 +111,7 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
   if (!(std::isfinite(q_scale) && q_scale > 0.f && std::isfinite(k_scale) && k_scale > 0.f &&
         std::isfinite(v_scale) && v_scale > 0.f))
     return ATTN_ERR_UNSUPPORTED;
+  if (!scale_folds(scale, q_scale * k_scale)) return ATTN_ERR_UNSUPPORTED;
   FwdArgs a = make_fwd_args(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d, causal, window, scale, false);
   if (a.qmode != 2) a.c *= q_scale * k_scale;  // scores: scale * q_scale * k_scale * (q . k codes); 2: zero scale
   a.v_scale = v_scale;
@@ -156,6 +164,7 @@ int decode_common(const void* q, const void* k_pool, const void* v_pool, const i
   if (a.kv_fmt < 0 || a.kv_fmt > 2) return ATTN_ERR_UNSUPPORTED;
   if (a.kv_fmt != 0 && !(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
     return ATTN_ERR_UNSUPPORTED;
+  if (a.kv_fmt != 0 && !scale_folds(scale, k_scale)) return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
   if (n_seq > 65535) return ATTN_ERR_SHAPE;
   const int group = Hq / Hkv;

@@ -16,8 +16,10 @@
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller, 16-byte aligned, row-major
- *     and contiguous.  The library allocates nothing, frees nothing and keeps no state besides
- *     read-only kernel code.  Inputs are not modified; outputs must not alias inputs.
+ *     and contiguous.  The library allocates nothing and frees nothing; besides its kernel code
+ *     it keeps only the decode worker count of each device, computed on first use from the
+ *     occupancy query and read-only afterwards.  Inputs are not modified; outputs must not
+ *     alias inputs.
  *   - Calls enqueue work on `stream` (a hipStream_t; NULL = the default stream) and return
  *     without synchronising.  Argument errors are detected on the host, before any device work,
  *     and returned as a status.  Device faults surface at the caller's next synchronisation.
@@ -43,8 +45,10 @@ typedef enum {
                                max_len < 1, pool_rows < 0, or a size too large to index (per head,
                                Lk*d*4 and max_len*Hkv*d*2 must stay below 2^31 bytes) */
   ATTN_ERR_UNSUPPORTED = 3, /* d not in {64, 128}; window > 0 without causal; scale not finite;
-                               a pointer not 16-byte aligned; an unknown FP8 format or an FP8
-                               pool scale that is not finite and > 0 */
+                               a pointer not 16-byte aligned; an unknown FP8 format, an FP8
+                               tensor scale that is not finite and > 0, or FP8 scales whose
+                               product with |scale| * log2(e) overflows fp32 (they are folded
+                               into the score scale) */
   ATTN_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than attn_decode_workspace_size / attn_bwd_workspace_size */
   ATTN_ERR_HIP = 5          /* the HIP runtime refused a launch */
 } attn_status;

@@ -85,6 +85,8 @@ def fwd8(**kw):
     (dict(qs=0.0), af.ATTN_ERR_UNSUPPORTED), (dict(ks=-1.0), af.ATTN_ERR_UNSUPPORTED),
     (dict(vs=math.nan), af.ATTN_ERR_UNSUPPORTED), (dict(scale=math.inf), af.ATTN_ERR_UNSUPPORTED),
     (dict(k=MISALIGNED), af.ATTN_ERR_UNSUPPORTED),
+    # the scales fold into the score scale in fp32: a product that overflows is refused
+    (dict(qs=1e30, ks=1e30), af.ATTN_ERR_UNSUPPORTED), (dict(scale=1e10, qs=1e20, ks=1e10), af.ATTN_ERR_UNSUPPORTED),
 ])
 def test_fwd_fp8_rejects_bad_arguments(kw, status):
     assert fwd8(**kw) == status
@@ -119,6 +121,7 @@ def dec8p(**kw):
     (dict(d=96), af.ATTN_ERR_UNSUPPORTED), (dict(scale=math.nan), af.ATTN_ERR_UNSUPPORTED),
     (dict(kp=MISALIGNED), af.ATTN_ERR_UNSUPPORTED),
     (dict(ws=None), af.ATTN_ERR_WORKSPACE), (dict(ws_bytes=16), af.ATTN_ERR_WORKSPACE),
+    (dict(scale=1e20, ks=1e20), af.ATTN_ERR_UNSUPPORTED),  # k_scale folds into the score scale
 ])
 def test_decode_fp8_rejects_bad_arguments(kw, status):
     assert dec8(**kw) == status
@@ -129,7 +132,7 @@ def test_decode_fp8_rejects_bad_arguments(kw, status):
     (dict(vs=-0.5), af.ATTN_ERR_UNSUPPORTED), (dict(ks=math.inf), af.ATTN_ERR_UNSUPPORTED),
     (dict(table=None), af.ATTN_ERR_NULL), (dict(page=0), af.ATTN_ERR_SHAPE), (dict(stride=6), af.ATTN_ERR_SHAPE),
     (dict(page=6, stride=17), af.ATTN_ERR_UNSUPPORTED),     # not a multiple of the 4-token block
-    (dict(ws=None), af.ATTN_ERR_WORKSPACE),
+    (dict(ws=None), af.ATTN_ERR_WORKSPACE), (dict(scale=-1e20, ks=1e20), af.ATTN_ERR_UNSUPPORTED),
 ])
 def test_decode_paged_fp8_rejects_bad_arguments(kw, status):
     assert dec8p(**kw) == status
