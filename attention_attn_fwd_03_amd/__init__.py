@@ -91,18 +91,39 @@ def _check(status: int):
         raise RuntimeError(status_str(status))
 
 
-def _stream():
-    import torch
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-
-
 def _require_gpu(*tensors):
+    """Contiguous GPU tensors, all on one device; returns that device."""
     import torch
     for t in tensors:
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
             raise ValueError("attnfwd works on GPU tensors only")
         if not t.is_contiguous():
             raise ValueError("attnfwd needs contiguous tensors")
+    dev = tensors[0].device
+    if any(t.device != dev for t in tensors):
+        raise ValueError("attnfwd needs all tensors on one GPU")
+    return dev
+
+
+def _output(t, shape, dtype, device, name: str):
+    """A new output tensor, or the caller's ``t`` once it is known to have exactly this shape,
+    dtype and device (the library sees only its address and writes the full extent)."""
+    import torch
+    shape = tuple(int(x) for x in shape)
+    if t is None:
+        return torch.empty(shape, device=device, dtype=dtype)
+    _require_gpu(t)
+    if tuple(t.shape) != shape or t.dtype != dtype or t.device != device:
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {shape} on {device}")
+    return t
+
+
+def _run(device, fn, *args):
+    """Call entry point ``fn`` with ``args`` and the current stream of ``device``, with that device
+    current (the library launches on the current device)."""
+    import torch
+    with torch.cuda.device(device):
+        _check(fn(*args, ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)))
 
 
 def attn_fwd(q, k, v, *, causal: bool = False, window: int = 0, scale: float | None = None,
@@ -112,7 +133,7 @@ def attn_fwd(q, k, v, *, causal: bool = False, window: int = 0, scale: float | N
     Returns O [B, Hq, Lq, d] (same dtype), and LSE [B, Hq, Lq] fp32 (natural log) when
     ``return_lse``.  ``scale`` defaults to 1/sqrt(d)."""
     import torch
-    _require_gpu(q, k, v)
+    dev = _require_gpu(q, k, v)
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("expected 4-d tensors [B, H, L, d]")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
@@ -123,14 +144,11 @@ def attn_fwd(q, k, v, *, causal: bool = False, window: int = 0, scale: float | N
         raise ValueError("shape mismatch between q, k and v")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty_like(q) if out is None else out
-    _require_gpu(o)
-    lse = None
-    if return_lse:
-        lse = torch.empty((B, Hq, Lq), device=q.device, dtype=torch.float32) if lse_out is None else lse_out
+    o = _output(out, q.shape, q.dtype, dev, "out")
+    lse = _output(lse_out, (B, Hq, Lq), torch.float32, dev, "lse_out") if return_lse else None
     fn = lib().attn_fwd if q.dtype == torch.bfloat16 else lib().attn_fwd_f32
-    _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr() if lse is not None else None,
-              B, Hq, Hkv, Lq, Lk, d, int(bool(causal)), int(window), float(scale), _stream()))
+    _run(dev, fn, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr() if lse is not None else None,
+         B, Hq, Hkv, Lq, Lk, d, int(bool(causal)), int(window), float(scale))
     return (o, lse) if return_lse else o
 
 
@@ -145,9 +163,11 @@ def attn_bwd(q, k, v, o, dout, lse, *, causal: bool = False, window: int = 0, sc
     and scale).  bf16.  ``workspace``: optional uint8 device tensor of bwd_workspace_size bytes;
     ``out``: optional (dq, dk, dv) tensors to write."""
     import torch
-    _require_gpu(q, k, v, o, dout, lse)
+    dev = _require_gpu(q, k, v, o, dout, lse)
     if any(t.dtype != torch.bfloat16 for t in (q, k, v, o, dout)) or lse.dtype != torch.float32:
         raise ValueError("attn_bwd takes bfloat16 q, k, v, o, dout and float32 lse")
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("expected 4-d tensors [B, H, L, d]")
     B, Hq, Lq, d = q.shape
     Hkv, Lk = k.shape[1], k.shape[2]
     if (tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != d or tuple(o.shape) != tuple(q.shape)
@@ -157,16 +177,16 @@ def attn_bwd(q, k, v, o, dout, lse, *, causal: bool = False, window: int = 0, sc
         scale = 1.0 / math.sqrt(d)
     need = bwd_workspace_size(B, Hq, Lq)
     if workspace is None:
-        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
-    _require_gpu(workspace)
-    if out is None:
-        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
-    dq, dk, dv = out
-    _require_gpu(dq, dk, dv)
-    _check(lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                          dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Lq, Lk, d, int(bool(causal)),
-                          int(window), float(scale), workspace.data_ptr(),
-                          workspace.numel() * workspace.element_size(), _stream()))
+        workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+    if _require_gpu(workspace) != dev:
+        raise ValueError("the workspace must be on the tensors' GPU")
+    dq, dk, dv = (None, None, None) if out is None else out
+    dq = _output(dq, q.shape, torch.bfloat16, dev, "dq")
+    dk = _output(dk, k.shape, torch.bfloat16, dev, "dk")
+    dv = _output(dv, v.shape, torch.bfloat16, dev, "dv")
+    _run(dev, lib().attn_bwd, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Lq, Lk, d, int(bool(causal)), int(window),
+         float(scale), workspace.data_ptr(), workspace.numel() * workspace.element_size())
     return dq, dk, dv
 
 
@@ -176,26 +196,24 @@ def attn_fwd_fp8(q, k, v, *, qkv_format: str, q_scale: float, k_scale: float, v_
     ``qkv_format`` ('e4m3fn' / 'e5m2') with per-tensor scales (real value = scale * code value).
     Returns O [B, Hq, Lq, d] bf16 and, when ``return_lse``, LSE [B, Hq, Lq] fp32."""
     import torch
-    _require_gpu(q, k, v)
+    dev = _require_gpu(q, k, v)
     if q.dtype != torch.uint8 or k.dtype != torch.uint8 or v.dtype != torch.uint8:
         raise ValueError("attn_fwd_fp8 takes uint8 FP8 codes")
     if qkv_format not in KV_FORMATS:
         raise ValueError("qkv_format must be 'e4m3fn' or 'e5m2'")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("expected 4-d tensors [B, H, L, d]")
     B, Hq, Lq, d = q.shape
     Bk, Hkv, Lk, dk = k.shape
     if Bk != B or dk != d or tuple(v.shape) != tuple(k.shape):
         raise ValueError("shape mismatch between q, k and v")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty((B, Hq, Lq, d), device=q.device, dtype=torch.bfloat16) if out is None else out
-    _require_gpu(o)
-    lse = None
-    if return_lse:
-        lse = torch.empty((B, Hq, Lq), device=q.device, dtype=torch.float32) if lse_out is None else lse_out
-    _check(lib().attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                              lse.data_ptr() if lse is not None else None, B, Hq, Hkv, Lq, Lk, d, int(bool(causal)),
-                              int(window), float(scale), KV_FORMATS[qkv_format], float(q_scale), float(k_scale),
-                              float(v_scale), _stream()))
+    o = _output(out, (B, Hq, Lq, d), torch.bfloat16, dev, "out")
+    lse = _output(lse_out, (B, Hq, Lq), torch.float32, dev, "lse_out") if return_lse else None
+    _run(dev, lib().attn_fwd_fp8, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+         lse.data_ptr() if lse is not None else None, B, Hq, Hkv, Lq, Lk, d, int(bool(causal)), int(window),
+         float(scale), KV_FORMATS[qkv_format], float(q_scale), float(k_scale), float(v_scale))
     return (o, lse) if return_lse else o
 
 
@@ -211,7 +229,9 @@ def attn_fwd_varlen(q, k_pool, v_pool, cu_seqlens_q, kv_offsets, kv_lens, *, max
     kv_lens int32, kv_offsets int64, all on the device; max_seqlen_q >= every sequence's new
     tokens.  Returns O [total_q, Hq, d] and, when ``return_lse``, LSE [total_q, Hq] fp32."""
     import torch
-    _require_gpu(q, k_pool, v_pool, cu_seqlens_q, kv_offsets, kv_lens)
+    dev = _require_gpu(q, k_pool, v_pool, cu_seqlens_q, kv_offsets, kv_lens)
+    if q.dim() != 3 or k_pool.dim() != 3:
+        raise ValueError("expected q [total_q, Hq, d] and pools [T, Hkv, d]")
     if q.dtype != torch.bfloat16 or k_pool.dtype != torch.bfloat16 or v_pool.dtype != torch.bfloat16:
         raise ValueError("ragged prefill takes bfloat16 q and pools")
     if cu_seqlens_q.dtype != torch.int32 or kv_lens.dtype != torch.int32 or kv_offsets.dtype != torch.int64:
@@ -224,15 +244,24 @@ def attn_fwd_varlen(q, k_pool, v_pool, cu_seqlens_q, kv_offsets, kv_lens, *, max
         raise ValueError("shape mismatch between q, pools, cu_seqlens_q, kv_offsets and kv_lens")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty_like(q) if out is None else out
-    lse = None
-    if return_lse:
-        lse = torch.empty((total_q, Hq), device=q.device, dtype=torch.float32) if lse_out is None else lse_out
-    _check(lib().attn_fwd_varlen(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), o.data_ptr(),
-                                 lse.data_ptr() if lse is not None else None, cu_seqlens_q.data_ptr(),
-                                 kv_offsets.data_ptr(), kv_lens.data_ptr(), n_seq, Hq, Hkv, d, int(max_seqlen_q),
-                                 total_q, T, int(bool(causal)), int(window), float(scale), _stream()))
+    o = _output(out, q.shape, torch.bfloat16, dev, "out")
+    lse = _output(lse_out, (total_q, Hq), torch.float32, dev, "lse_out") if return_lse else None
+    _run(dev, lib().attn_fwd_varlen, q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), o.data_ptr(),
+         lse.data_ptr() if lse is not None else None, cu_seqlens_q.data_ptr(), kv_offsets.data_ptr(),
+         kv_lens.data_ptr(), n_seq, Hq, Hkv, d, int(max_seqlen_q), total_q, T, int(bool(causal)), int(window),
+         float(scale))
     return (o, lse) if return_lse else o
+
+
+def _decode_workspace(workspace, N, Hq, Hkv, d, max_len, dev):
+    """The caller's workspace (its size is checked by the library), or a new one of the size the
+    library asks for."""
+    import torch
+    if workspace is None:
+        return torch.empty(max(decode_workspace_size(N, Hq, Hkv, d, max_len), 16), device=dev, dtype=torch.uint8)
+    if _require_gpu(workspace) != dev:
+        raise ValueError("the workspace must be on the tensors' GPU")
+    return workspace
 
 
 def _kv_format(q, k_pool, v_pool, kv_format, k_scale, v_scale):
@@ -261,30 +290,28 @@ def attn_decode(q, k_pool, v_pool, offsets, lens, *, max_len: int, window: int =
     offsets int64 [N] (first pool row of each sequence); lens int32 [N]; max_len >= max(lens).
     Returns O [N, Hq, d] bf16 and, when ``return_lse``, LSE [N, Hq] fp32."""
     import torch
-    _require_gpu(q, k_pool, v_pool, offsets, lens)
+    dev = _require_gpu(q, k_pool, v_pool, offsets, lens)
     fmt = _kv_format(q, k_pool, v_pool, kv_format, k_scale, v_scale)
     if offsets.dtype != torch.int64 or lens.dtype != torch.int32:
         raise ValueError("offsets must be int64 and lens int32")
+    if q.dim() != 3 or k_pool.dim() != 3:
+        raise ValueError("expected q [N, Hq, d] and pools [T, Hkv, d]")
     N, Hq, d = q.shape
     T, Hkv, dk = k_pool.shape
     if dk != d or tuple(v_pool.shape) != tuple(k_pool.shape) or offsets.numel() != N or lens.numel() != N:
         raise ValueError("shape mismatch between q, pools, offsets and lens")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    need = decode_workspace_size(N, Hq, Hkv, d, max_len)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
-    o = torch.empty_like(q) if out is None else out
-    lse = None
-    if return_lse:
-        lse = torch.empty((N, Hq), device=q.device, dtype=torch.float32) if lse_out is None else lse_out
+    workspace = _decode_workspace(workspace, N, Hq, Hkv, d, max_len, dev)
+    o = _output(out, q.shape, torch.bfloat16, dev, "out")
+    lse = _output(lse_out, (N, Hq), torch.float32, dev, "lse_out") if return_lse else None
     args = (q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), offsets.data_ptr(), lens.data_ptr(), o.data_ptr(),
             lse.data_ptr() if lse is not None else None, N, Hq, Hkv, d, T, int(max_len), int(window), float(scale))
-    tail = (workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream())
+    tail = (workspace.data_ptr(), workspace.numel() * workspace.element_size())
     if fmt == 0:
-        _check(lib().attn_decode(*args, *tail))
+        _run(dev, lib().attn_decode, *args, *tail)
     else:
-        _check(lib().attn_decode_fp8(*args, fmt, float(k_scale), float(v_scale), *tail))
+        _run(dev, lib().attn_decode_fp8, *args, fmt, float(k_scale), float(v_scale), *tail)
     return (o, lse) if return_lse else o
 
 
@@ -300,8 +327,10 @@ def attn_decode_paged(q, k_pool, v_pool, block_table, lens, *, page_size: int, m
     max_len >= max(lens).  FP8 pools as attn_decode.  Returns O [N, Hq, d] bf16 and, when
     ``return_lse``, LSE [N, Hq]."""
     import torch
-    _require_gpu(q, k_pool, v_pool, block_table, lens)
+    dev = _require_gpu(q, k_pool, v_pool, block_table, lens)
     fmt = _kv_format(q, k_pool, v_pool, kv_format, k_scale, v_scale)
+    if q.dim() != 3 or k_pool.dim() != 3:
+        raise ValueError("expected q [N, Hq, d] and pools [pool_pages * page_size, Hkv, d]")
     if block_table.dtype != torch.int32 or lens.dtype != torch.int32:
         raise ValueError("block_table and lens must be int32")
     if block_table.dim() != 2 or not block_table.is_contiguous():
@@ -315,21 +344,17 @@ def attn_decode_paged(q, k_pool, v_pool, block_table, lens, *, page_size: int, m
         raise ValueError("shape mismatch between q, pools, block_table and lens")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    need = decode_workspace_size(N, Hq, Hkv, d, max_len)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
-    o = torch.empty_like(q) if out is None else out
-    lse = None
-    if return_lse:
-        lse = torch.empty((N, Hq), device=q.device, dtype=torch.float32) if lse_out is None else lse_out
+    workspace = _decode_workspace(workspace, N, Hq, Hkv, d, max_len, dev)
+    o = _output(out, q.shape, torch.bfloat16, dev, "out")
+    lse = _output(lse_out, (N, Hq), torch.float32, dev, "lse_out") if return_lse else None
     args = (q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), block_table.data_ptr(), int(block_table.shape[1]),
             int(page_size), T // page_size, lens.data_ptr(), o.data_ptr(), lse.data_ptr() if lse is not None else None,
             N, Hq, Hkv, d, int(max_len), int(window), float(scale))
-    tail = (workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream())
+    tail = (workspace.data_ptr(), workspace.numel() * workspace.element_size())
     if fmt == 0:
-        _check(lib().attn_decode_paged(*args, *tail))
+        _run(dev, lib().attn_decode_paged, *args, *tail)
     else:
-        _check(lib().attn_decode_paged_fp8(*args, fmt, float(k_scale), float(v_scale), *tail))
+        _run(dev, lib().attn_decode_paged_fp8, *args, fmt, float(k_scale), float(v_scale), *tail)
     return (o, lse) if return_lse else o
 
 
