@@ -67,7 +67,7 @@ MIXED = [1, 31, 32, 33, 0, 64, 5, 100, 1000, 2049, 3, 777]
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (32, 1), (8, 8), (40, 8)])
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (32, 1), (8, 8), (40, 8), (64, 1)])
 def test_fp8_decode_shapes(fmt, d, Hq, Hkv):
     fp8_case(MIXED, Hq, Hkv, d, fmt, seed=Hq + Hkv + d)
 
@@ -127,14 +127,14 @@ def test_fp8_named_decode(fmt, name):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("Hkv,P", [(8, 16), (8, 64), (1, 32), (2, 48)])
-def test_fp8_decode_paged(fmt, Hkv, P):
+@pytest.mark.parametrize("Hkv,P,d", [(8, 16, 128), (8, 64, 128), (1, 32, 128), (2, 48, 128), (8, 32, 64), (1, 64, 64)])
+def test_fp8_decode_paged(fmt, Hkv, P, d):
     lens = np.array(MIXED, np.int32)
-    label = f"fp8 paged {fmt} Hkv{Hkv} P{P}"
+    label = f"fp8 paged {fmt} Hkv{Hkv} P{P} d{d}"
     say(label)
-    q, kc, vc, table, lens_t, layout, ks, vs = wl.fp8_paged_decode_inputs(len(lens), 32, Hkv, 128, lens, P, fmt,
-                                                                          seed=P + Hkv, extra_pages=3)
-    o = torch.full((len(lens), 32, 128), float("nan"), device=DEV, dtype=torch.bfloat16)
+    q, kc, vc, table, lens_t, layout, ks, vs = wl.fp8_paged_decode_inputs(len(lens), 32, Hkv, d, lens, P, fmt,
+                                                                          seed=P + Hkv + d, extra_pages=3)
+    o = torch.full((len(lens), 32, d), float("nan"), device=DEV, dtype=torch.bfloat16)
     lse = torch.full((len(lens), 32), float("nan"), device=DEV, dtype=torch.float32)
     af.attn_decode_paged(q.to(DEV), kc.to(DEV), vc.to(DEV), table.to(DEV), lens_t.to(DEV), page_size=P,
                          max_len=int(lens.max()), scale=0.0884, return_lse=True, out=o, lse_out=lse, kv_format=fmt,
