@@ -23,6 +23,9 @@
  *   - Calls enqueue work on `stream` (a hipStream_t; NULL = the default stream) and return
  *     without synchronising.  Argument errors are detected on the host, before any device work,
  *     and returned as a status.  Device faults surface at the caller's next synchronisation.
+ *     A call only launches kernels on `stream` (no copies, memsets or allocations), so it may be
+ *     captured into a HIP graph and replayed; sizes and pointers are fixed at capture, while the
+ *     contents of device arrays (lens, offsets, block tables, q, ...) are read at each replay.
  *   - scale is explicit (1/sqrt(d) is the usual choice); any finite value, including 0 and
  *     negative values, is accepted.
  *   - A query row that sees no key gets O = 0 and LSE = -inf.  NaN/Inf inputs propagate.
