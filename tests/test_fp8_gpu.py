@@ -127,6 +127,32 @@ def test_fp8_named_decode(fmt, name):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("W,Hkv", [(1, 8), (45, 2), (700, 1)])
+def test_fp8_decode_paged_window(fmt, W, Hkv):
+    """An FP8 paged cache under a window: block 0 starts at the block boundary below the first
+    visible key (masked up to it), and table entries of pages wholly before the window are -1, so
+    reading one would turn the sequence's output into NaN."""
+    P = 32
+    lens = np.array([1, 50, 1031, 3 * 1024 + 1, 2000, 33, 64, 0], np.int32)
+    label = f"fp8 paged window {fmt} W{W} Hkv{Hkv}"
+    say(label)
+    q, kc, vc, table, lens_t, layout, ks, vs = wl.fp8_paged_decode_inputs(len(lens), 16, Hkv, 128, lens, P, fmt,
+                                                                          seed=W + Hkv, extra_pages=2)
+    ktab = table.clone()  # the kernel's table; the oracle gathers every token, so it gets the full one
+    for s_, n in enumerate(layout.lens):
+        ktab[s_, :max(int(n) - W, 0) // P] = -1
+    o = torch.full((len(lens), 16, 128), float("nan"), device=DEV, dtype=torch.bfloat16)
+    lse = torch.full((len(lens), 16), float("nan"), device=DEV, dtype=torch.float32)
+    af.attn_decode_paged(q.to(DEV), kc.to(DEV), vc.to(DEV), ktab.to(DEV), lens_t.to(DEV), page_size=P,
+                         max_len=int(lens.max()), window=W, scale=0.0884, return_lse=True, out=o, lse_out=lse,
+                         kv_format=fmt, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.decode_paged_fp8kv(wl.to_f64(q), kc.numpy(), vc.numpy(), layout.table, layout.lens, P,
+                                             ks, vs, fmt, scale=0.0884, window=W)
+    check(wl.to_f64(o), O_ref, lse.cpu().numpy(), L_ref, "bf16", label)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("Hkv,P,d", [(8, 16, 128), (8, 64, 128), (1, 32, 128), (2, 48, 128), (8, 32, 64), (1, 64, 64)])
 def test_fp8_decode_paged(fmt, Hkv, P, d):
     lens = np.array(MIXED, np.int32)

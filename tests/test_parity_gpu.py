@@ -508,8 +508,8 @@ def test_decode_paged_page_sizes(Hkv, d):
         decode_paged_case(lens, Hq, Hkv, d, P, seed=1800 + P + Hkv + d)
 
 
-@pytest.mark.parametrize("W", [1, 31, 100, 600, 5000])
-def test_decode_paged_window(W):
+@pytest.mark.parametrize("W,Hkv", [(1, 2), (31, 2), (100, 2), (600, 2), (5000, 2), (700, 1), (45, 8)])
+def test_decode_paged_window(W, Hkv):
     """Under a window the first block starts at the page boundary below the first visible key
     (masked up to it); table entries of pages wholly before the window are set to -1 for the
     kernel, which must not read them."""
@@ -521,7 +521,7 @@ def test_decode_paged_window(W):
             table[s, :lo // P] = -1
         return table
 
-    decode_paged_case([1, 50, 1031, 3 * 1024 + 1, 2000, 33, 64], 8, 2, 128, P, window=W, seed=1900 + W,
+    decode_paged_case([1, 50, 1031, 3 * 1024 + 1, 2000, 33, 64], 8, Hkv, 128, P, window=W, seed=1900 + W + Hkv,
                       table_fn=drop_early_pages)
 
 
