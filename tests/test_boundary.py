@@ -34,6 +34,41 @@ def test_library_loads_and_exports_header_symbols():
         assert hasattr(L, n), n
 
 
+def declared_prototypes():
+    """{name: [parameter type, ...]} of every function include/attn.h declares."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"^\s*(?:const\s+)?\w+\**\s+\**(attn_\w+)\s*\(([^)]*)\)\s*;", text, flags=re.M):
+        params = [" ".join(p.split()) for p in m.group(2).split(",") if p.strip()]
+        out[m.group(1)] = [re.sub(r"\s*\b\w+$", "", p) if not p.endswith("*") else p for p in params]
+    return out
+
+
+def _ctype_class(t: str):
+    """The ctypes argtype a C parameter type needs: pointers of any kind are c_void_p or a
+    POINTER(...); int, float, int64_t and size_t must match exactly."""
+    if t.endswith("*"):
+        return "pointer"
+    return {"int": ctypes.c_int, "float": ctypes.c_float, "int64_t": ctypes.c_int64, "size_t": ctypes.c_size_t}[t]
+
+
+def test_binding_argtypes_match_the_header():
+    """Every entry point's ctypes argtypes agree with its C prototype in count, and in kind for each
+    parameter (a dropped or swapped argument would pass garbage to the library)."""
+    L = af.lib()
+    protos = declared_prototypes()
+    assert set(protos) == set(af.EXPORTS)
+    for name, params in protos.items():
+        argtypes = getattr(L, name).argtypes
+        assert argtypes is not None and len(argtypes) == len(params), (name, params, argtypes)
+        for i, (t, a) in enumerate(zip(params, argtypes)):
+            want = _ctype_class(t)
+            if want == "pointer":
+                assert a is ctypes.c_void_p or issubclass(a, ctypes._Pointer) or a is ctypes.c_char_p, (name, i, t, a)
+            else:
+                assert a is want, (name, i, t, a)
+
+
 def test_status_strings():
     for s in range(6):
         assert af.status_str(s).startswith("ATTN_")
