@@ -21,7 +21,7 @@ KV_FORMATS = {"e4m3fn": 1, "e5m2": 2}  # attn_kv_format
 EXPORTS = ["attn_fwd", "attn_fwd_f32", "attn_fwd_varlen", "attn_decode_workspace_size", "attn_decode",
            "attn_decode_paged", "attn_status_str", "attn_fwd_plan", "attn_fwd_schedule", "attn_fwd_varlen_schedule",
            "attn_decode_plan", "attn_bwd_workspace_size", "attn_bwd", "attn_decode_fp8", "attn_decode_paged_fp8",
-           "attn_fwd_fp8"]
+           "attn_fwd_fp8", "attn_decode_rows"]
 
 
 class FwdPlanInfo(ctypes.Structure):
@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_varlen_schedule.restype = i32
     L.attn_decode_plan.argtypes = [i32, i32, i32, i32] + [ctypes.POINTER(ctypes.c_int32)] * 3
     L.attn_decode_plan.restype = i32
+    L.attn_decode_rows.argtypes = [i32, i32, vp, vp, vp, i64]
+    L.attn_decode_rows.restype = i32
     _lib = L
     return L
 
@@ -390,6 +392,15 @@ def decode_plan(n_seq: int, Hq: int, Hkv: int, d: int) -> tuple[int, int, int]:
     _check(lib().attn_decode_plan(int(n_seq), int(Hq), int(Hkv), int(d), ctypes.byref(t), ctypes.byref(r),
                                   ctypes.byref(b)))
     return t.value, r.value, b.value
+
+
+def decode_rows(Hq: int, Hkv: int) -> np.ndarray:
+    """[rows_per_seq, 3] (KV head, first query head, query heads) of each row of the decode split."""
+    n = max(1, int(Hkv)) * max(1, -(-(int(Hq) // max(1, int(Hkv))) // 32))  # enough for either layout
+    kv, first, nh = (np.zeros(n, np.int32) for _ in range(3))
+    _check(lib().attn_decode_rows(int(Hq), int(Hkv), kv.ctypes.data, first.ctypes.data, nh.ctypes.data, n))
+    rows = 1 if (Hq <= 32 and 32 % Hkv == 0) else n
+    return np.stack([kv[:rows], first[:rows], nh[:rows]], axis=1)
 
 
 def decode_pieces(lens, teams: int, tokens_per_block: int = 32, window: int = 0, max_len: int | None = None,

@@ -430,6 +430,19 @@ int attn_fwd_varlen_schedule(int n_seq, int Hq, int Hkv, int max_seqlen_q, int32
   return ATTN_OK;
 }
 
+int attn_decode_rows(int Hq, int Hkv, int32_t* kv_head, int32_t* first_head, int32_t* n_heads, int64_t out_len) {
+  if (!kv_head || !first_head || !n_heads) return ATTN_ERR_NULL;
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  const int rows = decode_rows_per_seq(Hq, Hkv);
+  if (out_len < rows) return ATTN_ERR_SHAPE;
+  for (int u = 0; u < rows; ++u) {
+    kv_head[u] = decode_row_kv_head(Hq, Hkv, u);
+    first_head[u] = decode_row_first_head(Hq, Hkv, u);
+    n_heads[u] = decode_row_heads(Hq, Hkv, u);
+  }
+  return ATTN_OK;
+}
+
 int attn_decode_plan(int n_seq, int Hq, int Hkv, int d, int32_t* teams, int32_t* rows_per_seq,
                      int32_t* tokens_per_block) {
   if (!teams || !rows_per_seq || !tokens_per_block) return ATTN_ERR_NULL;

@@ -157,8 +157,8 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
   const int lane = threadIdx.x, h = lane >> 5, col = lane & 31;
   const int team = blockIdx.x / a.rows, u = blockIdx.x % a.rows;
   const int pack = a.pack, tpb = a.tpb, pack_log2 = __builtin_ctz((unsigned)a.pack);
-  const int kvh0 = pack > 1 ? 0 : u / a.hblocks;                               // KV head of block row 0
-  const int qbase = pack > 1 ? 0 : kvh0 * a.group + (u % a.hblocks) * 32;      // query head of column 0
+  const int kvh0 = decode_row_kv_head(a.Hq, a.Hkv, u);      // KV head of block row 0
+  const int qbase = decode_row_first_head(a.Hq, a.Hkv, u);  // query head of column 0
   const bool writer = blockIdx.x == 0;  // publishes the share and the prefix for the merge pass
 
   // ---- This team's share of the blocks: [start, stop) of the concatenated block order. ----
@@ -263,7 +263,9 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
   const auto* lens_c = kernel_constant(a.lens);
   const auto* offs_c = kernel_constant(a.offsets);
   const QTransform qt = q_transform(a.qmode);
-  const bool q_ok = col < a.nh;  // columns past the row's heads read head qbase and are zeroed
+  // Columns past the row's own heads (the last head block of a group may hold fewer than 32)
+  // read head qbase instead, are zeroed and never stored.
+  const bool q_ok = col < decode_row_heads(a.Hq, a.Hkv, u);
 
   if (a.n_seq > 64) {
     n_cur = lens_c[s_cur];

@@ -190,6 +190,22 @@ ATTN_HD int decode_tokens_per_block(int Hq, int Hkv) { return kDecodeBlockRows /
 ATTN_HD int decode_rows_per_seq(int Hq, int Hkv) {
   return decode_pack(Hq, Hkv) > 1 ? 1 : Hkv * decode_head_blocks(Hq / Hkv);
 }
+// Row u of a sequence: its KV head, the first query head it serves and how many it serves.  In
+// the packed layout the one row serves all Hq heads; otherwise row u is KV head u / head_blocks
+// and head block u % head_blocks of that head's group, whose last block may hold fewer than 32.
+ATTN_HD int decode_row_kv_head(int Hq, int Hkv, int u) {
+  return decode_pack(Hq, Hkv) > 1 ? 0 : u / decode_head_blocks(Hq / Hkv);
+}
+ATTN_HD int decode_row_first_head(int Hq, int Hkv, int u) {
+  if (decode_pack(Hq, Hkv) > 1) return 0;
+  const int group = Hq / Hkv, hb = decode_head_blocks(group);
+  return (u / hb) * group + (u % hb) * 32;
+}
+ATTN_HD int decode_row_heads(int Hq, int Hkv, int u) {
+  if (decode_pack(Hq, Hkv) > 1) return Hq;
+  const int group = Hq / Hkv, left = group - (u % decode_head_blocks(group)) * 32;
+  return left < 32 ? left : 32;
+}
 // Query heads per partial slot.
 ATTN_HD int decode_heads_per_slot(int Hq, int Hkv) {
   const int group = Hq / Hkv;

@@ -247,6 +247,15 @@ int attn_fwd_varlen_schedule(int n_seq, int Hq, int Hkv, int max_seqlen_q, int32
 int attn_decode_plan(int n_seq, int Hq, int Hkv, int d, int32_t* teams, int32_t* rows_per_seq,
                      int32_t* tokens_per_block);
 
+/* The rows of one sequence in the decode split (host only, no device work): for each row u <
+ * attn_decode_plan's rows_per_seq, kv_head[u] is the KV head its blocks hold (0 in the packed
+ * layout, whose blocks hold every KV head), and the row serves query heads first_head[u] ..
+ * first_head[u] + n_heads[u] - 1 of each sequence; the kernels read and write q and o rows of
+ * those heads only.  out_len is the length of each output array (host memory); ATTN_ERR_SHAPE
+ * if it is below rows_per_seq or the head counts are invalid. */
+int attn_decode_rows(int Hq, int Hkv, int32_t* kv_head, int32_t* first_head, int32_t* n_heads,
+                     int64_t out_len);
+
 #ifdef __cplusplus
 }
 #endif

@@ -654,6 +654,93 @@ def check_fp8_attention(seed=31):
         assert np.allclose(O3, 2 * O, rtol=1e-12, atol=1e-13) and np.allclose(L3, L_, rtol=1e-12, atol=1e-13)
 
 
+def check_decode_paged_fp8kv(seed=32):
+    """Paged decode over FP8 pools: the code pools scattered over pages in random order (unused
+    pages and page tails hold NaN codes) give what decode() gives over contiguous pools that
+    torch's float8 conversion dequantizes (an independent route), for both formats and with a
+    window; v_scale scales O and leaves the LSE; k_scale acts as a factor on the scores."""
+    import torch
+    rng = _rng(seed)
+    N, Hq, Hkv, d, P = 4, 4, 2, 8, 4
+    lens = np.array([5, 1, 11, 0], np.int32)
+    q = rng.standard_normal((N, Hq, d))
+    for fmt, dt, nan_code in (("e4m3fn", torch.float8_e4m3fn, 0x7F), ("e5m2", torch.float8_e5m2, 0x7F)):
+        kseq = [torch.from_numpy(rng.standard_normal((n, Hkv, d)) * 3).to(dt).view(torch.uint8).numpy() for n in lens]
+        vseq = [torch.from_numpy(rng.standard_normal((n, Hkv, d)) * 3).to(dt).view(torch.uint8).numpy() for n in lens]
+        need = [-(-int(n) // P) for n in lens]
+        n_pages = sum(need) + 3
+        order = rng.permutation(n_pages)
+        kp = np.full((n_pages * P, Hkv, d), nan_code, np.uint8)
+        vp = np.full((n_pages * P, Hkv, d), nan_code, np.uint8)
+        table = np.full((N, max(need)), -1, np.int64)
+        used = 0
+        for s_, n in enumerate(lens):
+            for j in range(need[s_]):
+                page = int(order[used])
+                used += 1
+                table[s_, j] = page
+                lo, hi = j * P, min((j + 1) * P, int(n))
+                kp[page * P:page * P + hi - lo] = kseq[s_][lo:hi]
+                vp[page * P:page * P + hi - lo] = vseq[s_][lo:hi]
+        ks, vs = 0.29, 1.7
+        kc = np.concatenate(kseq) if lens.sum() else np.zeros((0, Hkv, d), np.uint8)
+        vc = np.concatenate(vseq)
+        offs = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+        kt = torch.from_numpy(kc).view(dt).to(torch.float64).numpy() * ks
+        vt = torch.from_numpy(vc).view(dt).to(torch.float64).numpy() * vs
+        for W in (0, 3):
+            O, L = oracle.decode_paged_fp8kv(q, kp, vp, table, lens, P, ks, vs, fmt, scale=0.5, window=W)
+            O2, L2 = oracle.decode(q, kt, vt, offs, lens, scale=0.5, window=W)
+            assert np.allclose(O, O2, rtol=1e-13, atol=1e-13) and np.allclose(L, L2, rtol=1e-13, atol=1e-13), (fmt, W)
+            assert np.all(np.isneginf(L[lens == 0])) and np.all(O[lens == 0] == 0.0)
+        O3, L3 = oracle.decode_paged_fp8kv(q, kp, vp, table, lens, P, ks, 2 * vs, fmt, scale=0.5)
+        O, L = oracle.decode_paged_fp8kv(q, kp, vp, table, lens, P, ks, vs, fmt, scale=0.5)
+        assert np.allclose(O3, 2 * O, rtol=1e-13, atol=1e-13) and np.allclose(L3, L, rtol=1e-13, atol=1e-13)
+        O4, L4 = oracle.decode_paged_fp8kv(q, kp, vp, table, lens, P, 1.0, vs, fmt, scale=0.5 * ks)
+        assert np.allclose(O4, O, rtol=1e-12, atol=1e-13) and np.allclose(L4, L, rtol=1e-12, atol=1e-13)
+
+
+def check_attention_rows(seed=33):
+    """attention_rows() returns, for each requested (b, h, i) in the order given (repeats allowed),
+    row i of head h of batch b of the full result: against attention() on causal, windowed,
+    non-causal, Lq != Lk (rows that see no key included) and GQA/MQA shapes, and against the
+    pure-Python brute force on a tiny shape."""
+    rng = _rng(seed)
+    for (B, Hq, Hkv, Lq, Lk, d) in [(2, 4, 2, 37, 37, 16), (1, 6, 1, 20, 45, 8), (2, 2, 2, 45, 20, 8)]:
+        q = rng.standard_normal((B, Hq, Lq, d))
+        k = rng.standard_normal((B, Hkv, Lk, d))
+        v = rng.standard_normal((B, Hkv, Lk, d))
+        for causal, W in ((False, 0), (True, 0), (True, 7)):
+            O, L = oracle.attention(q, k, v, scale=0.3, causal=causal, window=W)
+            n = 25
+            samples = list(zip(rng.integers(0, B, n).tolist(), rng.integers(0, Hq, n).tolist(),
+                               rng.integers(0, Lq, n).tolist()))
+            samples += [samples[3], (B - 1, Hq - 1, Lq - 1), (0, 0, 0)]
+            Or, Lr = oracle.attention_rows(q, k, v, samples, scale=0.3, causal=causal, window=W)
+            for m, (b, h, i) in enumerate(samples):
+                assert np.max(np.abs(Or[m] - O[b, h, i])) <= 1e-13, (b, h, i, causal, W)
+                if np.isneginf(L[b, h, i]):
+                    assert np.isneginf(Lr[m]), (b, h, i)
+                else:
+                    assert abs(Lr[m] - L[b, h, i]) <= 1e-13, (b, h, i, causal, W)
+    q = rng.standard_normal((1, 4, 9, 3))
+    k = rng.standard_normal((1, 2, 11, 3))
+    v = rng.standard_normal((1, 2, 11, 3))
+    Ob, Lb = brute_force(q, k, v, 0.9, True, 4)
+    samples = [(0, 3, 8), (0, 0, 2), (0, 2, 5), (0, 1, 0), (0, 3, 1)]
+    Or, Lr = oracle.attention_rows(q, k, v, samples, scale=0.9, causal=True, window=4)
+    for m, (b, h, i) in enumerate(samples):
+        assert np.max(np.abs(Or[m] - Ob[b, h, i])) <= 1e-12 and abs(Lr[m] - Lb[b, h, i]) <= 1e-12, (h, i)
+
+
+def check_useful_flops():
+    """4 * d per visible pair per query head: the closed forms L*L*4d*B*Hq without a mask and
+    L(L+1)/2 * 4d * B*Hq under causal masking, and the mask count otherwise."""
+    assert oracle.useful_flops(2, 3, 64, 64, 16, False, 0) == 4 * 16 * 2 * 3 * 64 * 64
+    assert oracle.useful_flops(1, 32, 4096, 4096, 128, True, 0) == 4 * 128 * 32 * 4096 * 4097 // 2
+    assert oracle.useful_flops(1, 2, 9, 30, 8, True, 5) == 4 * 8 * 2 * int(oracle.visibility(9, 30, True, 5).sum())
+
+
 def check_golden():
     """Hand-derived exact values (tests/golden/worked_example.json)."""
     g = json.load(open(GOLDEN))
@@ -691,4 +778,4 @@ ALL_CHECKS = [check_golden, check_brute_force, check_torch_sdpa, check_softmax_r
               check_paged_matches_contiguous, check_paged_brute_force, check_varlen_brute_force,
               check_varlen_chunks, check_backward_autograd, check_backward_finite_differences,
               check_backward_closed_forms, check_visible_pairs, check_fp8_decoders, check_fp8kv_decode,
-              check_fp8_attention]
+              check_fp8_attention, check_decode_paged_fp8kv, check_attention_rows, check_useful_flops]

@@ -479,3 +479,27 @@ def test_schedule_bands_heads_by_xcd():
         assert heads == set(range(x * band, (x + 1) * band))
         kv = {(bh // Hq, (bh % Hq) // (Hq // Hkv)) for bh in heads}
         assert len(kv) == band // (Hq // Hkv)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (32, 1), (8, 2), (4, 4), (48, 1), (40, 1), (64, 1), (40, 8), (96, 2),
+                                    (33, 1), (5, 5), (64, 64)])
+def test_decode_rows_read_only_their_own_heads(Hq, Hkv):
+    """Every query head is served by exactly one row, a row's heads all share its KV head (or, in
+    the packed layout, one row serves every head), and so the q rows a worker reads,
+    s * Hq + first + col for col < n_heads, never leave sequence s's Hq rows: for the last
+    sequence they stay inside q (a group of 48 heads over one KV head takes a block of 32 and a
+    block of 16)."""
+    rows = af.decode_rows(Hq, Hkv)
+    g = Hq // Hkv
+    packed = Hq <= 32 and 32 % Hkv == 0
+    seen = np.zeros(Hq, np.int64)
+    for kvh, first, nh in rows.tolist():
+        assert 1 <= nh <= (Hq if packed else 32)
+        assert 0 <= first and first + nh <= Hq
+        if not packed:
+            assert first // g == kvh and (first + nh - 1) // g == kvh
+        seen[first:first + nh] += 1
+    assert np.all(seen == 1)
+    n_seq = 3
+    last_row_read = (n_seq - 1) * Hq + max(f + n - 1 for _, f, n in rows.tolist())
+    assert last_row_read < n_seq * Hq

@@ -115,6 +115,26 @@ def _key_grads_unscaled(dS, P, q, dO, scale):
     return dS.T @ q, P.T @ dO
 
 
+def _rows_reversed(q, k, v, samples, scale=None, causal=False, window=0, threads=None):
+    # the rows come back in the reverse of the requested order
+    O, L = _orig_rows(q, k, v, samples, scale=scale, causal=causal, window=window, threads=threads)
+    return O[::-1].copy(), L[::-1].copy()
+
+
+def _rows_offset_dropped(q, k, v, samples, scale=None, causal=False, window=0, threads=None):
+    # the requested row index ignored: the n-th sample computes row n of its head
+    samples = [(b, h, min(n, np.asarray(q).shape[2] - 1)) for n, (b, h, _) in enumerate(samples)]
+    return _orig_rows(q, k, v, samples, scale=scale, causal=causal, window=window, threads=threads)
+
+
+def _rows_mask_dropped(q, k, v, samples, scale=None, causal=False, window=0, threads=None):
+    # the causal mask (and window) not applied to sampled rows
+    return _orig_rows(q, k, v, samples, scale=scale, causal=False, window=0, threads=threads)
+
+
+_orig_rows = mod.attention_rows
+
+
 MUTANTS = {
     "gqa_interleaved": ("kv_head", _interleaved_kv_head),
     "window_off_by_one": ("_visibility_rows", _window_one_too_wide),
@@ -131,6 +151,9 @@ MUTANTS = {
     "varlen_offsets_ignored": ("_seq_rows", _seq_rows_from_zero),
     "backward_no_rowsum": ("_softmax_backward", _softmax_backward_no_rowsum),
     "backward_dk_unscaled": ("_key_grads", _key_grads_unscaled),
+    "rows_order_reversed": ("attention_rows", _rows_reversed),
+    "rows_offset_dropped": ("attention_rows", _rows_offset_dropped),
+    "rows_mask_dropped": ("attention_rows", _rows_mask_dropped),
 }
 
 
@@ -194,12 +217,25 @@ def _fp8_attention_v_unscaled(q_codes, k_codes, v_codes, q_scale, k_scale, v_sca
                             fp8mod.dequantize(v_codes, 1.0, fmt), **kw)
 
 
+def _paged_fp8kv_scales_swapped(q, k_codes, v_codes, block_table, lens, page_size, k_scale, v_scale, fmt, **kw):
+    return fp8mod.decode_paged(q, fp8mod.dequantize(k_codes, v_scale, fmt), fp8mod.dequantize(v_codes, k_scale, fmt),
+                               block_table, lens, page_size, **kw)
+
+
+def _paged_fp8kv_as_e4m3(q, k_codes, v_codes, block_table, lens, page_size, k_scale, v_scale, fmt, **kw):
+    # the format argument ignored
+    return fp8mod.decode_paged(q, fp8mod.dequantize(k_codes, k_scale, "e4m3fn"),
+                               fp8mod.dequantize(v_codes, v_scale, "e4m3fn"), block_table, lens, page_size, **kw)
+
+
 FP8_MUTANTS = {
     "fp8_attention_v_scale_dropped": ("attention_fp8", _fp8_attention_v_unscaled),
     "e4m3_bias_8": ("decode_e4m3fn", _e4m3_bias8),
     "e4m3_subnormals_flushed": ("decode_e4m3fn", _e4m3_flush_subnormals),
     "e5m2_read_as_e4m3": ("decode_e5m2", fp8mod.decode_e4m3fn),
     "fp8kv_scales_swapped": ("decode_fp8kv", _fp8kv_scales_swapped),
+    "paged_fp8kv_scales_swapped": ("decode_paged_fp8kv", _paged_fp8kv_scales_swapped),
+    "paged_fp8kv_format_ignored": ("decode_paged_fp8kv", _paged_fp8kv_as_e4m3),
 }
 
 
