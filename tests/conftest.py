@@ -27,3 +27,19 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """One line per named workload with the errors its parity test measured (max abs error and
+    relative RMS of O over the whole output, largest LSE error), so a quiet run still shows them."""
+    try:
+        import parity
+    except ImportError:  # pragma: no cover
+        return
+    if not parity.SUMMARY:
+        return
+    tr = terminalreporter
+    tr.section("parity against the fp64 oracle (whole outputs)")
+    for name, st in parity.SUMMARY:
+        parts = [f"{k} {v:.3g}" if isinstance(v, float) else f"{k} {v}" for k, v in st.items()]
+        tr.write_line(f"{name}: " + ", ".join(parts))

@@ -1,18 +1,20 @@
 """Parity bar between the HIP path and the fp64 oracle.
 
-Tolerances: fp32 inputs, max |O - O_ref| <= 1e-5; bf16 inputs, max |O - O_ref| <= 2e-2 and
-relative RMS ||O - O_ref|| / ||O_ref|| <= 5e-3.  The LSE bound is derived from the arithmetic:
-scores are products summed in fp32, whose rounding error grows with the operands' magnitude;
-for a peaked row LSE is close to the largest score, so the error scales with |LSE|.  The row
-sum adds fp32 probabilities and exp2/log2 are within one ulp.  The bar is
-|LSE - LSE_ref| <= tau * max(1, |LSE_ref|) with tau = 1e-4 for bf16 inputs and 1e-5 for fp32
-inputs.  Rows that see no key must be exactly O = 0 and LSE = -inf.
+Tolerances on O: fp32 inputs, max |O - O_ref| <= 1e-5; bf16 inputs, max |O - O_ref| <= 2e-2 and
+relative RMS ||O - O_ref|| / ||O_ref|| <= 5e-3.
 
-The bounds are stated for the specified workloads, whose scores have unit variance
-(scale = 1/sqrt(d), N(0, 1) inputs).  Rounding error in fp32 scores is proportional to their
-magnitude, so a stress test that multiplies the scores by a factor f passes ``magnitude=f`` and
-the O bound grows by f (the bf16 bounds are dominated by the bf16 rounding of P and O and do
-not change).
+LSE (the pages fix no bar for it): |LSE - LSE_ref| <= 1e-4 for bf16 inputs and 1e-5 for fp32
+inputs, absolute.  The scores are exact products of the inputs summed in fp32 and the row sum
+adds fp32 probabilities, so on the specified workloads (scale = 1/sqrt(d), N(0, 1) inputs, unit
+variance scores, |LSE| below about 16) the fp32 rounding stays near 1e-6.  Rows that see no key
+must be exactly O = 0 and LSE = -inf.
+
+Stress tests outside the specified workloads multiply the scores by a factor f (a scale of 2,
+inputs times 30): fp32 rounding of a score grows with its magnitude, and LSE is close to the
+row's largest score, so such a test passes ``magnitude=f`` and ``lse_relative=True``.  Then the
+fp32 O bound is multiplied by max(1, f) and the LSE bound becomes tau * max(1, |LSE_ref|) (the bf16
+O bounds are dominated by the bf16 rounding of P and O and do not change).  The named workloads
+never use this relaxation.
 
 Gradients (attn_bwd, bf16) have no specified bar; it is derived the same way.  The inputs are
 exact in both paths; the GPU rounds P and dS = P (dP - D) to bf16 before the products that use
@@ -38,16 +40,32 @@ def say(*args):
     sys.stdout.flush()
 
 
-# FP8 inputs (attn_fwd_fp8): v_mfma_f32_32x32x64_f8f6f4 adds its 64 exact products with about 13
-# bits of precision, not fp32's 24: over 65,536 outputs of full-range random E4M3 codes the error was
-# at most 1.05e-4 of the sum of |products| (about 2^-13).  A score therefore carries up to
-# FP8_MFMA_EPS * |scale| * sum_i |q_i k_i| of error (bound taken at twice the largest measured), and
-# so may the LSE; check() takes that per row as ``lse_abs_extra``.  O is not affected beyond the
-# bf16 bar (the score error stays below the bf16 rounding of P).
+# Errors measured on the named workloads, printed by tests/conftest.py at the end of a run.
+SUMMARY: list = []
+
+
+def record(name: str, stats: dict) -> dict:
+    """Keep the measured errors of a named workload for the end-of-run summary; returns them."""
+    SUMMARY.append((name, dict(stats)))
+    say(name, stats)
+    return stats
+
+
+# FP8 inputs (attn_fwd_fp8): S = Q K^T runs on v_mfma_f32_32x32x64_f8f6f4, which adds its 64
+# products with fewer bits than fp32 carries.  A score may therefore be off by up to
+# FP8_MFMA_EPS * |scale| * sum_i |q_i k_i|, and so may the LSE; check() adds that per row
+# (``lse_abs_extra``) to the LSE bar and reports the raw LSE error beside it.  The bound is
+# measured, not assumed: tests/test_fp8_gpu.py::test_fp8_score_accumulation_error reads single
+# scores back through the LSE of one-key rows over full-range random codes and requires every
+# error to stay within it.  O is not affected beyond the bf16 bar (the score error stays below
+# the bf16 rounding of P).
 FP8_MFMA_EPS = 2.0 ** -12
 
 
-def check(o, o_ref, lse, lse_ref, dtype: str, label: str = "", magnitude: float = 1.0, lse_abs_extra=None):
+def check(o, o_ref, lse, lse_ref, dtype: str, label: str = "", magnitude: float = 1.0, lse_relative: bool = False,
+          lse_abs_extra=None):
+    """O and LSE against the oracle; returns the measured errors (max_abs, rel_rms, lse_err, and
+    lse_bound_used when an FP8 allowance applies)."""
     o = np.asarray(o, np.float64)
     o_ref = np.asarray(o_ref, np.float64)
     assert o.shape == o_ref.shape, (label, o.shape, o_ref.shape)
@@ -61,12 +79,17 @@ def check(o, o_ref, lse, lse_ref, dtype: str, label: str = "", magnitude: float 
             fin = ~empty
             assert np.all(np.isfinite(lse[fin])), (label, "non-finite LSE")
             diff = np.abs(lse[fin] - lse_ref[fin])
+            bound = np.full(diff.shape, LSE_TOL[dtype])
+            if lse_relative:
+                bound = bound * np.maximum(1.0, np.abs(lse_ref[fin]))
             if lse_abs_extra is not None:
-                diff = np.maximum(0.0, diff - np.broadcast_to(np.asarray(lse_abs_extra, np.float64), lse.shape)[fin])
-            rel = diff / np.maximum(1.0, np.abs(lse_ref[fin]))
-            lerr = float(np.max(rel, initial=0.0))
-            stats["lse_err"] = lerr
-            assert lerr <= LSE_TOL[dtype], (label, "LSE error (relative to max(1, |LSE|))", lerr)
+                extra = np.broadcast_to(np.asarray(lse_abs_extra, np.float64), lse.shape)[fin]
+                bound = bound + extra
+                stats["lse_bound_max"] = float(np.max(bound, initial=0.0))
+            stats["lse_err"] = float(np.max(diff, initial=0.0))
+            worst = int(np.argmax(diff - bound)) if diff.size else 0
+            assert diff.size == 0 or diff[worst] <= bound[worst], (label, "LSE error", float(diff[worst]),
+                                                                   "bound", float(bound[worst]))
         assert np.all(o[empty] == 0.0), (label, "rows that see no key need O = 0")
     assert np.all(np.isfinite(o)), (label, "non-finite output")
     err = float(np.max(np.abs(o - o_ref), initial=0.0))

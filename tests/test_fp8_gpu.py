@@ -13,7 +13,7 @@ import torch
 import attention_attn_fwd_03_amd as af
 import oracle
 import workloads as wl
-from parity import FP8_MFMA_EPS, check, say
+from parity import FP8_MFMA_EPS, check, record, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -107,23 +107,23 @@ def test_fp8_equals_bf16_path_with_power_of_two_scales(fmt, Hkv):
     assert torch.equal(o8.view(torch.int16), o.view(torch.int16)) and torch.equal(l8, lse)
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("name", ["gqa_decode_bf16", "mqa_decode_bf16"])
 def test_fp8_named_decode(fmt, name):
     """The full decode batch (64 sequences, lengths 1k..32k, NaN codes in the pool's gaps) with an
-    FP8 cache: every output finite, 16+ sequences against the oracle."""
+    FP8 cache: every sequence against the oracle."""
     c = wl.DECODE[name]
     lens = wl.decode_lens(c.n_seq, c.len_lo, c.len_hi, c.lens_seed)
     say(f"fp8 decode {fmt} {name} full size on device")
     q, kc, vc, offs, lens_t, layout, ks, vs = wl.fp8_decode_inputs(c.n_seq, c.Hq, c.Hkv, c.d, lens, fmt,
                                                                    seed=c.value_seed, device=DEV, max_gap=c.max_gap)
     o, lse = run(q, kc, vc, offs, lens_t, int(lens.max()), 0, c.scale, fmt, ks, vs)
-    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
-    seqs = sorted(set(np.random.default_rng(c.value_seed).choice(c.n_seq, 16, replace=False).tolist())
-                  | {int(np.argmax(lens)), int(np.argmin(lens))})
+    seqs = list(range(c.n_seq))
     kg, vg, po, pl = gather_codes(kc, vc, layout.offsets, layout.lens, seqs)
     O_ref, L_ref = oracle.decode_fp8kv(wl.to_f64(q)[seqs], kg, vg, po, pl, ks, vs, fmt, scale=c.scale)
-    say(name, fmt, check(wl.to_f64(o)[seqs], O_ref, lse.cpu().numpy()[seqs], L_ref, "bf16", name + " " + fmt))
+    record(name.replace("_bf16", f"_fp8_{fmt}"), check(wl.to_f64(o)[seqs], O_ref, lse.cpu().numpy()[seqs], L_ref,
+                                                         "bf16", name + " " + fmt))
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -257,35 +257,67 @@ def test_fp8_fwd_scales(fmt, scale, mult):
     fp8_fwd_case(1, 4, 2, 300, 300, 128, True, 0, fmt, seed=11, scale=scale, scale_mult=mult)
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("name", ["gqa_causal_bf16_L4096", "swa_gqa_bf16_L16384_W4096"])
-def test_fp8_fwd_named_workload_sampled(fmt, name):
+def test_fp8_fwd_named_workload_full_size(fmt, name):
     """The causal GQA L4096 workload (B2 Hq32 Hkv8 d128) and the window workload (L16384, W4096)
-    with FP8 inputs, full-size launch, checked on sampled rows of every head; every output finite."""
+    with FP8 inputs, full-size launch, against the oracle over the whole output."""
     c = wl.PREFILL[name]
     say(f"fp8 fwd {fmt} {name} full size on device")
     qc, kc, vc, qs, ks, vs = wl.fp8_prefill_inputs(c.B, c.Hq, c.Hkv, c.Lq, c.Lk, c.d, fmt, seed=c.seed, device=DEV)
     o, lse = af.attn_fwd_fp8(qc, kc, vc, qkv_format=fmt, q_scale=qs, k_scale=ks, v_scale=vs, causal=True,
                              window=c.window, scale=c.scale, return_lse=True)
     torch.cuda.synchronize()
-    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
-    rng = np.random.default_rng(c.seed)
-    fixed = [0, 1, 63, 64, 127, 128, 129, c.Lq // 2, c.Lq - 129, c.Lq - 2, c.Lq - 1]
-    rows = sorted(set(fixed) | set(rng.integers(0, c.Lq, 4).tolist()))
-    samples = [(b, h, i) for b in range(c.B) for h in range(c.Hq) for i in rows]
+    og, lg = wl.to_f64(o), lse.cpu().numpy()
+    del o, lse
     qd, kd, vd = (oracle.dequantize(x.cpu().numpy(), s_, fmt) for x, s_ in ((qc, qs), (kc, ks), (vc, vs)))
-    O_ref, L_ref = oracle.attention_rows(qd, kd, vd, samples, scale=c.scale, causal=True, window=c.window)
-    idx = tuple(np.array(samples).T)
-    extra = fp8_lse_allowance(qd, kd, c.scale, rows=samples)
-    say(fmt, check(wl.to_f64(o)[idx], O_ref, lse.cpu().numpy().astype(np.float64)[idx], L_ref, "bf16", f"fp8 {name}",
-                   lse_abs_extra=extra))
+    O_ref, L_ref = oracle.attention(qd, kd, vd, scale=c.scale, causal=True, window=c.window)
+    extra = fp8_lse_allowance(qd, kd, c.scale)
+    record(name.replace("_bf16_", f"_fp8_{fmt}_"), check(og, O_ref, lg, L_ref, "bf16", f"fp8 {name}",
+                                                          lse_abs_extra=extra))
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_score_accumulation_error(fmt, d):
+    """Measures the bound the FP8 LSE bar rests on.  With one key per row (Lk = 1, no mask) the
+    row's probability is exactly 1, so its LSE is the score itself, scale * q . k, read back
+    through fp32 (a few ulps).  Over 32768 scores of uniformly random finite codes (the full range
+    of the format, both signs) the error of each must stay within FP8_MFMA_EPS * |scale| *
+    sum_i |q_i k_i|; the largest measured ratio is printed."""
+    rng = np.random.default_rng(77 + d)
+    B, H, Lq = 2, 16, 1024
+    codes = np.arange(256, dtype=np.uint8)
+    vals = oracle.dequantize(codes, 1.0, fmt)
+    finite = codes[np.isfinite(vals)]
+    qc = rng.choice(finite, size=(B, H, Lq, d)).astype(np.uint8)
+    kc = rng.choice(finite, size=(B, H, 1, d)).astype(np.uint8)
+    vc = rng.choice(finite, size=(B, H, 1, d)).astype(np.uint8)
+    qd, kd = oracle.dequantize(qc, 1.0, fmt), oracle.dequantize(kc, 1.0, fmt)
+    scale = 1.0 / math.sqrt(d)
+    _, lse = af.attn_fwd_fp8(torch.from_numpy(qc).to(DEV), torch.from_numpy(kc).to(DEV), torch.from_numpy(vc).to(DEV),
+                             qkv_format=fmt, q_scale=1.0, k_scale=1.0, v_scale=1.0, causal=False, scale=scale,
+                             return_lse=True)
+    torch.cuda.synchronize()
+    exact = scale * np.einsum("bhid,bhd->bhi", qd, kd[:, :, 0])
+    mag = abs(scale) * np.einsum("bhid,bhd->bhi", np.abs(qd), np.abs(kd[:, :, 0]))
+    err = np.abs(lse.cpu().numpy().astype(np.float64) - exact)
+    # what fp32 itself costs: the fold of the scale into log2(e) units and back (a few ulps)
+    fp32_part = 8 * np.finfo(np.float32).eps * np.abs(exact)
+    ratio = np.maximum(err - fp32_part, 0.0) / np.maximum(mag, 1e-30)
+    record(f"fp8_{fmt}_score_accumulation_d{d}",
+           {"max_err_over_abs_sum": float(ratio.max()), "bound": FP8_MFMA_EPS, "scores": int(ratio.size)})
+    assert np.all(np.isfinite(lse.cpu().numpy()))
+    assert ratio.max() <= FP8_MFMA_EPS
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("name", ["gqa_decode_bf16", "mqa_decode_bf16"])
 def test_fp8_named_decode_paged(fmt, name):
     """The full decode batch with an FP8 cache in 64-token pages scattered over the pool (spare
-    pages and page tails NaN codes): every output finite, 16+ sequences against the oracle."""
+    pages and page tails NaN codes): every sequence against the oracle."""
     c = wl.DECODE[name]
     P = 64
     lens = wl.decode_lens(c.n_seq, c.len_lo, c.len_hi, c.lens_seed)
@@ -295,9 +327,7 @@ def test_fp8_named_decode_paged(fmt, name):
     o, lse = af.attn_decode_paged(q, kc, vc, table, lens_t, page_size=P, max_len=int(lens.max()), scale=c.scale,
                                   return_lse=True, kv_format=fmt, k_scale=ks, v_scale=vs)
     torch.cuda.synchronize()
-    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
-    seqs = sorted(set(np.random.default_rng(c.value_seed).choice(c.n_seq, 16, replace=False).tolist())
-                  | {int(np.argmax(lens)), int(np.argmin(lens))})
+    seqs = list(range(c.n_seq))
     tab = layout.table
     used = sorted({int(tab[s_, j]) for s_ in seqs for j in range(-(-int(lens[s_]) // P))})
     new_id = {p_: i for i, p_ in enumerate(used)}
@@ -309,4 +339,5 @@ def test_fp8_named_decode_paged(fmt, name):
             sub[i, j] = new_id[int(tab[s_, j])]
     O_ref, L_ref = oracle.decode_paged_fp8kv(wl.to_f64(q)[seqs], kcomp, vcomp, sub, lens[seqs], P, ks, vs, fmt,
                                              scale=c.scale)
-    say(name, fmt, check(wl.to_f64(o)[seqs], O_ref, lse.cpu().numpy()[seqs], L_ref, "bf16", f"{name} {fmt} paged"))
+    record(name.replace("_bf16", f"_fp8_{fmt}") + "_paged_P64",
+           check(wl.to_f64(o)[seqs], O_ref, lse.cpu().numpy()[seqs], L_ref, "bf16", f"{name} {fmt} paged"))

@@ -1,10 +1,10 @@
 """HIP path vs the fp64 oracle, element by element, through the C ABI (Python binding).
 
 Inputs are seeded N(0, 1) draws from workloads.py; the oracle sees the same bf16/fp32 values
-upcast exactly to fp64.  Full-size workloads are checked on sampled rows (every head, rows at
-tile edges plus random ones) with the launch configuration the benchmark times; small shapes are
-checked in full.  Outputs are pre-filled with NaN so that any row the kernel fails to write
-fails the test."""
+upcast exactly to fp64.  Every named workload is compared in full (every output element and
+every LSE) with the launch configuration the benchmark times, and its max abs error, relative
+RMS and LSE error are printed.  Outputs are pre-filled with NaN so that any row the kernel fails
+to write fails the test."""
 import math
 
 import numpy as np
@@ -14,7 +14,7 @@ import torch
 import attention_attn_fwd_03_amd as af
 import oracle
 import workloads as wl
-from parity import check, say
+from parity import check, record, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -42,7 +42,9 @@ def full_case(B, Hq, Hkv, Lq, Lk, d, causal, window, dtype, seed, scale=None):
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     o, lse = run_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal, window, scale)
     O_ref, L_ref = oracle.attention(to64(q), to64(k), to64(v), scale=scale, causal=causal, window=window)
-    return check(to64(o), O_ref, lse.cpu().numpy(), L_ref, dtype, label, magnitude=abs(scale) * math.sqrt(d))
+    magnitude = abs(scale) * math.sqrt(d)
+    return check(to64(o), O_ref, lse.cpu().numpy(), L_ref, dtype, label, magnitude=magnitude,
+                 lse_relative=magnitude > 1.0)
 
 
 # ---------------------------------------------------------------------------------------------
@@ -51,34 +53,22 @@ def full_case(B, Hq, Hkv, Lq, Lk, d, causal, window, dtype, seed, scale=None):
 @pytest.mark.parametrize("name", ["mha_f32_L128", "mha_f32_L128_causal", "mha_bf16_L1024"])
 def test_named_workload_full(name):
     c = wl.PREFILL[name]
-    full_case(c.B, c.Hq, c.Hkv, c.Lq, c.Lk, c.d, c.causal, c.window, c.dtype, c.seed)
+    record(name, full_case(c.B, c.Hq, c.Hkv, c.Lq, c.Lk, c.d, c.causal, c.window, c.dtype, c.seed))
 
 
-def sample_rows(Lq, rng, n_random=6):
-    fixed = [0, 1, 63, 64, 127, 128, 129, Lq // 2, Lq - 129, Lq - 128, Lq - 2, Lq - 1]
-    rows = sorted({r for r in fixed if 0 <= r < Lq} | set(rng.integers(0, Lq, n_random).tolist()))
-    return rows
-
-
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["gqa_causal_bf16_L4096", "swa_gqa_bf16_L16384_W4096"])
-def test_named_workload_sampled(name):
-    """Full-size launch (the configuration the benchmark times), checked on sampled rows of
-    every head against the oracle, and every output finite."""
+def test_named_workload_full_size(name):
+    """The full-size launch (the configuration the benchmark times) against the oracle over the
+    whole output: every element of O and every LSE."""
     c = wl.PREFILL[name]
     say(f"fwd {name} full size on device")
     q, k, v = wl.prefill_inputs_for(c, device=DEV)
     o, lse = run_fwd(q, k, v, c.causal, c.window, c.scale)
-    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
-    rng = np.random.default_rng(c.seed)
-    samples = [(b, h, i) for b in range(c.B) for h in range(c.Hq) for i in sample_rows(c.Lq, rng)]
-    qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
-    O_ref, L_ref = oracle.attention_rows(qh.float().numpy(), kh.float().numpy(), vh.float().numpy(), samples,
-                                         scale=c.scale, causal=c.causal, window=c.window)
-    idx = tuple(np.array(samples).T)
-    og = to64(o)[idx]
-    lg = lse.cpu().numpy().astype(np.float64)[idx]
-    stats = check(og, O_ref, lg, L_ref, "bf16", name)
-    say(name, stats)
+    og, lg = to64(o), lse.cpu().numpy()
+    del o, lse
+    O_ref, L_ref = oracle.attention(to64(q), to64(k), to64(v), scale=c.scale, causal=c.causal, window=c.window)
+    record(name, check(og, O_ref, lg, L_ref, "bf16", name))
 
 
 # ---------------------------------------------------------------------------------------------
@@ -147,7 +137,7 @@ def test_large_values_and_nan_propagation():
     q = q * 30  # scores up to a few hundred: exercises the rescale path
     o, lse = run_fwd(q.to(DEV), k.to(DEV), v.to(DEV), True, 0, 0.125)
     O_ref, L_ref = oracle.attention(to64(q), to64(k), to64(v), scale=0.125, causal=True)
-    check(to64(o), O_ref, lse.cpu().numpy(), L_ref, "f32", "large scores", magnitude=30.0)
+    check(to64(o), O_ref, lse.cpu().numpy(), L_ref, "f32", "large scores", magnitude=30.0, lse_relative=True)
     k2 = k.clone()
     k2[0, 0, 5, 3] = float("nan")
     o, _ = run_fwd(q.to(DEV), k2.to(DEV), v.to(DEV), True, 0, 0.125)
@@ -321,22 +311,20 @@ def decode_case(lens, Hq, Hkv, d, window=0, seed=0, scale=None, max_len=None, de
     return check(to64(o)[seqs], O_ref, lse.cpu().numpy()[seqs], L_ref, "bf16", label)
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["gqa_decode_bf16", "mqa_decode_bf16"])
 def test_named_decode(name):
-    """Full-size decode batch (64 sequences, lengths 1k..32k, NaN-poisoned gaps in the pool);
-    the oracle checks 16 of the sequences, every output is finite."""
+    """Full-size decode batch (64 sequences, lengths 1k..32k, NaN-poisoned gaps in the pool)
+    against the oracle: every sequence, every query head, every element."""
     c = wl.DECODE[name]
     lens = wl.decode_lens(c.n_seq, c.len_lo, c.len_hi, c.lens_seed)
     say(f"decode {name} full size on device")
     q, kp, vp, offs, lens_t, layout = wl.decode_inputs(c.n_seq, c.Hq, c.Hkv, c.d, lens, seed=c.value_seed,
                                                        device=DEV, max_gap=c.max_gap)
     o, lse = run_decode(q, kp, vp, offs, lens_t, int(lens.max()), 0, c.scale)
-    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
-    seqs = sorted(set(np.random.default_rng(c.value_seed).choice(c.n_seq, 16, replace=False).tolist())
-                  | {int(np.argmax(lens)), int(np.argmin(lens))})
+    seqs = list(range(c.n_seq))
     O_ref, L_ref = oracle_decode(q, kp, vp, layout.offsets, layout.lens, seqs, c.scale)
-    stats = check(to64(o)[seqs], O_ref, lse.cpu().numpy()[seqs], L_ref, "bf16", name)
-    say(name, stats)
+    record(name, check(to64(o), O_ref, lse.cpu().numpy(), L_ref, "bf16", name))
 
 
 def edge_lens(n_seq, share_blocks):
@@ -466,12 +454,12 @@ def decode_paged_case(lens, Hq, Hkv, d, page_size, window=0, seed=0, scale=None,
     return check(to64(o)[seqs], O_ref, lse.cpu().numpy()[seqs], L_ref, "bf16", label)
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["gqa_decode_bf16", "mqa_decode_bf16"])
 def test_named_decode_paged(name):
     """The full decode batch with its cache in 64-token pages scattered over the pool (unused
-    pages and page tails NaN): every output finite, 16+ sequences against the oracle, and the
-    result bit-identical to the contiguous entry point on the same keys (same split, same
-    arithmetic)."""
+    pages and page tails NaN): every sequence against the oracle, and the result bit-identical
+    to the contiguous entry point on the same keys (same split, same arithmetic)."""
     c = wl.DECODE[name]
     P = 64
     lens = wl.decode_lens(c.n_seq, c.len_lo, c.len_hi, c.lens_seed)
@@ -479,12 +467,9 @@ def test_named_decode_paged(name):
     q, kp, vp, table, lens_t, layout = wl.paged_decode_inputs(c.n_seq, c.Hq, c.Hkv, c.d, lens, P, seed=c.value_seed,
                                                               device=DEV, extra_pages=97)
     o, lse = run_decode_paged(q, kp, vp, table, lens_t, P, int(lens.max()), 0, c.scale)
-    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
-    seqs = sorted(set(np.random.default_rng(c.value_seed).choice(c.n_seq, 16, replace=False).tolist())
-                  | {int(np.argmax(lens)), int(np.argmin(lens))})
+    seqs = list(range(c.n_seq))
     O_ref, L_ref = oracle_decode_paged(q, kp, vp, layout.table, layout.lens, P, seqs, c.scale)
-    stats = check(to64(o)[seqs], O_ref, lse.cpu().numpy()[seqs], L_ref, "bf16", name + " paged")
-    say(name, "paged", stats)
+    record(name + "_paged_P64", check(to64(o)[seqs], O_ref, lse.cpu().numpy()[seqs], L_ref, "bf16", name + " paged"))
     # the same keys laid out contiguously, through attn_decode
     rows = np.concatenate([(layout.table[s, :-(-int(n) // P)].astype(np.int64)[:, None] * P
                             + np.arange(P)[None, :]).ravel()[:int(n)] for s, n in enumerate(lens)])
