@@ -21,7 +21,7 @@ KV_FORMATS = {"e4m3fn": 1, "e5m2": 2}  # attn_kv_format
 EXPORTS = ["attn_fwd", "attn_fwd_f32", "attn_fwd_varlen", "attn_decode_workspace_size", "attn_decode",
            "attn_decode_paged", "attn_status_str", "attn_fwd_plan", "attn_fwd_schedule", "attn_fwd_varlen_schedule",
            "attn_decode_plan", "attn_bwd_workspace_size", "attn_bwd", "attn_decode_fp8", "attn_decode_paged_fp8",
-           "attn_fwd_fp8", "attn_decode_rows"]
+           "attn_fwd_fp8", "attn_decode_rows", "attn_probe_mfma_ceiling"]
 
 
 class FwdPlanInfo(ctypes.Structure):
@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_workspace_size.restype = sz
     L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, i32, f32, vp, sz, vp]
     L.attn_decode.restype = i32
+    L.attn_probe_mfma_ceiling.argtypes = [i32, i32, vp, sz, vp]
+    L.attn_probe_mfma_ceiling.restype = i32
     L.attn_decode_paged.argtypes = [vp, vp, vp, vp, i32, i32, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                                     vp, sz, vp]
     L.attn_decode_paged.restype = i32
@@ -358,6 +360,16 @@ def attn_decode_paged(q, k_pool, v_pool, block_table, lens, *, page_size: int, m
     else:
         _run(dev, lib().attn_decode_paged_fp8, *args, fmt, float(k_scale), float(v_scale), *tail)
     return (o, lse) if return_lse else o
+
+
+def probe_mfma_ceiling(workgroups: int, steps: int, sink) -> None:
+    """Enqueue the matrix-core ceiling probe (include/attn_probe.h) on the current stream of the
+    sink's GPU; ``sink`` is a float32 device tensor of at least workgroups * 256 elements."""
+    import torch
+    dev = _require_gpu(sink)
+    if sink.dtype != torch.float32:
+        raise ValueError("sink must be float32")
+    _run(dev, lib().attn_probe_mfma_ceiling, int(workgroups), int(steps), sink.data_ptr(), sink.numel() * 4)
 
 
 def fwd_plan(B, Hq, Hkv, Lq, Lk, d, causal=False, window=0, f32=False) -> dict:

@@ -141,9 +141,11 @@ __device__ __forceinline__ void stage_offsets(unsigned (&voff)[N], int lane, int
   }
 }
 
-// PAGED selects the pool addressing and KV the pool's element format at compile time, so the
-// contiguous bf16 kernel carries none of the page-table or conversion code.
-template <int D, bool PAGED, int KV>
+// PAGED selects the pool addressing, KV the pool's element format and PACKED the block layout
+// (all Hkv heads of 32 / Hkv tokens, or 32 tokens of one head) at compile time, so the contiguous
+// bf16 kernel carries none of the page-table or conversion code, and the one-head layout (MQA,
+// large groups) none of the packed layout's masking.
+template <int D, bool PAGED, int KV, bool PACKED>
 // At d = 128 the two LDS stages (38 KB) allow four waves per CU, one per SIMD, so the wave may use
 // the whole register file; at d = 64 two waves per SIMD fit.
 __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecArgs a) {
@@ -156,7 +158,8 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
 
   const int lane = threadIdx.x, h = lane >> 5, col = lane & 31;
   const int team = blockIdx.x / a.rows, u = blockIdx.x % a.rows;
-  const int pack = a.pack, tpb = a.tpb, pack_log2 = __builtin_ctz((unsigned)a.pack);
+  const int pack = PACKED ? a.pack : 1, tpb = PACKED ? a.tpb : kDecodeBlockRows;
+  const int pack_log2 = PACKED ? __builtin_ctz((unsigned)a.pack) : 0;
   const int kvh0 = decode_row_kv_head(a.Hq, a.Hkv, u);      // KV head of block row 0
   const int qbase = decode_row_first_head(a.Hq, a.Hkv, u);  // query head of column 0
   const bool writer = blockIdx.x == 0;  // publishes the share and the prefix for the merge pass
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
   // S^T register i of this lane holds block row r(i) = 8*(i/4) + 4*h + i%4 against query head
   // qbase + col.  In the packed layout only rows of the head's own KV group count.
   unsigned head_ok = 0xFFFFu;
-  if (pack > 1) {
+  if constexpr (PACKED) {
     head_ok = 0u;
     const int g = col / a.group;
 #pragma unroll
@@ -366,7 +369,7 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
           const bool ok = ((head_ok >> i) & 1u) && tok < t_end && (!PAGED || tok >= vis_lo);
           sv[0][i] = ok ? sv[0][i] : -INFINITY;
         }
-      } else if (pack > 1) {  // rows of other KV groups
+      } else if constexpr (PACKED) {  // rows of other KV groups
 #pragma unroll
         for (int i = 0; i < 16; ++i) sv[0][i] = ((head_ok >> i) & 1u) ? sv[0][i] : -INFINITY;
       }
@@ -450,7 +453,7 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
 // D/64 output columns over the pieces, the piece weight broadcast from the lane that holds it.
 // The partial O rows are fetched MB pieces at a time, all loads of a batch issued before any of
 // them is used, so a sequence with few pieces costs about two memory round trips.
-template <int D>
+template <int D, bool PACKED>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
   constexpr int PER = D / 64;
   constexpr int MB = 16;
@@ -471,8 +474,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
   const int kvh = hq / a.group, within = hq % a.group;
   // Slot row and column of this query head: one row holding every head in the packed layout,
   // else row (KV head, block of 32 heads).
-  const int u = a.pack > 1 ? 0 : kvh * a.hblocks + within / 32;
-  const int col = a.pack > 1 ? hq : within % 32;
+  const int u = PACKED ? 0 : kvh * a.hblocks + within / 32;
+  const int col = PACKED ? hq : within % 32;
 
   float M = -INFINITY, L = 0.f;
   bool bad = false;  // a piece read a page entry outside the pool (its m is NaN)
@@ -542,20 +545,23 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
     a.lse[(size_t)s * a.Hq + hq] = bad ? NAN : L > 0.f ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
 }
 
-template __global__ void decode_split_kernel<64, false, kKvBf16>(DecArgs);
-template __global__ void decode_split_kernel<128, false, kKvBf16>(DecArgs);
-template __global__ void decode_split_kernel<64, true, kKvBf16>(DecArgs);
-template __global__ void decode_split_kernel<128, true, kKvBf16>(DecArgs);
-template __global__ void decode_split_kernel<64, false, kKvE4M3>(DecArgs);
-template __global__ void decode_split_kernel<128, false, kKvE4M3>(DecArgs);
-template __global__ void decode_split_kernel<64, true, kKvE4M3>(DecArgs);
-template __global__ void decode_split_kernel<128, true, kKvE4M3>(DecArgs);
-template __global__ void decode_split_kernel<64, false, kKvE5M2>(DecArgs);
-template __global__ void decode_split_kernel<128, false, kKvE5M2>(DecArgs);
-template __global__ void decode_split_kernel<64, true, kKvE5M2>(DecArgs);
-template __global__ void decode_split_kernel<128, true, kKvE5M2>(DecArgs);
-template __global__ void decode_merge_kernel<64>(DecArgs);
-template __global__ void decode_merge_kernel<128>(DecArgs);
+#define ATTN_DECODE_VARIANTS(KV)                                                 \
+  template __global__ void decode_split_kernel<64, false, KV, false>(DecArgs);  \
+  template __global__ void decode_split_kernel<128, false, KV, false>(DecArgs); \
+  template __global__ void decode_split_kernel<64, true, KV, false>(DecArgs);   \
+  template __global__ void decode_split_kernel<128, true, KV, false>(DecArgs);  \
+  template __global__ void decode_split_kernel<64, false, KV, true>(DecArgs);   \
+  template __global__ void decode_split_kernel<128, false, KV, true>(DecArgs);  \
+  template __global__ void decode_split_kernel<64, true, KV, true>(DecArgs);    \
+  template __global__ void decode_split_kernel<128, true, KV, true>(DecArgs);
+ATTN_DECODE_VARIANTS(kKvBf16)
+ATTN_DECODE_VARIANTS(kKvE4M3)
+ATTN_DECODE_VARIANTS(kKvE5M2)
+#undef ATTN_DECODE_VARIANTS
+template __global__ void decode_merge_kernel<64, false>(DecArgs);
+template __global__ void decode_merge_kernel<128, false>(DecArgs);
+template __global__ void decode_merge_kernel<64, true>(DecArgs);
+template __global__ void decode_merge_kernel<128, true>(DecArgs);
 
 DecWorkspaceLayout decode_workspace_layout(int n_seq, int Hq, int Hkv, int d) {
   const size_t slots = (size_t)decode_max_slots(n_seq, decode_rows_per_seq(Hq, Hkv));
@@ -581,11 +587,13 @@ int decode_workers(int d, bool fp8) {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
   hipError_t e;
   if (fp8)
-    e = d == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<128, false, kKvE4M3>, 64, 0)
-                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<64, false, kKvE4M3>, 64, 0);
+    e = d == 128
+            ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<128, false, kKvE4M3, true>, 64, 0)
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<64, false, kKvE4M3, true>, 64, 0);
   else
-    e = d == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<128, false, kKvBf16>, 64, 0)
-                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<64, false, kKvBf16>, 64, 0);
+    e = d == 128
+            ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<128, false, kKvBf16, true>, 64, 0)
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<64, false, kKvBf16, true>, 64, 0);
   if (e != hipSuccess || cus <= 0 || per_cu <= 0) return -1;
   const int cap = fp8 ? kDecodeWorkersPerCuFp8 : kDecodeWorkersPerCu;
   if (per_cu > cap) per_cu = cap;
@@ -596,10 +604,13 @@ int decode_workers(int d, bool fp8) {
 
 template <int D, int KV>
 void launch_split(const DecArgs& a, dim3 grid, hipStream_t stream) {
-  if (a.paged)
-    hipLaunchKernelGGL((decode_split_kernel<D, true, KV>), grid, dim3(64), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_split_kernel<D, false, KV>), grid, dim3(64), 0, stream, a);
+  if (a.pack > 1) {
+    if (a.paged) hipLaunchKernelGGL((decode_split_kernel<D, true, KV, true>), grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL((decode_split_kernel<D, false, KV, true>), grid, dim3(64), 0, stream, a);
+  } else {
+    if (a.paged) hipLaunchKernelGGL((decode_split_kernel<D, true, KV, false>), grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL((decode_split_kernel<D, false, KV, false>), grid, dim3(64), 0, stream, a);
+  }
 }
 
 template <int D>
@@ -612,7 +623,8 @@ void launch_decode_d(const DecArgs& a, hipStream_t stream) {
     launch_split<D, kKvE5M2>(a, g1, stream);
   else
     launch_split<D, kKvBf16>(a, g1, stream);
-  hipLaunchKernelGGL(decode_merge_kernel<D>, g2, dim3(64), 0, stream, a);
+  if (a.pack > 1) hipLaunchKernelGGL((decode_merge_kernel<D, true>), g2, dim3(64), 0, stream, a);
+  else hipLaunchKernelGGL((decode_merge_kernel<D, false>), g2, dim3(64), 0, stream, a);
 }
 
 hipError_t launch_decode(const DecArgs& a, int d, hipStream_t stream) {

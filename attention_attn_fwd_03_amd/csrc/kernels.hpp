@@ -5,6 +5,10 @@
 
 namespace attnfwd {
 
+// Mask modes of the prefill kernels (a compile-time parameter): no mask, causal, causal with a
+// sliding window.
+enum MaskMode : int { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2 };
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -18,7 +22,7 @@ struct FwdArgs {
   int qmode;          // kQAsIs, kQNegate (scale < 0) or kQZero (scale = 0): c is always > 0
   int n_qt;           // query tiles per head (ragged batches: of the longest sequence)
   int heads_per_xcd;  // > 0: XCD-banded block order (see plan.hpp)
-  // Ragged batches against a pool (fwd_bf16_kernel<..., true>): B is the number of sequences;
+  // Ragged batches against a pool (fwd_bf16_kernel<..., true, ...>): B is the number of sequences;
   // q and o are [total_q, Hq, d] with sequence b's rows cu_q[b] .. cu_q[b+1] - 1; k and v are the
   // pools [pool_rows, Hkv, d] with its keys at rows kv_offs[b] .. + kv_lens[b] - 1; lse is
   // [total_q, Hq].  Lq and Lk are the largest query count (max_seqlen_q) and unused.
@@ -105,5 +109,9 @@ int decode_workers(int d, bool fp8 = false);
 hipError_t launch_decode(const DecArgs& a, int d, hipStream_t stream);
 
 hipError_t launch_backward(const BwdArgs& a, int d, hipStream_t stream);
+
+// Matrix-core ceiling probe (probe.hip): `workgroups` workgroups of four waves, each running
+// `steps` 32-key steps of the prefill loop's MFMA and LDS work; sink holds workgroups * 256 floats.
+hipError_t launch_probe_mfma(int workgroups, int steps, float* sink, hipStream_t stream);
 
 }  // namespace attnfwd

@@ -66,10 +66,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t strided_rows_rsrc(const unsign
 // (two stages of K and V take 38 KB; tiles of 64 would take 74 KB) and d = 64 in tiles of 64 (42 KB).
 // VARLEN: a ragged batch against a pool (see FwdArgs): each workgroup finds its sequence's query
 // rows and keys, rows are strided by the head count, and tiles past a sequence's end exit at once.
-template <int D, int BK, bool VARLEN>
+// MASK (kMaskNone, kMaskCausal, kMaskWindow) is the mask mode, fixed at compile time: a kernel
+// without a window carries none of its tests.
+template <int D, int BK, bool VARLEN, int MASK>
 __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(FwdArgs a) {
   using C = Bf16Cfg<D, BK>;
   constexpr int NB = C::NB;
+  constexpr int causal = MASK != kMaskNone;
+  const int window = MASK == kMaskWindow ? a.window : 0;
   // Two K stages and two V stages, filled straight from global memory by buffer loads while the
   // other stage is being computed on.  Each stage is its own LDS object, so the compiler can see
   // that reads of one stage do not depend on the loads still landing in the other and does not
@@ -94,7 +98,7 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(FwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (C::WAVES - 1);
   const int h = lane >> 5, col = lane & 31;
   const PrefillTile t = VARLEN ? prefill_tile_grouped(blockIdx.x, a.B, a.Hq, a.Hkv, a.n_qt)
-                               : prefill_tile(blockIdx.x, a.B, a.Hq, a.group, a.n_qt, a.causal, a.heads_per_xcd);
+                               : prefill_tile(blockIdx.x, a.B, a.Hq, a.group, a.n_qt, causal, a.heads_per_xcd);
   if (VARLEN && t.b >= a.B) return;  // padding block of the grouped order
   const int q_start = t.qt * C::BQ;
   const int q = q_start + wave * 32 + col;  // query row of this lane
@@ -138,7 +142,7 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(FwdArgs a) {
     Qg = (const unsigned short*)a.q + ((size_t)(t.b * a.Hq + t.hq) * a.Lq) * D;
     kv_off = ((size_t)(t.b * a.Hkv + t.hkv) * a.Lk) * D;
   }
-  const KeyRange kr = key_range(q_start, C::BQ, a.Lq, a.Lk, BK, a.causal, a.window);
+  const KeyRange kr = key_range(q_start, C::BQ, a.Lq, a.Lk, BK, causal, window);
   const unsigned short* Kh = (const unsigned short*)a.k + kv_off;  // this head's K and V rows
   const unsigned short* Vh = (const unsigned short*)a.v + kv_off;
 
@@ -230,7 +234,7 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(FwdArgs a) {
   };
   const int lo = kr.kt_lo, hi = kr.kt_hi;
   const int w_start = q_start + wave * 32;  // this wave's rows: [w_start, w_start + 32)
-  const KeyRange wkr = key_range(w_start, 32, a.Lq, a.Lk, BK, a.causal, a.window);
+  const KeyRange wkr = key_range(w_start, 32, a.Lq, a.Lk, BK, causal, window);
   const int w_lo = wkr.kt_lo, w_hi = wkr.kt_hi;
   // One tile on stage `stage` (a compile-time constant after the unroll below): start the loads of
   // tile kt+1 into the other stage, S = K Q^T, mask (edge tiles only), the online softmax of S,
@@ -249,9 +253,9 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(FwdArgs a) {
       f32x16 sc[NB];
       qk(Cur{}, sc);
       const int k0 = kt * BK;
-      if (!tile_full(k0, w_start, 32, a.Lq, a.Lk, BK, a.causal, a.window)) {
+      if (!tile_full(k0, w_start, 32, a.Lq, a.Lk, BK, causal, window)) {
         int elo, ehi;
-        edge_key_limits(k0, h, q, a.Lq, a.Lk, a.causal, a.window, elo, ehi);
+        edge_key_limits(k0, h, q, a.Lq, a.Lk, causal, window, elo, ehi);
         mask_tile(sc, elo, ehi);
       }
       const float mb = update_max(sc, st, o, c);
@@ -448,10 +452,16 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
 // ---------------------------------------------------------------------------------------------
 
 // Explicit instantiations: the host pass must emit a launch stub for every variant.
-template __global__ void fwd_bf16_kernel<64, 64, false>(FwdArgs);
-template __global__ void fwd_bf16_kernel<128, 32, false>(FwdArgs);
-template __global__ void fwd_bf16_kernel<64, 64, true>(FwdArgs);
-template __global__ void fwd_bf16_kernel<128, 32, true>(FwdArgs);
+#define ATTN_FWD_BF16_VARIANTS(VARLEN, MASK)                          \
+  template __global__ void fwd_bf16_kernel<64, 64, VARLEN, MASK>(FwdArgs); \
+  template __global__ void fwd_bf16_kernel<128, 32, VARLEN, MASK>(FwdArgs);
+ATTN_FWD_BF16_VARIANTS(false, kMaskNone)
+ATTN_FWD_BF16_VARIANTS(false, kMaskCausal)
+ATTN_FWD_BF16_VARIANTS(false, kMaskWindow)
+ATTN_FWD_BF16_VARIANTS(true, kMaskNone)
+ATTN_FWD_BF16_VARIANTS(true, kMaskCausal)
+ATTN_FWD_BF16_VARIANTS(true, kMaskWindow)
+#undef ATTN_FWD_BF16_VARIANTS
 template __global__ void fwd_f32_kernel<64>(FwdArgs);
 template __global__ void fwd_f32_kernel<128>(FwdArgs);
 
@@ -463,6 +473,23 @@ int prefill_lds_bytes(bool f32, int d) {
   return d == 64 ? Bf16Cfg<64, 64>::LDS_BYTES : Bf16Cfg<128, 32>::LDS_BYTES;
 }
 
+int mask_mode(const FwdArgs& a) { return a.causal ? (a.window > 0 ? kMaskWindow : kMaskCausal) : kMaskNone; }
+
+template <bool VARLEN, int MASK>
+void launch_bf16(const FwdArgs& a, int d, dim3 g, hipStream_t stream) {
+  if (d == 64) hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, VARLEN, MASK>), g, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((fwd_bf16_kernel<128, 32, VARLEN, MASK>), g, dim3(256), 0, stream, a);
+}
+
+template <bool VARLEN>
+void launch_bf16_masked(const FwdArgs& a, int d, dim3 g, hipStream_t stream) {
+  switch (mask_mode(a)) {
+    case kMaskNone: launch_bf16<VARLEN, kMaskNone>(a, d, g, stream); break;
+    case kMaskCausal: launch_bf16<VARLEN, kMaskCausal>(a, d, g, stream); break;
+    default: launch_bf16<VARLEN, kMaskWindow>(a, d, g, stream); break;
+  }
+}
+
 hipError_t launch_prefill(const FwdArgs& a, bool f32, int d, hipStream_t stream) {
   const int64_t grid = (int64_t)a.n_qt * a.B * a.Hq;
   const dim3 g((unsigned)grid), b(256);
@@ -470,17 +497,14 @@ hipError_t launch_prefill(const FwdArgs& a, bool f32, int d, hipStream_t stream)
     if (d == 64) hipLaunchKernelGGL(fwd_f32_kernel<64>, g, b, 0, stream, a);
     else hipLaunchKernelGGL(fwd_f32_kernel<128>, g, b, 0, stream, a);
   } else {
-    if (d == 64) hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, false>), g, b, 0, stream, a);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<128, 32, false>), g, b, 0, stream, a);
+    launch_bf16_masked<false>(a, d, g, stream);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_varlen(const FwdArgs& a, int d, hipStream_t stream) {
   const int64_t grid = prefill_grouped_blocks(a.B, a.Hq, a.Hkv, a.n_qt);
-  const dim3 g((unsigned)grid), b(256);
-  if (d == 64) hipLaunchKernelGGL((fwd_bf16_kernel<64, 64, true>), g, b, 0, stream, a);
-  else hipLaunchKernelGGL((fwd_bf16_kernel<128, 32, true>), g, b, 0, stream, a);
+  launch_bf16_masked<true>(a, d, dim3((unsigned)grid), stream);
   return hipGetLastError();
 }
 

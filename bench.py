@@ -1,22 +1,27 @@
 #!/usr/bin/env python3
 """Throughput of the attention hot path on one MI355X.
 
-One step = one pass of the whole path over one batch of synthetic input:
-  * prefill: attn_fwd on the causal GQA workload (B=2, Hq=32, Hkv=8, L=4096, d=128, bf16,
-    LSE returned), and
+One step = one pass of the whole path over one batch of synthetic input, in this order:
+  * prefill: attn_fwd on the causal GQA workload (B=2, Hq=32, Hkv=8, L=4096, d=128, bf16, LSE),
+  * prefill: attn_fwd on the sliding-window workload (B=1, Hq=32, Hkv=8, L=16384, W=4096, d=128),
   * decode: attn_decode on the GQA decode batch (64 sequences, Hq=32, Hkv=8, d=128, KV lengths
-    uniform in [1024, 32768], one pooled K/V buffer with poisoned gaps).
-Inputs are generated on the device before timing.  The reported value is the prefill's useful
-TFLOP/s (4*d per visible (query, key) pair per query head); the decode's KV-read GB/s is
-reported beside it.  Kernel times come from HIP events recorded on the stream the kernels run
-on, over the timed steps.
+    uniform in [1024, 32768], one pooled K/V buffer with poisoned gaps),
+  * decode: attn_decode on the MQA batch (same lengths, Hkv=1), rotated over pool replicas so
+    that the 256 MB last-level cache cannot serve the 0.6 GB pool from one step to the next.
+Inputs are generated on the device before timing.  The reported value is the causal GQA
+prefill's useful TFLOP/s (4*d per visible (query, key) pair per query head); every part gets its
+own roofline object.  Kernel times come from HIP events recorded on the stream the kernels run on,
+around each part of each timed step.  After the timed steps the causal prefill is also timed back
+to back (no other kernel between its calls) and reported beside the in-step figure.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+  python bench.py --only PART    # one part of the step only (profiling)
   python bench.py --suite        # one JSON line per workload (the five, the backward of the dense
                                  # bf16 ones, both decode batches in a
                                  # paged cache, and a ragged chunked-prefill batch), for the tables
+  python bench.py --mfma-ceiling # the matrix-core + LDS ceiling probe (include/attn_probe.h)
   python bench.py --copy-calib   # a plain device copy of known size, to scale HBM counters
-  python bench.py --summarize-counters FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
+  python bench.py --summarize-counters FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR [MFMA_DIR]
                                  # rocprofv3 --pmc outputs -> per-launch HBM bytes (profiles/hbm_traffic.md)
 
 The roofline "traffic" fields come from profiles/hbm_traffic.md (FETCH_SIZE / WRITE_SIZE counter
@@ -213,6 +218,47 @@ def cpu_baseline(c, q, k, v):
                       f"{dt:.1f} s wall", "seconds": dt}
 
 
+# The parts of one step, in order: (name, kind, workload).
+STEP_PARTS = [("prefill", "prefill", "gqa_causal_bf16_L4096"),
+              ("prefill_window", "prefill", "swa_gqa_bf16_L16384_W4096"),
+              ("decode", "decode", "gqa_decode_bf16"),
+              ("decode_mqa", "decode", "mqa_decode_bf16")]
+# Kernel names as rocprofv3 reports them (template arguments: head size, key tile, ragged, mask mode;
+# head size, paged, pool format, packed layout), for the counter summary's traffic fields.
+PART_KERNELS = {"prefill": ["fwd_bf16_kernel<128, 32, false, 1>"],
+                "prefill_window": ["fwd_bf16_kernel<128, 32, false, 2>"],
+                "decode": ["decode_split_kernel<128, false, 0, true>", "decode_merge_kernel<128, true>"],
+                "decode_mqa": ["decode_split_kernel<128, false, 0, false>", "decode_merge_kernel<128, false>"]}
+MQA_REPLICAS = 4  # 4 x 0.62 GB of MQA pools: well past the 256 MB last-level cache
+
+
+def mfma_ceiling(args):
+    """The ceiling probe: 768 workgroups (one per slot: three per CU), timed over several launches
+    of `steps` 32-key steps each, as TFLOP/s and as a fraction of the nominal bf16 peak."""
+    import torch
+    import attention_attn_fwd_03_amd as af
+    wgs, steps = 768, 4096
+    sink = torch.empty(wgs * 256, device="cuda", dtype=torch.float32)
+    for _ in range(3):
+        af.probe_mfma_ceiling(wgs, steps, sink)
+    torch.cuda.synchronize()
+    ev = _events(2)
+    reps = 10
+    ev[0].record()
+    for _ in range(reps):
+        af.probe_mfma_ceiling(wgs, steps, sink)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    flops = wgs * 4 * steps * 16 * 2 * 32 * 32 * 16
+    tf = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({"probe": "mfma_lds_ceiling", "workgroups": wgs, "steps": steps, "ms_per_launch": round(ms, 4),
+                      "TFLOP/s": round(tf, 1), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                      "peak_TFLOP/s": PEAK_BF16_TFLOPS,
+                      "what": "16 bf16 32x32x16 MFMAs per 32-key step with K / V^T operands from LDS, the "
+                              "prefill kernel's launch shape, no softmax and no global loads"}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,8 +267,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--suite", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
-                    help="profile helper: run only one half of the step")
+    ap.add_argument("--mfma-ceiling", action="store_true")
+    ap.add_argument("--only", choices=[p[0] for p in STEP_PARTS], default=None,
+                    help="profile helper: run only this part of the step")
     ap.add_argument("--workload", default=None, help="with --suite: run only this workload")
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR", default=None,
                     help="rocprofv3 --pmc output dirs: FETCH_SIZE, WRITE_SIZE, both for --copy-calib, "
@@ -260,45 +307,71 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calib_bytes_read": n, "copy_calib_bytes_written": n}), flush=True)
         return
-
+    if args.mfma_ceiling:
+        return mfma_ceiling(args)
     if args.suite:
         return run_suite(args)
 
-    cp = wl.PREFILL["gqa_causal_bf16_L4096"]
-    cd = wl.DECODE["gqa_decode_bf16"]
-    q, k, v = wl.prefill_inputs_for(cp, device=dev)
-    o = torch.empty_like(q)
-    lse = torch.empty(q.shape[:3], device=dev, dtype=torch.float32)
-    lens = wl.decode_lens(cd.n_seq, cd.len_lo, cd.len_hi, cd.lens_seed)
-    qd, kp, vp, offs, lens_t, layout = wl.decode_inputs(cd.n_seq, cd.Hq, cd.Hkv, cd.d, lens, seed=cd.value_seed,
-                                                        device=dev, max_gap=cd.max_gap)
-    max_len = int(lens.max())
-    od = torch.empty_like(qd)
-    lsed = torch.empty((cd.n_seq, cd.Hq), device=dev, dtype=torch.float32)
-    ws = torch.empty(af.decode_workspace_size(cd.n_seq, cd.Hq, cd.Hkv, cd.d, max_len), device=dev, dtype=torch.uint8)
+    parts = [p for p in STEP_PARTS if args.only in (None, p[0])]
+    run = {}    # part -> callable enqueuing it
+    info = {}   # part -> config dict and work / bytes per call
+    for name, kind, wname in parts:
+        if kind == "prefill":
+            c = wl.PREFILL[wname]
+            q, k, v = wl.prefill_inputs_for(c, device=dev)
+            o = torch.empty_like(q)
+            lse = torch.empty(q.shape[:3], device=dev, dtype=torch.float32)
+            run[name] = (lambda c=c, q=q, k=k, v=v, o=o, lse=lse:
+                         af.attn_fwd(q, k, v, causal=c.causal, window=c.window, scale=c.scale, return_lse=True,
+                                     out=o, lse_out=lse))
+            fl = prefill_flops(c)
+            info[name] = {"cfg": c, "work": fl, "inputs": (q, k, v),
+                          "config": {"workload": wname, "B": c.B, "Hq": c.Hq, "Hkv": c.Hkv, "L": c.Lq, "d": c.d,
+                                     "causal": c.causal, "window": c.window, "lse": True,
+                                     "useful_gflop": round(fl / 1e9, 3)}}
+        else:
+            c = wl.DECODE[wname]
+            lens = wl.decode_lens(c.n_seq, c.len_lo, c.len_hi, c.lens_seed)
+            max_len = int(lens.max())
+            n_rep = MQA_REPLICAS if c.Hkv == 1 else 1
+            reps = []
+            for r in range(n_rep):
+                qd, kp, vp, offs, lens_t, _ = wl.decode_inputs(c.n_seq, c.Hq, c.Hkv, c.d, lens,
+                                                               seed=c.value_seed + 100 * r, device=dev,
+                                                               max_gap=c.max_gap)
+                reps.append((qd, kp, vp, offs, lens_t))
+            od = torch.empty_like(reps[0][0])
+            lsed = torch.empty((c.n_seq, c.Hq), device=dev, dtype=torch.float32)
+            ws = torch.empty(af.decode_workspace_size(c.n_seq, c.Hq, c.Hkv, c.d, max_len), device=dev,
+                             dtype=torch.uint8)
+            it = [0]
+
+            def call(c=c, reps=reps, it=it, od=od, lsed=lsed, ws=ws, max_len=max_len):
+                qd, kp, vp, offs, lens_t = reps[it[0] % len(reps)]
+                it[0] += 1
+                af.attn_decode(qd, kp, vp, offs, lens_t, max_len=max_len, scale=c.scale, return_lse=True,
+                               workspace=ws, out=od, lse_out=lsed)
+            run[name] = call
+            n_tok = int(lens.sum())
+            by = decode_bytes(n_tok, c.n_seq, c.Hq, c.Hkv, c.d)
+            info[name] = {"cfg": c, "work": by,
+                          "config": {"workload": wname, "n_seq": c.n_seq, "Hq": c.Hq, "Hkv": c.Hkv, "d": c.d,
+                                     "kv_tokens": n_tok, "max_len": max_len, "pool_replicas": n_rep,
+                                     "algorithmic_gb": round(by / 1e9, 4)}}
     torch.cuda.synchronize()
 
-    do_pre = args.only in (None, "prefill")
-    do_dec = args.only in (None, "decode")
-
     def step(ev=None):
+        for i, (name, _, _) in enumerate(parts):
+            if ev is not None:
+                ev[i].record()
+            run[name]()
         if ev is not None:
-            ev[0].record()
-        if do_pre:
-            af.attn_fwd(q, k, v, causal=cp.causal, window=cp.window, scale=cp.scale, return_lse=True, out=o,
-                        lse_out=lse)
-        if ev is not None:
-            ev[1].record()
-        if do_dec:
-            af.attn_decode(qd, kp, vp, offs, lens_t, max_len=max_len, scale=cd.scale, return_lse=True,
-                           workspace=ws, out=od, lse_out=lsed)
-        if ev is not None:
-            ev[2].record()
+            ev[len(parts)].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [_events(3) for _ in range(args.steps)]
+    evs = [_events(len(parts) + 1) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -308,20 +381,48 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    pre_avg = sum(pre_ms) / len(pre_ms)
-    dec_avg = sum(dec_ms) / len(dec_ms)
-    n_tok = int(lens.sum())
-    pflops = prefill_flops(cp)
-    dbytes = decode_bytes(n_tok, cd.n_seq, cd.Hq, cd.Hkv, cd.d)
-    pre_tflops = pflops / (pre_avg * 1e-3) / 1e12 if do_pre else 0.0
-    dec_gbs = dbytes / (dec_avg * 1e-3) / 1e9 if do_dec else 0.0
+    for i, (name, _, _) in enumerate(parts):
+        ms = [e[i].elapsed_time(e[i + 1]) for e in evs]
+        info[name]["ms"] = sum(ms) / len(ms)
+        info[name]["ms_min"] = min(ms)
 
+    # The causal prefill back to back: `steps` calls with nothing in between, one event pair.
+    if "prefill" in run:
+        ev = _events(2)
+        ev[0].record()
+        for _ in range(args.steps):
+            run["prefill"]()
+        ev[1].record()
+        torch.cuda.synchronize()
+        info["prefill"]["back_to_back_ms"] = ev[0].elapsed_time(ev[1]) / args.steps
+
+    def roofline(name):
+        x = info[name]
+        if x["cfg"].__class__.__name__ == "PrefillConfig":
+            tf = x["work"] / (x["ms"] * 1e-3) / 1e12
+            r = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": PART_KERNELS[name][0],
+                 "workload": x["config"]["workload"], "kernel_ms": round(x["ms"], 4),
+                 "kernel_ms_min": round(x["ms_min"], 4),
+                 "per_launch": f"{x['work'] / 1e9:.1f} GFLOP useful (4*d per visible pair, all heads)"}
+            if "back_to_back_ms" in x:
+                b2b = x["work"] / (x["back_to_back_ms"] * 1e-3) / 1e12
+                r["back_to_back"] = {"kernel_ms": round(x["back_to_back_ms"], 4), "achieved": round(b2b, 2),
+                                     "frac": round(b2b / PEAK_BF16_TFLOPS, 4)}
+            return r
+        gbs = x["work"] / (x["ms"] * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "kernels": " + ".join(PART_KERNELS[name]),
+                "workload": x["config"]["workload"], "kernels_ms": round(x["ms"], 4),
+                "kernels_ms_min": round(x["ms_min"], 4),
+                "per_launch": f"{x['work'] / 1e9:.3f} GB (one read of live K/V rows + q, O, LSE)"}
+
+    head = "prefill" if "prefill" in info else parts[0][0]
+    main_roof = roofline(head)
     line = {
         "metric": "prefill attn TFLOP/s (% MFMA peak) + decode KV-read GB/s (% HBM peak), 1 GPU",
-        "value": round(pre_tflops, 2),
-        "unit": "TFLOP/s",
+        "value": main_roof["achieved"],
+        "unit": main_roof["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -330,42 +431,28 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic: seeded N(0,1) q/k/v (bf16), decode pool with seeded lengths and NaN gaps",
-        "config": {
-            "workload": "prefill gqa_causal_bf16_L4096 + decode gqa_decode_bf16",
-            "prefill": {"B": cp.B, "Hq": cp.Hq, "Hkv": cp.Hkv, "L": cp.Lq, "d": cp.d, "causal": cp.causal,
-                        "window": cp.window, "lse": True, "useful_gflop": round(pflops / 1e9, 3),
-                        "kernel_ms": round(pre_avg, 4), "kernel_ms_min": round(min(pre_ms), 4)},
-            "decode": {"n_seq": cd.n_seq, "Hq": cd.Hq, "Hkv": cd.Hkv, "d": cd.d, "kv_tokens": n_tok,
-                       "max_len": max_len, "algorithmic_gb": round(dbytes / 1e9, 4),
-                       "kernels_ms": round(dec_avg, 4), "kernels_ms_min": round(min(dec_ms), 4),
-                       "GB/s": round(dec_gbs, 1), "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4)},
-            "parallelism": "single GPU",
-        },
-        "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "fwd_bf16_kernel<128,32,false>",
-                     "per_launch": f"{pflops / 1e9:.1f} GFLOP useful (4*d per visible pair, 64 heads)"},
-        "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                            "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                            "kernels": "decode_split_kernel<128, false, 0> + decode_merge_kernel<128>",
-                            "per_launch": f"{dbytes / 1e9:.3f} GB (one read of live K/V rows + q, O, LSE)"},
+        "data": "synthetic: seeded N(0,1) q/k/v (bf16), decode pools with seeded lengths and NaN gaps",
+        "config": {"workload": " + ".join(info[n]["config"]["workload"] for n, _, _ in parts),
+                   **{n: info[n]["config"] for n, _, _ in parts}, "parallelism": "single GPU"},
+        "roofline": main_roof,
     }
+    for n, _, _ in parts:
+        if n != head:
+            line["roofline_" + n] = roofline(n)
     traffic = load_traffic()
     if traffic is not None:
-        kp = traffic["kernels"].get("fwd_bf16_kernel<128, 32, false>")
-        ks = traffic["kernels"].get("decode_split_kernel<128, false, 0>")
-        km = traffic["kernels"].get("decode_merge_kernel<128>")
-        if kp:
-            line["roofline"]["traffic"] = kp["traffic_bytes"]
-            for key in ("mfma_busy_frac", "engine_clock_ghz"):
-                if key in kp:
-                    line["roofline"]["counters_" + key] = kp[key]
-        if ks and km:
-            line["roofline_decode"]["traffic"] = ks["traffic_bytes"] + km["traffic_bytes"]
-    if not args.no_cpu_baseline and do_pre:
+        for n, _, _ in parts:
+            key = "roofline" if n == head else "roofline_" + n
+            ks = [traffic["kernels"].get(k) for k in PART_KERNELS[n]]
+            if all(ks):
+                line[key]["traffic"] = sum(k["traffic_bytes"] for k in ks)
+                for field in ("mfma_busy_frac", "engine_clock_ghz"):
+                    if field in ks[0]:
+                        line[key]["counters_" + field] = ks[0][field]
+    if not args.no_cpu_baseline and "prefill" in info:
         print("# timing the oracle on the host", file=sys.stderr, flush=True)
-        cb = cpu_baseline(cp, q.cpu(), k.cpu(), v.cpu())
+        q, k, v = info["prefill"]["inputs"]
+        cb = cpu_baseline(info["prefill"]["cfg"], q.cpu(), k.cpu(), v.cpu())
         line["cpu_baseline"] = {kk: cb[kk] for kk in ("value", "unit", "cores", "kind", "sample")}
     print(json.dumps(line), flush=True)
 

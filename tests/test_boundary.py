@@ -12,7 +12,12 @@ import pytest
 import attention_attn_fwd_03_amd as af
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "attn.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
+
+
+def _header_text():
+    return "\n".join(open(h).read() for h in HEADERS)
 
 # Fake, 16-byte aligned "device" addresses: never dereferenced, because every call below is
 # rejected by host-side validation first.
@@ -21,8 +26,7 @@ MISALIGNED = 0x10008
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"/\*.*?\*/", "", _header_text(), flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(attn_\w+)\s*\(", text, flags=re.M)))
 
 
@@ -35,8 +39,8 @@ def test_library_loads_and_exports_header_symbols():
 
 
 def declared_prototypes():
-    """{name: [parameter type, ...]} of every function include/attn.h declares."""
-    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    """{name: [parameter type, ...]} of every function include/*.h declares."""
+    text = re.sub(r"/\*.*?\*/", "", _header_text(), flags=re.S)
     out = {}
     for m in re.finditer(r"^\s*(?:const\s+)?\w+\**\s+\**(attn_\w+)\s*\(([^)]*)\)\s*;", text, flags=re.M):
         params = [" ".join(p.split()) for p in m.group(2).split(",") if p.strip()]
@@ -503,3 +507,11 @@ def test_decode_rows_read_only_their_own_heads(Hq, Hkv):
     n_seq = 3
     last_row_read = (n_seq - 1) * Hq + max(f + n - 1 for _, f, n in rows.tolist())
     assert last_row_read < n_seq * Hq
+
+
+def test_probe_rejects_bad_arguments():
+    L = af.lib()
+    assert L.attn_probe_mfma_ceiling(768, 10, None, 1 << 20, None) == af.ATTN_ERR_NULL
+    assert L.attn_probe_mfma_ceiling(0, 10, P, 1 << 20, None) == af.ATTN_ERR_SHAPE
+    assert L.attn_probe_mfma_ceiling(768, 0, P, 1 << 20, None) == af.ATTN_ERR_SHAPE
+    assert L.attn_probe_mfma_ceiling(768, 10, P, 768 * 256 * 4 - 4, None) == af.ATTN_ERR_WORKSPACE
