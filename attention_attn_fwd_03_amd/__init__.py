@@ -21,7 +21,8 @@ KV_FORMATS = {"e4m3fn": 1, "e5m2": 2}  # attn_kv_format
 EXPORTS = ["attn_fwd", "attn_fwd_f32", "attn_fwd_varlen", "attn_decode_workspace_size", "attn_decode",
            "attn_decode_paged", "attn_status_str", "attn_fwd_plan", "attn_fwd_schedule", "attn_fwd_varlen_schedule",
            "attn_decode_plan", "attn_bwd_workspace_size", "attn_bwd", "attn_decode_fp8", "attn_decode_paged_fp8",
-           "attn_fwd_fp8", "attn_decode_rows", "attn_probe_mfma_ceiling"]
+           "attn_fwd_fp8", "attn_decode_rows", "attn_decode_noalloc", "attn_probe_mfma_ceiling"]
+DECODE_NOALLOC_BYTES = 64 << 20  # ATTN_DECODE_NOALLOC_BYTES
 
 
 class FwdPlanInfo(ctypes.Structure):
@@ -53,6 +54,8 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_workspace_size.restype = sz
     L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, i32, f32, vp, sz, vp]
     L.attn_decode.restype = i32
+    L.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, i32, f32, vp]
+    L.attn_decode_noalloc.restype = i32
     L.attn_probe_mfma_ceiling.argtypes = [i32, i32, vp, sz, vp]
     L.attn_probe_mfma_ceiling.restype = i32
     L.attn_decode_paged.argtypes = [vp, vp, vp, vp, i32, i32, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
@@ -317,6 +320,34 @@ def attn_decode(q, k_pool, v_pool, offsets, lens, *, max_len: int, window: int =
     else:
         _run(dev, lib().attn_decode_fp8, *args, fmt, float(k_scale), float(v_scale), *tail)
     return (o, lse) if return_lse else o
+
+
+def attn_decode_noalloc(q, k_pool, v_pool, offsets, lens, *, max_len: int, out, lse_out=None, window: int = 0,
+                        scale: float | None = None):
+    """attn_decode (bf16 pools) through the entry point that allocates nothing: the library's fixed
+    per-GPU workspace of DECODE_NOALLOC_BYTES replaces the caller's, and the outputs ``out``
+    [N, Hq, d] bf16 and optional ``lse_out`` [N, Hq] fp32 must be given.  Calls that overlap in
+    time on one GPU race (they share that workspace)."""
+    import torch
+    dev = _require_gpu(q, k_pool, v_pool, offsets, lens)
+    if _kv_format(q, k_pool, v_pool, None, None, None) != 0:
+        raise ValueError("attn_decode_noalloc takes bfloat16 pools")
+    if offsets.dtype != torch.int64 or lens.dtype != torch.int32:
+        raise ValueError("offsets must be int64 and lens int32")
+    if q.dim() != 3 or k_pool.dim() != 3:
+        raise ValueError("expected q [N, Hq, d] and pools [T, Hkv, d]")
+    N, Hq, d = q.shape
+    T, Hkv, dk = k_pool.shape
+    if dk != d or tuple(v_pool.shape) != tuple(k_pool.shape) or offsets.numel() != N or lens.numel() != N:
+        raise ValueError("shape mismatch between q, pools, offsets and lens")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = _output(out, q.shape, torch.bfloat16, dev, "out")
+    lse = _output(lse_out, (N, Hq), torch.float32, dev, "lse_out") if lse_out is not None else None
+    _run(dev, lib().attn_decode_noalloc, q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), offsets.data_ptr(),
+         lens.data_ptr(), o.data_ptr(), lse.data_ptr() if lse is not None else None, N, Hq, Hkv, d, T, int(max_len),
+         int(window), float(scale))
+    return o
 
 
 def attn_decode_paged(q, k_pool, v_pool, block_table, lens, *, page_size: int, max_len: int, window: int = 0,

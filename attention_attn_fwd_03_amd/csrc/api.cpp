@@ -156,7 +156,8 @@ namespace {
 // a.kv_fmt selects the pool's element format; k_scale and v_scale apply to fp8 pools only.
 int decode_common(const void* q, const void* k_pool, const void* v_pool, const int32_t* lens, void* o,
                   float* lse, int n_seq, int Hq, int Hkv, int d, int max_len, int window, float scale,
-                  float k_scale, float v_scale, void* workspace, size_t workspace_bytes, void* stream, DecArgs& a) {
+                  float k_scale, float v_scale, void* workspace, size_t workspace_bytes, void* stream, DecArgs& a,
+                  bool static_scratch = false) {
   if (!q || !k_pool || !v_pool || !lens || !o) return ATTN_ERR_NULL;
   if (n_seq <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_len < 1 || window < 0) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
@@ -179,6 +180,12 @@ int decode_common(const void* q, const void* k_pool, const void* v_pool, const i
     return ATTN_ERR_SHAPE;
   if (a.paged && a.page_size % tpb != 0) return ATTN_ERR_UNSUPPORTED;
   const DecWorkspaceLayout lay = decode_workspace_layout(n_seq, Hq, Hkv, d);
+  if (static_scratch) {  // the library's own fixed workspace (attn_decode_noalloc)
+    if (lay.total > kDecodeScratchBytes) return ATTN_ERR_WORKSPACE;
+    workspace = decode_scratch();
+    if (workspace == nullptr) return ATTN_ERR_HIP;
+    workspace_bytes = kDecodeScratchBytes;
+  }
   if (workspace == nullptr || workspace_bytes < lay.total) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_UNSUPPORTED;
   const int workers = decode_workers(d, a.kv_fmt != 0);
@@ -233,6 +240,19 @@ int attn_decode(const void* q, const void* k_pool, const void* v_pool, const int
   a.paged = 0;
   return decode_common(q, k_pool, v_pool, lens, o, lse, n_seq, Hq, Hkv, d, max_len, window, scale, 1.f, 1.f,
                        workspace, workspace_bytes, stream, a);
+}
+
+int attn_decode_noalloc(const void* q, const void* k_pool, const void* v_pool, const int64_t* offsets,
+                        const int32_t* lens, void* o, float* lse, int n_seq, int Hq, int Hkv, int d,
+                        int64_t pool_rows, int max_len, int window, float scale, void* stream) {
+  if (!offsets) return ATTN_ERR_NULL;
+  if (pool_rows < 0) return ATTN_ERR_SHAPE;
+  DecArgs a{};
+  a.offsets = offsets;
+  a.pool_rows = pool_rows;
+  a.paged = 0;
+  return decode_common(q, k_pool, v_pool, lens, o, lse, n_seq, Hq, Hkv, d, max_len, window, scale, 1.f, 1.f,
+                       nullptr, 0, stream, a, true);
 }
 
 int attn_decode_fp8(const void* q, const void* k_pool, const void* v_pool, const int64_t* offsets,
@@ -360,7 +380,9 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_UNSUPPORTED:
       return "ATTN_ERR_UNSUPPORTED: unsupported head size, window without causal, non-finite scale or "
              "misaligned pointer";
-    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace missing or too small";
+    case ATTN_ERR_WORKSPACE:
+      return "ATTN_ERR_WORKSPACE: workspace missing or too small (attn_decode_noalloc: the call needs more than "
+             "the library's fixed ATTN_DECODE_NOALLOC_BYTES of decode workspace)";
     case ATTN_ERR_HIP: return "ATTN_ERR_HIP: kernel launch failed";
     default: return "unknown attn status";
   }
@@ -430,6 +452,8 @@ int attn_fwd_varlen_schedule(int n_seq, int Hq, int Hkv, int max_seqlen_q, int32
   }
   return ATTN_OK;
 }
+
+static_assert(ATTN_DECODE_NOALLOC_BYTES == kDecodeScratchBytes, "the header states the scratch size");
 
 int attn_decode_rows(int Hq, int Hkv, int32_t* kv_head, int32_t* first_head, int32_t* n_heads, int64_t out_len) {
   if (!kv_head || !first_head || !n_heads) return ATTN_ERR_NULL;

@@ -26,6 +26,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "attn_device.hpp"
@@ -574,6 +575,29 @@ DecWorkspaceLayout decode_workspace_layout(int n_seq, int Hq, int Hkv, int d) {
   l.o = l.ml + up(slots * nh * 2 * sizeof(float));
   l.total = l.o + slots * nh * (size_t)d * sizeof(float);
   return l;
+}
+
+// Workspace of attn_decode_noalloc, for callers that cannot allocate device memory: a fixed array
+// in the library's code object.  Each GPU the library runs on holds its own copy (at its own
+// address) until the process ends.  Host code never uses the array's name as an address; the
+// device address comes from hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+void* decode_scratch() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> ptrs[kMaxDevices];
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = ptrs[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(mu);
+  p = ptrs[dev].load(std::memory_order_relaxed);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    ptrs[dev].store(p, std::memory_order_release);
+  }
+  return p;
 }
 
 int decode_workers(int d, bool fp8) {

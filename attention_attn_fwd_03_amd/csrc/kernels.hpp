@@ -104,6 +104,11 @@ hipError_t launch_prefill(const FwdArgs& a, bool f32, int d, hipStream_t stream)
 hipError_t launch_prefill_varlen(const FwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_prefill_fp8(const FwdArgs& a, int d, int fmt, hipStream_t stream);
 
+// The static decode workspace of the current device (attn_decode_noalloc): its device address,
+// looked up once per device, or nullptr if the runtime refuses.
+constexpr size_t kDecodeScratchBytes = size_t(64) << 20;
+void* decode_scratch();
+
 // One resident round of split workers on the current device (bf16 or fp8 pool), or < 0.
 int decode_workers(int d, bool fp8 = false);
 hipError_t launch_decode(const DecArgs& a, int d, hipStream_t stream);

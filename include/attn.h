@@ -178,6 +178,23 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Lq, int Lk, int d,
              int causal, int window, float scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/* attn_decode for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, layout, results and status
+ * codes as attn_decode, without the workspace: the decode workspace is a fixed array of
+ * ATTN_DECODE_NOALLOC_BYTES (64 MiB) inside the library, one per GPU, which that GPU holds until
+ * the process ends.  A call whose attn_decode_workspace_size(...) exceeds it returns
+ * ATTN_ERR_WORKSPACE before any device work (at Hq = 32, d = 128: up to about 1900 sequences).
+ * The call allocates nothing and calls no allocating routine; its device address is looked up
+ * on its first call on each device (ATTN_ERR_HIP if the runtime refuses).  Every call on one GPU
+ * shares that GPU's array, whatever the stream: calls that overlap in time on one GPU race and
+ * their results are undefined; calls in order on one stream, or separated by synchronisation,
+ * are independent (nothing in the array needs to start at zero). */
+#define ATTN_DECODE_NOALLOC_BYTES ((size_t)64 << 20)
+int attn_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                        const int64_t* offsets, const int32_t* lens, void* o, float* lse,
+                        int n_seq, int Hq, int Hkv, int d, int64_t pool_rows, int max_len, int window,
+                        float scale, void* stream);
+
 /* attn_decode over an FP8 KV cache: k_pool and v_pool [pool_rows, Hkv, d] hold 8-bit codes of
  * format kv_format (one byte per element, same layout as the bf16 pools), with one scale per pool:
  * the key is k_scale * K(code), the value v_scale * V(code) (k_scale, v_scale finite and > 0).

@@ -509,6 +509,26 @@ def test_decode_rows_read_only_their_own_heads(Hq, Hkv):
     assert last_row_read < n_seq * Hq
 
 
+def test_decode_noalloc_refuses_calls_beyond_its_workspace():
+    """attn_decode_noalloc refuses, before any device work, a call whose workspace would exceed the
+    library's fixed ATTN_DECODE_NOALLOC_BYTES, and validates its arguments as attn_decode does."""
+    L = af.lib()
+
+    def call(n_seq=4, Hq=32, Hkv=8, d=128, max_len=100, offs=P, q=P):
+        return L.attn_decode_noalloc(q, P, P, offs, P, P, None, n_seq, Hq, Hkv, d, 1 << 20, max_len, 0, 0.1, None)
+
+    need = af.decode_workspace_size(3000, 32, 8, 128, 100)
+    assert need > af.DECODE_NOALLOC_BYTES
+    assert call(n_seq=3000) == af.ATTN_ERR_WORKSPACE
+    assert af.decode_workspace_size(64, 32, 1, 128, 32768) <= af.DECODE_NOALLOC_BYTES  # the named MQA batch fits
+    assert af.decode_workspace_size(64, 32, 8, 128, 32768) <= af.DECODE_NOALLOC_BYTES
+    assert call(offs=None) == af.ATTN_ERR_NULL
+    assert call(q=None) == af.ATTN_ERR_NULL
+    assert call(Hq=6, Hkv=4) == af.ATTN_ERR_SHAPE
+    assert call(d=96) == af.ATTN_ERR_UNSUPPORTED
+    assert call(q=MISALIGNED) == af.ATTN_ERR_UNSUPPORTED
+
+
 def test_probe_rejects_bad_arguments():
     L = af.lib()
     assert L.attn_probe_mfma_ceiling(768, 10, None, 1 << 20, None) == af.ATTN_ERR_NULL
