@@ -56,7 +56,7 @@ def lib() -> ctypes.CDLL:
     L.attn_decode.restype = i32
     L.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, i32, f32, vp]
     L.attn_decode_noalloc.restype = i32
-    L.attn_probe_mfma_ceiling.argtypes = [i32, i32, vp, sz, vp]
+    L.attn_probe_mfma_ceiling.argtypes = [i32, i32, i32, vp, sz, vp]
     L.attn_probe_mfma_ceiling.restype = i32
     L.attn_decode_paged.argtypes = [vp, vp, vp, vp, i32, i32, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                                     vp, sz, vp]
@@ -393,14 +393,15 @@ def attn_decode_paged(q, k_pool, v_pool, block_table, lens, *, page_size: int, m
     return (o, lse) if return_lse else o
 
 
-def probe_mfma_ceiling(workgroups: int, steps: int, sink) -> None:
-    """Enqueue the matrix-core ceiling probe (include/attn_probe.h) on the current stream of the
-    sink's GPU; ``sink`` is a float32 device tensor of at least workgroups * 256 elements."""
+def probe_mfma_ceiling(workgroups: int, steps: int, sink, mode: int = 1) -> None:
+    """Enqueue the matrix-core ceiling probe (include/attn_probe.h; mode 0: MFMAs alone, 1: with
+    LDS operands, 2: with the softmax's vector work too) on the current stream of the sink's GPU;
+    ``sink`` is a float32 device tensor of at least workgroups * 256 elements."""
     import torch
     dev = _require_gpu(sink)
     if sink.dtype != torch.float32:
         raise ValueError("sink must be float32")
-    _run(dev, lib().attn_probe_mfma_ceiling, int(workgroups), int(steps), sink.data_ptr(), sink.numel() * 4)
+    _run(dev, lib().attn_probe_mfma_ceiling, int(mode), int(workgroups), int(steps), sink.data_ptr(), sink.numel() * 4)
 
 
 def fwd_plan(B, Hq, Hkv, Lq, Lk, d, causal=False, window=0, f32=False) -> dict:

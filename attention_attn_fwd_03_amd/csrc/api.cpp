@@ -481,11 +481,12 @@ int attn_decode_plan(int n_seq, int Hq, int Hkv, int d, int32_t* teams, int32_t*
   return ATTN_OK;
 }
 
-int attn_probe_mfma_ceiling(int workgroups, int steps, float* sink, size_t sink_bytes, void* stream) {
+int attn_probe_mfma_ceiling(int mode, int workgroups, int steps, float* sink, size_t sink_bytes, void* stream) {
   if (!sink) return ATTN_ERR_NULL;
   if (workgroups <= 0 || steps <= 0) return ATTN_ERR_SHAPE;
+  if (mode < 0 || mode > 2) return ATTN_ERR_UNSUPPORTED;
   if (sink_bytes < (size_t)workgroups * 256 * sizeof(float)) return ATTN_ERR_WORKSPACE;
-  const hipError_t e = launch_probe_mfma(workgroups, steps, sink, reinterpret_cast<hipStream_t>(stream));
+  const hipError_t e = launch_probe_mfma(mode, workgroups, steps, sink, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

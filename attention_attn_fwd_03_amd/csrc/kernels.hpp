@@ -116,7 +116,8 @@ hipError_t launch_decode(const DecArgs& a, int d, hipStream_t stream);
 hipError_t launch_backward(const BwdArgs& a, int d, hipStream_t stream);
 
 // Matrix-core ceiling probe (probe.hip): `workgroups` workgroups of four waves, each running
-// `steps` 32-key steps of the prefill loop's MFMA and LDS work; sink holds workgroups * 256 floats.
-hipError_t launch_probe_mfma(int workgroups, int steps, float* sink, hipStream_t stream);
+// `steps` 32-key steps of the prefill loop's MFMA work (mode 0), with its LDS operand reads
+// (mode 1), and with the softmax's vector work (mode 2); sink holds workgroups * 256 floats.
+hipError_t launch_probe_mfma(int mode, int workgroups, int steps, float* sink, hipStream_t stream);
 
 }  // namespace attnfwd

@@ -1,11 +1,16 @@
-// Measurement probe: the matrix-core ceiling of the prefill kernel's inner loop on this part.
+// Measurement probe: the ceilings of the prefill kernel's inner loop on this part.
 //
 // Same launch shape as fwd_bf16_kernel<128, 32, false, *> (256 threads, three workgroups per CU,
-// two 19 KB LDS stages), and per 32-key step the same matrix work and LDS operand reads: eight
-// v_mfma_f32_32x32x16_bf16 of S^T = K Q^T with K read from LDS, then eight of O^T = V^T P^T with
-// V^T read by ds_read_b64_tr_b16.  No softmax, no global loads, no barrier: how many FLOP/s the
-// matrix cores and LDS alone sustain under the part's power limit, the ceiling against which the
-// prefill kernel's own fraction of the nominal peak is read.
+// two 19 KB LDS stages), and per 32-key step the same matrix work: eight v_mfma_f32_32x32x16_bf16
+// of S^T = K Q^T, then eight of O^T = V^T P^T.  Three modes, each adding one part of the kernel's
+// work, none with global loads, barriers or dependency waits on memory:
+//   0  the matrix instructions alone, operands in registers;
+//   1  with the operands read from LDS as the kernel reads them (K rows, V^T by ds_read_b64_tr_b16);
+//   2  mode 1 plus the softmax's vector work per step: a 16-value row maximum (max3), one fma, one
+//      exp2 and one add per score, the bf16 packing of P.
+// Under sustained matrix load the part runs at its power limit, so these measure how many FLOP/s
+// the matrix cores sustain with each part of the kernel's energy added: the ceilings against which
+// the prefill kernel's own fraction of the nominal peak is read.
 #include <hip/hip_runtime.h>
 
 #include "attn_device.hpp"
@@ -18,6 +23,7 @@ constexpr int kProbeD = 128, kProbeKpb = kProbeD * 2 + 16, kProbeVpb = kProbeD *
 constexpr int kProbeKTile = 9216, kProbeVTile = 10240;  // the prefill kernel's stage sizes at d = 128
 }  // namespace
 
+template <int MODE>
 __global__ __launch_bounds__(256, 3) void probe_mfma_lds_kernel(int steps, float* sink) {
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds[2][kProbeKTile];
   __shared__ __attribute__((aligned(1024))) unsigned char v_lds[2][kProbeVTile];
@@ -42,16 +48,50 @@ __global__ __launch_bounds__(256, 3) void probe_mfma_lds_kernel(int steps, float
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
   const int k_lane = col * kProbeKpb + h * 16;
   const int v_lane = (4 * h + ((lane & 15) >> 2)) * kProbeVpb + ((lane >> 4) & 1) * 32 + (lane & 3) * 8;
+  // mode 0: operands held in registers for the whole loop
+  bf16x8 kreg[kProbeD / 16], vreg[kProbeD / 32][2];
+#pragma unroll
+  for (int ks = 0; ks < kProbeD / 16; ++ks) kreg[ks] = *(const bf16x8*)(k_lds[0] + k_lane + ks * 32);
+#pragma unroll
+  for (int dt = 0; dt < kProbeD / 32; ++dt)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const unsigned char* Vs = v_lds[0] + v_lane;
+      const u32x2 r0 = lds_read_tr16(Vs + 16 * half * kProbeVpb + dt * 64);
+      const u32x2 r1 = lds_read_tr16(Vs + (16 * half + 8) * kProbeVpb + dt * 64);
+      vreg[dt][half] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3));
+    }
+  float lsum = 0.f, mref = 0.f;
   for (int step = 0; step < steps; ++step) {
     const int st = step & 1;
     f32x16 s = {};
     const unsigned char* Ks = k_lds[st] + k_lane;
 #pragma unroll
-    for (int ks = 0; ks < kProbeD / 16; ++ks) s = mfma_32x32x16(*(const bf16x8*)(Ks + ks * 32), qf[ks], s);
-    // P as bf16, from the scores (one conversion per pair, as the real kernel's packing)
+    for (int ks = 0; ks < kProbeD / 16; ++ks)
+      s = mfma_32x32x16(MODE == 0 ? kreg[ks] : *(const bf16x8*)(Ks + ks * 32), qf[ks], s);
     unsigned pk[8];
+    if constexpr (MODE == 2) {
+      // the softmax's vector work on these scores (values stay small: P <= 2^8)
+      float mx = s[0];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pk[i] = pack_bf16x2(s[2 * i] * (1.f / 256.f), s[2 * i + 1] * (1.f / 256.f));
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+      mx = pair_max(mx);
+      mref = fmaxf(mref, mx * 0.125f);
+      float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[2 * i], 0.125f, -mref));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[2 * i + 1], 0.125f, -mref));
+        l0 += e0;
+        l1 += e1;
+        pk[i] = pack_bf16x2(e0, e1);
+      }
+      lsum += l0 + l1;
+    } else {
+      // P as bf16, from the scores (one conversion per pair, as the kernel's packing)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pk[i] = pack_bf16x2(s[2 * i] * (1.f / 256.f), s[2 * i + 1] * (1.f / 256.f));
+    }
     const unsigned char* Vs = v_lds[st] + v_lane;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -59,20 +99,33 @@ __global__ __launch_bounds__(256, 3) void probe_mfma_lds_kernel(int steps, float
                                                          pk[4 * half + 3]});
 #pragma unroll
       for (int dt = 0; dt < kProbeD / 32; ++dt) {
-        const u32x2 r0 = lds_read_tr16(Vs + 16 * half * kProbeVpb + dt * 64);
-        const u32x2 r1 = lds_read_tr16(Vs + (16 * half + 8) * kProbeVpb + dt * 64);
-        o[dt] = mfma_32x32x16(__builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3)), pb, o[dt]);
+        bf16x8 vf;
+        if constexpr (MODE == 0) {
+          vf = vreg[dt][half];
+        } else {
+          const u32x2 r0 = lds_read_tr16(Vs + 16 * half * kProbeVpb + dt * 64);
+          const u32x2 r1 = lds_read_tr16(Vs + (16 * half + 8) * kProbeVpb + dt * 64);
+          vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3));
+        }
+        o[dt] = mfma_32x32x16(vf, pb, o[dt]);
       }
     }
   }
-  float acc = 0.f;
+  float acc = lsum;
   for (int dt = 0; dt < kProbeD / 32; ++dt)
     for (int i = 0; i < 16; ++i) acc += o[dt][i];
   sink[(size_t)blockIdx.x * 256 + tid] = acc;
 }
 
-hipError_t launch_probe_mfma(int workgroups, int steps, float* sink, hipStream_t stream) {
-  hipLaunchKernelGGL(probe_mfma_lds_kernel, dim3((unsigned)workgroups), dim3(256), 0, stream, steps, sink);
+template __global__ void probe_mfma_lds_kernel<0>(int, float*);
+template __global__ void probe_mfma_lds_kernel<1>(int, float*);
+template __global__ void probe_mfma_lds_kernel<2>(int, float*);
+
+hipError_t launch_probe_mfma(int mode, int workgroups, int steps, float* sink, hipStream_t stream) {
+  const dim3 g((unsigned)workgroups), b(256);
+  if (mode == 0) hipLaunchKernelGGL(probe_mfma_lds_kernel<0>, g, b, 0, stream, steps, sink);
+  else if (mode == 1) hipLaunchKernelGGL(probe_mfma_lds_kernel<1>, g, b, 0, stream, steps, sink);
+  else hipLaunchKernelGGL(probe_mfma_lds_kernel<2>, g, b, 0, stream, steps, sink);
   return hipGetLastError();
 }
 

@@ -233,30 +233,33 @@ MQA_REPLICAS = 4  # 4 x 0.62 GB of MQA pools: well past the 256 MB last-level ca
 
 
 def mfma_ceiling(args):
-    """The ceiling probe: 768 workgroups (one per slot: three per CU), timed over several launches
-    of `steps` 32-key steps each, as TFLOP/s and as a fraction of the nominal bf16 peak."""
+    """The ceiling probe in its three modes (matrix instructions alone, with LDS operands, with the
+    softmax's vector work too): 768 workgroups (three per CU), timed over several launches of
+    `steps` 32-key steps each, as TFLOP/s and as a fraction of the nominal bf16 peak."""
     import torch
     import attention_attn_fwd_03_amd as af
     wgs, steps = 768, 4096
     sink = torch.empty(wgs * 256, device="cuda", dtype=torch.float32)
-    for _ in range(3):
-        af.probe_mfma_ceiling(wgs, steps, sink)
-    torch.cuda.synchronize()
-    ev = _events(2)
-    reps = 10
-    ev[0].record()
-    for _ in range(reps):
-        af.probe_mfma_ceiling(wgs, steps, sink)
-    ev[1].record()
-    torch.cuda.synchronize()
-    ms = ev[0].elapsed_time(ev[1]) / reps
-    flops = wgs * 4 * steps * 16 * 2 * 32 * 32 * 16
-    tf = flops / (ms * 1e-3) / 1e12
-    print(json.dumps({"probe": "mfma_lds_ceiling", "workgroups": wgs, "steps": steps, "ms_per_launch": round(ms, 4),
-                      "TFLOP/s": round(tf, 1), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                      "peak_TFLOP/s": PEAK_BF16_TFLOPS,
-                      "what": "16 bf16 32x32x16 MFMAs per 32-key step with K / V^T operands from LDS, the "
-                              "prefill kernel's launch shape, no softmax and no global loads"}), flush=True)
+    what = {0: "MFMAs alone, operands in registers", 1: "MFMAs with K / V^T operands read from LDS",
+            2: "MFMAs, LDS operands and the softmax's vector work (max, fma, exp2, add, bf16 pack)"}
+    for mode in (0, 1, 2):
+        for _ in range(3):
+            af.probe_mfma_ceiling(wgs, steps, sink, mode=mode)
+        torch.cuda.synchronize()
+        ev = _events(2)
+        reps = 10
+        ev[0].record()
+        for _ in range(reps):
+            af.probe_mfma_ceiling(wgs, steps, sink, mode=mode)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / reps
+        flops = wgs * 4 * steps * 16 * 2 * 32 * 32 * 16
+        tf = flops / (ms * 1e-3) / 1e12
+        print(json.dumps({"probe": "mfma_ceiling", "mode": mode, "what": what[mode], "workgroups": wgs,
+                          "steps": steps, "ms_per_launch": round(ms, 4), "TFLOP/s": round(tf, 1),
+                          "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4), "peak_TFLOP/s": PEAK_BF16_TFLOPS}),
+              flush=True)
 
 
 def main():

@@ -16,13 +16,17 @@ extern "C" {
 
 /* Launch `workgroups` workgroups shaped like the d = 128 prefill kernel's (256 threads, three per
  * CU, the same two LDS stages), each of whose four waves runs `steps` steps of that kernel's
- * matrix work and LDS operand reads: 16 v_mfma_f32_32x32x16_bf16 per step (2 * 32 * 32 * 16 *
- * 16 = 524288 FLOP per wave), eight with A from LDS, eight with A read transposed from LDS, and
- * nothing else (no softmax, no global loads, no barriers).  sink: device memory of at least
- * workgroups * 256 floats, overwritten (keeps the results live).  Enqueued on `stream`; the
- * caller times it.  Status codes as attn.h: ATTN_ERR_NULL, ATTN_ERR_SHAPE (a count <= 0),
+ * matrix work: 16 v_mfma_f32_32x32x16_bf16 per step (2 * 32 * 32 * 16 * 16 = 524288 FLOP per
+ * wave), and, by `mode`:
+ *   0  nothing else (operands held in registers);
+ *   1  the operand reads from LDS (K rows for S^T = K Q^T, V^T by ds_read_b64_tr_b16);
+ *   2  mode 1 plus the softmax's vector work per step (row maximum, one fma, exp2 and add per
+ *      score, bf16 packing of P).
+ * No global loads, no barriers.  sink: device memory of at least workgroups * 256 floats,
+ * overwritten (keeps the results live).  Enqueued on `stream`; the caller times it.  Status codes
+ * as attn.h: ATTN_ERR_NULL, ATTN_ERR_SHAPE (a count <= 0), ATTN_ERR_UNSUPPORTED (mode not 0-2),
  * ATTN_ERR_WORKSPACE (sink too small), ATTN_ERR_HIP. */
-int attn_probe_mfma_ceiling(int workgroups, int steps, float* sink, size_t sink_bytes, void* stream);
+int attn_probe_mfma_ceiling(int mode, int workgroups, int steps, float* sink, size_t sink_bytes, void* stream);
 
 #ifdef __cplusplus
 }

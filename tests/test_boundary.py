@@ -531,7 +531,8 @@ def test_decode_noalloc_refuses_calls_beyond_its_workspace():
 
 def test_probe_rejects_bad_arguments():
     L = af.lib()
-    assert L.attn_probe_mfma_ceiling(768, 10, None, 1 << 20, None) == af.ATTN_ERR_NULL
-    assert L.attn_probe_mfma_ceiling(0, 10, P, 1 << 20, None) == af.ATTN_ERR_SHAPE
-    assert L.attn_probe_mfma_ceiling(768, 0, P, 1 << 20, None) == af.ATTN_ERR_SHAPE
-    assert L.attn_probe_mfma_ceiling(768, 10, P, 768 * 256 * 4 - 4, None) == af.ATTN_ERR_WORKSPACE
+    assert L.attn_probe_mfma_ceiling(1, 768, 10, None, 1 << 20, None) == af.ATTN_ERR_NULL
+    assert L.attn_probe_mfma_ceiling(1, 0, 10, P, 1 << 20, None) == af.ATTN_ERR_SHAPE
+    assert L.attn_probe_mfma_ceiling(1, 768, 0, P, 1 << 20, None) == af.ATTN_ERR_SHAPE
+    assert L.attn_probe_mfma_ceiling(3, 768, 10, P, 1 << 20, None) == af.ATTN_ERR_UNSUPPORTED
+    assert L.attn_probe_mfma_ceiling(1, 768, 10, P, 768 * 256 * 4 - 4, None) == af.ATTN_ERR_WORKSPACE
