@@ -13,7 +13,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libattnfwd.so")
+# ATTNFWD_LIB names another build of the same C ABI (the host-only sanitizer build the CPU tests
+# make); by default the in-tree library.
+LIB_PATH = os.environ.get("ATTNFWD_LIB") or os.path.join(_HERE, "libattnfwd.so")
 
 ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(6)
 KV_FORMATS = {"e4m3fn": 1, "e5m2": 2}  # attn_kv_format

@@ -564,19 +564,6 @@ template __global__ void decode_merge_kernel<128, false>(DecArgs);
 template __global__ void decode_merge_kernel<64, true>(DecArgs);
 template __global__ void decode_merge_kernel<128, true>(DecArgs);
 
-DecWorkspaceLayout decode_workspace_layout(int n_seq, int Hq, int Hkv, int d) {
-  const size_t slots = (size_t)decode_max_slots(n_seq, decode_rows_per_seq(Hq, Hkv));
-  const size_t nh = (size_t)decode_heads_per_slot(Hq, Hkv);
-  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  DecWorkspaceLayout l;
-  l.share = 0;
-  l.prefix = 256;
-  l.ml = l.prefix + up(sizeof(int) * ((size_t)n_seq + 1));
-  l.o = l.ml + up(slots * nh * 2 * sizeof(float));
-  l.total = l.o + slots * nh * (size_t)d * sizeof(float);
-  return l;
-}
-
 // Workspace of attn_decode_noalloc, for callers that cannot allocate device memory: a fixed array
 // in the library's code object.  Each GPU the library runs on holds its own copy (at its own
 // address) until the process ends.  Host code never uses the array's name as an address; the

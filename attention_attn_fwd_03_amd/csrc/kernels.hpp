@@ -91,10 +91,6 @@ struct BwdArgs {
   int heads_per_xcd;  // dQ block order, as the forward's (plan.hpp)
 };
 
-struct DecWorkspaceLayout {
-  size_t share, prefix, ml, o, total;  // byte offsets of each region, and the size
-};
-DecWorkspaceLayout decode_workspace_layout(int n_seq, int Hq, int Hkv, int d);
 
 int prefill_block_q(bool f32);
 int prefill_block_k(bool f32, int d);

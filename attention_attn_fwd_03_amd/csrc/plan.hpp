@@ -10,6 +10,7 @@
 // invisible pairs are masked ("003-注意力机制详解…", §三.2: compute the band, do not build the
 // full matrix and mask it).
 #pragma once
+#include <stddef.h>
 #include <stdint.h>
 
 #if defined(__HIPCC__)
@@ -230,6 +231,25 @@ ATTN_HD int decode_key_blocks(int n, int window, int tokens_per_block, int align
 }
 ATTN_HD long long decode_max_slots(int n_seq, int rows_per_seq) {
   return (long long)rows_per_seq * (decode_teams(kDecodeMaxWorkers, rows_per_seq) + n_seq);
+}
+
+// Decode workspace (host side): the blocks-per-team share (one int, 256-byte region), the
+// exclusive prefix of per-sequence block counts (n_seq + 1 ints), then for every partial slot
+// the (m, l) pair and the unnormalised fp32 O of its query heads.
+struct DecWorkspaceLayout {
+  size_t share, prefix, ml, o, total;  // byte offsets of each region, and the size
+};
+inline DecWorkspaceLayout decode_workspace_layout(int n_seq, int Hq, int Hkv, int d) {
+  const size_t slots = (size_t)decode_max_slots(n_seq, decode_rows_per_seq(Hq, Hkv));
+  const size_t nh = (size_t)decode_heads_per_slot(Hq, Hkv);
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  DecWorkspaceLayout l;
+  l.share = 0;
+  l.prefix = 256;
+  l.ml = l.prefix + up(sizeof(int) * ((size_t)n_seq + 1));
+  l.o = l.ml + up(slots * nh * 2 * sizeof(float));
+  l.total = l.o + slots * nh * (size_t)d * sizeof(float);
+  return l;
 }
 
 }  // namespace attnfwd
