@@ -188,7 +188,7 @@ int decode_common(const void* q, const void* k_pool, const void* v_pool, const i
   }
   if (workspace == nullptr || workspace_bytes < lay.total) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_UNSUPPORTED;
-  const int workers = decode_workers(d, a.kv_fmt != 0);
+  const int workers = decode_workers(d, a.kv_fmt != 0, decode_pack(Hq, Hkv) > 1);
   if (workers <= 0) return ATTN_ERR_HIP;
 
   a.q = q;
@@ -473,7 +473,7 @@ int attn_decode_plan(int n_seq, int Hq, int Hkv, int d, int32_t* teams, int32_t*
   if (!teams || !rows_per_seq || !tokens_per_block) return ATTN_ERR_NULL;
   if (n_seq <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  const int workers = decode_workers(d);
+  const int workers = decode_workers(d, false, decode_pack(Hq, Hkv) > 1);
   if (workers <= 0) return ATTN_ERR_HIP;
   *rows_per_seq = decode_rows_per_seq(Hq, Hkv);
   *tokens_per_block = decode_tokens_per_block(Hq, Hkv);

@@ -452,94 +452,133 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
 // One 64-lane workgroup per (query head, sequence).  Lane j holds piece j's (m, l) (64 pieces at a
 // time); the maximum and the sum of weights come from wave reductions; each lane accumulates
 // D/64 output columns over the pieces, the piece weight broadcast from the lane that holds it.
-// The partial O rows are fetched MB pieces at a time, all loads of a batch issued before any of
-// them is used, so a sequence with few pieces costs about two memory round trips.
-template <int D, bool PACKED>
+// The kernel is two memory round trips with no branch around a load: the sequence's length and
+// offset and the split's share and prefix (scalar loads, all issued together), then the pieces'
+// (m, l) and the O slices of the first MB pieces (unconditional loads at clamped piece indices,
+// whose surplus values are dropped by selects).
+// Wave-wide maximum and sum in VALU steps: within each 16-lane row by DPP (swap neighbours, swap
+// pairs, mirror halves of 8, mirror the row), then across the four rows by readlane.
+#define ATTN_DPP(v, ctrl) \
+  __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (v)), (ctrl), 0xF, 0xF, false))
+__device__ __forceinline__ float wave_max_f(float x) {
+  x = fmaxf(x, ATTN_DPP(x, 0xB1));   // quad_perm [1, 0, 3, 2]
+  x = fmaxf(x, ATTN_DPP(x, 0x4E));   // quad_perm [2, 3, 0, 1]
+  x = fmaxf(x, ATTN_DPP(x, 0x141));  // row_half_mirror
+  x = fmaxf(x, ATTN_DPP(x, 0x140));  // row_mirror
+  const int b = __builtin_bit_cast(int, x);
+  return fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)),
+                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))),
+               fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)),
+                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48))));
+}
+__device__ __forceinline__ float wave_sum_f(float x) {
+  x += ATTN_DPP(x, 0xB1);
+  x += ATTN_DPP(x, 0x4E);
+  x += ATTN_DPP(x, 0x141);
+  x += ATTN_DPP(x, 0x140);
+  const int b = __builtin_bit_cast(int, x);
+  return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))) +
+         (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48)));
+}
+#undef ATTN_DPP
+
+template <int PER>
+__device__ __forceinline__ void load_slice(const float* p, float (&v)[PER]) {
+  if constexpr (PER == 2) {
+    const f32x2 w = *(const f32x2*)p;
+    v[0] = w.x;
+    v[1] = w.y;
+  } else {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) v[e] = p[e];
+  }
+}
+
+template <int D, bool PACKED, bool PAGED>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
   constexpr int PER = D / 64;
   constexpr int MB = 16;
   const int hq = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
-  // Independent loads first: one memory round trip for all of them.
-  const int n = a.lens[s];
-  const int64_t base = a.paged ? 0 : a.offsets[s];
-  const int share = a.ws_share[0];
-  const int p0 = a.ws_prefix[s];
-  unsigned short* O = (unsigned short*)a.o + ((size_t)s * a.Hq + hq) * D;
-  if (!decode_seq_valid(a, n, base, a.paged)) {
-    const __bf16 nanb = (__bf16)NAN;
-    for (int e = 0; e < PER; ++e) O[lane * PER + e] = __builtin_bit_cast(unsigned short, nanb);
-    if (a.lse != nullptr && lane == 0) a.lse[(size_t)s * a.Hq + hq] = NAN;
-    return;
-  }
-  const int nb = decode_key_blocks(n, a.window, a.tpb, a.paged);
+  // Wave-uniform and constant while the merge runs (the split kernel before it wrote the share and
+  // the prefix): through the scalar cache, none of them behind a branch.
+  const int n = kernel_constant(a.lens)[s];
+  const int64_t base = PAGED ? 0 : kernel_constant(a.offsets)[s];
+  const int share = kernel_constant(a.ws_share)[0];
+  const int p0 = kernel_constant(a.ws_prefix)[s];
+  const bool valid = decode_seq_valid(a, n, base, PAGED);  // else the outputs become NaN
+  const int nb = valid ? decode_key_blocks(n, a.window, a.tpb, PAGED) : 0;
   const int kvh = hq / a.group, within = hq % a.group;
   // Slot row and column of this query head: one row holding every head in the packed layout,
   // else row (KV head, block of 32 heads).
   const int u = PACKED ? 0 : kvh * a.hblocks + within / 32;
   const int col = PACKED ? hq : within % 32;
+  // Teams t0 .. t0 + np - 1 met this sequence; piece j is slot (t0 + j + s) * rows + u, head col.
+  const int sh = share > 0 ? share : 1;
+  const int t0 = p0 / sh;
+  const int np = nb > 0 ? (p0 + nb - 1) / sh - t0 + 1 : 0;
+  const size_t idx0 = ((size_t)(t0 + s) * a.rows + u) * a.nh + col;
+  const size_t step = (size_t)a.rows * a.nh;
+  const float* wo0 = a.ws_o + idx0 * D + lane * PER;
 
   float M = -INFINITY, L = 0.f;
-  bool bad = false;  // a piece read a page entry outside the pool (its m is NaN)
+  bool bad = !valid;  // also set when a piece read a page entry outside the pool (its m is NaN)
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  if (nb > 0) {
-    const int t0 = p0 / share;
-    const int np = (p0 + nb - 1) / share - t0 + 1;  // teams whose share meets this sequence
-    // Partial index of piece j: slot (t0 + j + s) * rows + u, head col.
-    const size_t idx0 = ((size_t)(t0 + s) * a.rows + u) * a.nh + col;
-    const size_t step = (size_t)a.rows * a.nh;
-    const float* wo0 = a.ws_o + idx0 * D + lane * PER;
-    for (int j0 = 0; j0 < np; j0 += 64) {
-      const int cnt = np - j0 < 64 ? np - j0 : 64;
-      // (m, l) of piece j0 + lane, and the O rows of the first MB pieces, in one round trip.
-      float mj = -INFINITY, lj = 0.f;
-      if (lane < cnt) {
-        const size_t idx = idx0 + (size_t)(j0 + lane) * step;
-        mj = a.ws_ml[2 * idx];
-        lj = a.ws_ml[2 * idx + 1];
+  for (int j0 = 0; j0 < np; j0 += 64) {
+    const int cnt = np - j0 < 64 ? np - j0 : 64;
+    const int jl = lane < cnt ? lane : cnt - 1;
+    const f32x2 ml = *(const f32x2*)(a.ws_ml + 2 * (idx0 + (size_t)(j0 + jl) * step));
+    float ov[MB][PER];
+    auto fetch = [&](int jb) {
+#pragma unroll
+      for (int jj = 0; jj < MB; ++jj) {
+        const int jc = jb + jj < cnt ? jb + jj : cnt - 1;
+        load_slice<PER>(wo0 + (size_t)(j0 + jc) * step * D, ov[jj]);
       }
-      float ov[MB][PER];
 #pragma unroll
       for (int jj = 0; jj < MB; ++jj)
 #pragma unroll
-        for (int e = 0; e < PER; ++e) ov[jj][e] = jj < cnt ? wo0[((size_t)(j0 + jj) * step) * D + e] : 0.f;
-      // Rescale what is accumulated so far to the new maximum, then add these pieces.
-      if (__builtin_amdgcn_ballot_w64(lane < cnt && __builtin_isnan(mj)) != 0) bad = true;
-      float Mc = mj;
+        for (int e = 0; e < PER; ++e) ov[jj][e] = jb + jj < cnt ? ov[jj][e] : 0.f;
+    };
+    fetch(0);
+    // Keep the first batch's loads next to the (m, l) load (one round trip for both) rather than
+    // behind the reductions that follow.
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) Mc = fmaxf(Mc, __shfl_xor(Mc, off));
-      const float Mn = fmaxf(M, Mc);
-      if (Mn != -INFINITY) {
-        const float alpha = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-        L *= alpha;
+    for (int jj = 0; jj < MB; ++jj)
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] *= alpha;
-        M = Mn;
-        const float w = lane < cnt ? __builtin_amdgcn_exp2f(mj - M) : 0.f;
-        L += w * lj;
-        for (int jb = 0; jb < cnt; jb += MB) {
-          if (jb > 0) {
+      for (int e = 0; e < PER; ++e) asm volatile("" : "+v"(ov[jj][e]));
+    const float mj = lane < cnt ? ml.x : -INFINITY;
+    const float lj = lane < cnt ? ml.y : 0.f;
+    // Rescale what is accumulated so far to the new maximum, then add these pieces.
+    if (__builtin_amdgcn_ballot_w64(__builtin_isnan(mj)) != 0) bad = true;
+    const float Mn = fmaxf(M, wave_max_f(mj));
+    if (Mn != -INFINITY) {
+      const float alpha = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+      L *= alpha;
 #pragma unroll
-            for (int jj = 0; jj < MB; ++jj)
+      for (int e = 0; e < PER; ++e) acc[e] *= alpha;
+      M = Mn;
+      const float w = lane < cnt ? __builtin_amdgcn_exp2f(mj - M) : 0.f;
+      L += w * lj;
+      for (int jb = 0; jb < cnt; jb += MB) {
+        if (jb > 0) fetch(jb);
 #pragma unroll
-              for (int e = 0; e < PER; ++e)
-                ov[jj][e] = jb + jj < cnt ? wo0[((size_t)(j0 + jb + jj) * step) * D + e] : 0.f;
-          }
+        for (int jj = 0; jj < MB; ++jj) {
+          const float wj =
+              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), (jb + jj) & 63));
 #pragma unroll
-          for (int jj = 0; jj < MB; ++jj) {
-            const float wj =
-                __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), (jb + jj) & 63));
-#pragma unroll
-            for (int e = 0; e < PER; ++e) acc[e] += wj * ov[jj][e];
-          }
+          for (int e = 0; e < PER; ++e) acc[e] += wj * ov[jj][e];
         }
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
   }
+  L = wave_sum_f(L);
   const float inv = L > 0.f ? 1.f / L : 0.f;
+  unsigned short* O = (unsigned short*)a.o + ((size_t)s * a.Hq + hq) * D;
+#pragma unroll
   for (int e = 0; e < PER; ++e)
     O[lane * PER + e] = __builtin_bit_cast(unsigned short, (__bf16)(bad ? NAN : acc[e] * inv));
   if (a.lse != nullptr && lane == 0)
@@ -559,10 +598,14 @@ ATTN_DECODE_VARIANTS(kKvBf16)
 ATTN_DECODE_VARIANTS(kKvE4M3)
 ATTN_DECODE_VARIANTS(kKvE5M2)
 #undef ATTN_DECODE_VARIANTS
-template __global__ void decode_merge_kernel<64, false>(DecArgs);
-template __global__ void decode_merge_kernel<128, false>(DecArgs);
-template __global__ void decode_merge_kernel<64, true>(DecArgs);
-template __global__ void decode_merge_kernel<128, true>(DecArgs);
+template __global__ void decode_merge_kernel<64, false, false>(DecArgs);
+template __global__ void decode_merge_kernel<128, false, false>(DecArgs);
+template __global__ void decode_merge_kernel<64, true, false>(DecArgs);
+template __global__ void decode_merge_kernel<128, true, false>(DecArgs);
+template __global__ void decode_merge_kernel<64, false, true>(DecArgs);
+template __global__ void decode_merge_kernel<128, false, true>(DecArgs);
+template __global__ void decode_merge_kernel<64, true, true>(DecArgs);
+template __global__ void decode_merge_kernel<128, true, true>(DecArgs);
 
 // Workspace of attn_decode_noalloc, for callers that cannot allocate device memory: a fixed array
 // in the library's code object.  Each GPU the library runs on holds its own copy (at its own
@@ -587,11 +630,11 @@ void* decode_scratch() {
   return p;
 }
 
-int decode_workers(int d, bool fp8) {
-  static std::atomic<int> cache[2][2][64];
+int decode_workers(int d, bool fp8, bool packed) {
+  static std::atomic<int> cache[2][2][2][64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
-  std::atomic<int>& slot = cache[d == 128 ? 1 : 0][fp8 ? 1 : 0][dev];
+  std::atomic<int>& slot = cache[d == 128 ? 1 : 0][fp8 ? 1 : 0][packed ? 1 : 0][dev];
   int w = slot.load(std::memory_order_relaxed);
   if (w > 0) return w;
   int cus = 0, per_cu = 0;
@@ -606,7 +649,7 @@ int decode_workers(int d, bool fp8) {
             ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<128, false, kKvBf16, true>, 64, 0)
             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<64, false, kKvBf16, true>, 64, 0);
   if (e != hipSuccess || cus <= 0 || per_cu <= 0) return -1;
-  const int cap = fp8 ? kDecodeWorkersPerCuFp8 : kDecodeWorkersPerCu;
+  const int cap = fp8 ? kDecodeWorkersPerCuFp8 : packed ? kDecodeWorkersPerCu : kDecodeWorkersPerCuOneHead;
   if (per_cu > cap) per_cu = cap;
   w = cus * per_cu < kDecodeMaxWorkers ? cus * per_cu : kDecodeMaxWorkers;
   slot.store(w, std::memory_order_relaxed);
@@ -634,8 +677,13 @@ void launch_decode_d(const DecArgs& a, hipStream_t stream) {
     launch_split<D, kKvE5M2>(a, g1, stream);
   else
     launch_split<D, kKvBf16>(a, g1, stream);
-  if (a.pack > 1) hipLaunchKernelGGL((decode_merge_kernel<D, true>), g2, dim3(64), 0, stream, a);
-  else hipLaunchKernelGGL((decode_merge_kernel<D, false>), g2, dim3(64), 0, stream, a);
+  if (a.pack > 1) {
+    if (a.paged) hipLaunchKernelGGL((decode_merge_kernel<D, true, true>), g2, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL((decode_merge_kernel<D, true, false>), g2, dim3(64), 0, stream, a);
+  } else {
+    if (a.paged) hipLaunchKernelGGL((decode_merge_kernel<D, false, true>), g2, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL((decode_merge_kernel<D, false, false>), g2, dim3(64), 0, stream, a);
+  }
 }
 
 hipError_t launch_decode(const DecArgs& a, int d, hipStream_t stream) {

@@ -105,8 +105,9 @@ hipError_t launch_prefill_fp8(const FwdArgs& a, int d, int fmt, hipStream_t stre
 constexpr size_t kDecodeScratchBytes = size_t(64) << 20;
 void* decode_scratch();
 
-// One resident round of split workers on the current device (bf16 or fp8 pool), or < 0.
-int decode_workers(int d, bool fp8 = false);
+// One resident round of split workers on the current device for a bf16 or fp8 pool in the packed
+// or one-head block layout (plan.hpp), or < 0.
+int decode_workers(int d, bool fp8, bool packed);
 hipError_t launch_decode(const DecArgs& a, int d, hipStream_t stream);
 
 hipError_t launch_backward(const BwdArgs& a, int d, hipStream_t stream);

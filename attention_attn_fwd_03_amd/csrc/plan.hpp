@@ -175,10 +175,13 @@ ATTN_HD PrefillTile prefill_tile_grouped(int bid, int B, int Hq, int Hkv, int n_
 // in at most one team, so slots never collide and at most U * (teams + n_seq) exist.
 constexpr int kDecodeBlockRows = 32;
 constexpr int kDecodeMaxWorkers = 2048;  // workers per launch, at most (one resident round)
-// Workers per CU, at most.  Three single-wave workers per CU stream the pool about 2% faster than
-// four (measured at d = 128, GQA and MQA batches; 2 and 3 per CU both beat 4, and counts that are
-// not a multiple of the CU count load the CUs unevenly and are slower still).
+// Workers per CU, at most.  Packed layout (GQA): three single-wave workers per CU stream the pool
+// about 2% faster than four and 3% faster than two (d = 128; counts that are not a multiple of the
+// CU count load the CUs unevenly and are slower still).  One-head layout (MQA, large groups): two
+// per CU, about 1% faster than three on the MQA batch (fewer partials to write and merge, the
+// stream no slower).
 constexpr int kDecodeWorkersPerCu = 3;
+constexpr int kDecodeWorkersPerCuOneHead = 2;
 // An FP8 pool halves the bytes per block while the per-block work grows (the codes are converted
 // to bf16 in registers): four workers per CU, one per SIMD, are about 9% faster than three on the
 // GQA batch (equal on MQA).

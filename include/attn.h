@@ -260,7 +260,8 @@ int attn_fwd_varlen_schedule(int n_seq, int Hq, int Hkv, int max_seqlen_q, int32
  * for a sequence that is not read) and T = sum of nb(s), the blocks of all sequences laid end
  * to end are cut into shares of ceil(T / teams) blocks; team t computes share t for every row,
  * one partial per (row, sequence) it meets.  ATTN_ERR_HIP without a usable device.  The plan is
- * that of bf16 pools (three workers per CU); FP8 pools (attn_decode_fp8) run four per CU. */
+ * that of bf16 pools (three workers per CU in the packed layout, two in the one-head layout);
+ * FP8 pools (attn_decode_fp8) run four per CU. */
 int attn_decode_plan(int n_seq, int Hq, int Hkv, int d, int32_t* teams, int32_t* rows_per_seq,
                      int32_t* tokens_per_block);
 

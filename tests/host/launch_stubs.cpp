@@ -20,7 +20,7 @@ hipError_t launch_prefill_fp8(const FwdArgs&, int, int, hipStream_t) { return hi
 hipError_t launch_decode(const DecArgs&, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_backward(const BwdArgs&, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_probe_mfma(int, int, int, float*, hipStream_t) { return hipSuccess; }
-int decode_workers(int, bool) { return 768; }
+int decode_workers(int, bool, bool packed) { return packed ? 768 : 512; }
 void* decode_scratch() {
   alignas(256) static unsigned char fake[256];
   return fake;  // never dereferenced: the stubbed launches read nothing
