@@ -156,10 +156,21 @@ def _mfma_counters(path: str) -> dict:
     return out
 
 
-def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, mfma_dir=None) -> dict:
+def _per_counter_means(path: str) -> dict:
+    """rocprofv3 --pmc CSV with several counters -> {kernel name: {counter: mean per dispatch}}."""
+    vals = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            vals.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in vals.items()}
+
+
+def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, mfma_dir=None, mops_dir=None) -> dict:
     """Per-dispatch FETCH_SIZE / WRITE_SIZE of the attention kernels, scaled to bytes with the
     factors a 1 GiB device copy (--copy-calib) gives for the same counters; with `mfma_dir`, also
-    the matrix-core busy fraction and engine clock of each kernel."""
+    the matrix-core busy fraction and engine clock of each kernel; with `mops_dir`, the executed
+    matrix-core work (SQ_INSTS_VALU_MFMA_MOPS_*, units of 512 FLOP) and LDS counters.  `parts`
+    names each part of the step with its workload and kernels."""
     def load(d):
         return _counter_means(os.path.join(d, "run_counter_collection.csv"))
     fetch, write = load(fetch_dir), load(write_dir)
@@ -181,6 +192,12 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, mfm
                                  "read_bytes": int(fb), "write_bytes": int(wb), "traffic_bytes": int(fb + wb)}
         if name in mfma:
             out["kernels"][short].update(mfma[name])
+    if mops_dir:
+        for name, cs in _per_counter_means(os.path.join(mops_dir, "run_counter_collection.csv")).items():
+            short = re.sub(r"^void attnfwd::|\(attnfwd::\w+\)$", "", name)
+            if short in out["kernels"]:
+                out["kernels"][short].update({c: round(v, 1) for c, v in cs.items() if c != "GRBM_GUI_ACTIVE"})
+    out["parts"] = {name: {"workload": w, "kernels": PART_KERNELS[name]} for name, _, w in STEP_PARTS}
     return out
 
 
@@ -223,12 +240,13 @@ STEP_PARTS = [("prefill", "prefill", "gqa_causal_bf16_L4096"),
               ("prefill_window", "prefill", "swa_gqa_bf16_L16384_W4096"),
               ("decode", "decode", "gqa_decode_bf16"),
               ("decode_mqa", "decode", "mqa_decode_bf16")]
-# Kernel names as rocprofv3 reports them (template arguments: head size, key tile, ragged, mask mode;
-# head size, paged, pool format, packed layout), for the counter summary's traffic fields.
+# Kernel names as rocprofv3 reports them, for the counter summary's traffic fields.  Template
+# arguments: prefill (head size, key tile, ragged, mask mode); decode split (head size, paged, pool
+# format, packed layout); decode merge (head size, packed layout, paged).
 PART_KERNELS = {"prefill": ["fwd_bf16_kernel<128, 32, false, 1>"],
                 "prefill_window": ["fwd_bf16_kernel<128, 32, false, 2>"],
-                "decode": ["decode_split_kernel<128, false, 0, true>", "decode_merge_kernel<128, true>"],
-                "decode_mqa": ["decode_split_kernel<128, false, 0, false>", "decode_merge_kernel<128, false>"]}
+                "decode": ["decode_split_kernel<128, false, 0, true>", "decode_merge_kernel<128, true, false>"],
+                "decode_mqa": ["decode_split_kernel<128, false, 0, false>", "decode_merge_kernel<128, false, false>"]}
 MQA_REPLICAS = 4  # 4 x 0.62 GB of MQA pools: well past the 256 MB last-level cache
 
 
@@ -276,12 +294,13 @@ def main():
     ap.add_argument("--workload", default=None, help="with --suite: run only this workload")
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR", default=None,
                     help="rocprofv3 --pmc output dirs: FETCH_SIZE, WRITE_SIZE, both for --copy-calib, "
-                         "and optionally a GRBM_GUI_ACTIVE + SQ_VALU_MFMA_BUSY_CYCLES pass")
+                         "optionally a GRBM_GUI_ACTIVE + SQ_VALU_MFMA_BUSY_CYCLES pass, then a "
+                         "SQ_INSTS_VALU_MFMA_MOPS_* + LDS pass")
     args = ap.parse_args()
 
     if args.summarize_counters:
-        if len(args.summarize_counters) not in (4, 5):
-            ap.error("--summarize-counters takes 4 or 5 directories")
+        if len(args.summarize_counters) not in (4, 5, 6):
+            ap.error("--summarize-counters takes 4 to 6 directories")
         print(json.dumps(summarize_counters(*args.summarize_counters), indent=1))
         return
 
