@@ -25,6 +25,7 @@ EXPORTS = ["attn_fwd", "attn_fwd_f32", "attn_fwd_varlen", "attn_decode_workspace
            "attn_decode_plan", "attn_bwd_workspace_size", "attn_bwd", "attn_decode_fp8", "attn_decode_paged_fp8",
            "attn_fwd_fp8", "attn_decode_rows", "attn_decode_noalloc", "attn_probe_mfma_ceiling"]
 DECODE_NOALLOC_BYTES = 64 << 20  # ATTN_DECODE_NOALLOC_BYTES
+PROBE_SOURCE_BYTES = 64 * (9216 + 10240)  # ATTN_PROBE_SOURCE_BYTES
 
 
 class FwdPlanInfo(ctypes.Structure):
@@ -397,8 +398,10 @@ def attn_decode_paged(q, k_pool, v_pool, block_table, lens, *, page_size: int, m
 
 def probe_mfma_ceiling(workgroups: int, steps: int, sink, mode: int = 1) -> None:
     """Enqueue the matrix-core ceiling probe (include/attn_probe.h; mode 0: MFMAs alone, 1: with
-    LDS operands, 2: with the softmax's vector work too) on the current stream of the sink's GPU;
-    ``sink`` is a float32 device tensor of at least workgroups * 256 elements."""
+    LDS operands, 2: with the softmax's vector work too, 3: with the per-step barrier, 4: with the
+    per-step global->LDS loads) on the current stream of the sink's GPU; ``sink`` is a float32
+    device tensor of at least workgroups * 256 elements, plus PROBE_SOURCE_BYTES / 4 in front
+    (the source blocks) for mode 4."""
     import torch
     dev = _require_gpu(sink)
     if sink.dtype != torch.float32:

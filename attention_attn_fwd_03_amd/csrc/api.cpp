@@ -484,8 +484,10 @@ int attn_decode_plan(int n_seq, int Hq, int Hkv, int d, int32_t* teams, int32_t*
 int attn_probe_mfma_ceiling(int mode, int workgroups, int steps, float* sink, size_t sink_bytes, void* stream) {
   if (!sink) return ATTN_ERR_NULL;
   if (workgroups <= 0 || steps <= 0) return ATTN_ERR_SHAPE;
-  if (mode < 0 || mode > 2) return ATTN_ERR_UNSUPPORTED;
-  if (sink_bytes < (size_t)workgroups * 256 * sizeof(float)) return ATTN_ERR_WORKSPACE;
+  if (mode < 0 || mode > 4) return ATTN_ERR_UNSUPPORTED;
+  if (sink_bytes < (size_t)workgroups * 256 * sizeof(float) + (mode == 4 ? kProbeSrcBytes : 0))
+    return ATTN_ERR_WORKSPACE;
+  static_assert(ATTN_PROBE_SOURCE_BYTES == kProbeSrcBytes, "header and kernel agree on the probe's source size");
   const hipError_t e = launch_probe_mfma(mode, workgroups, steps, sink, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }

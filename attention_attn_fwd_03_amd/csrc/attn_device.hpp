@@ -110,6 +110,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const unsigned short
 struct RowState {
   float m;   // reference maximum, base-2 scaled units (score * |scale| * log2 e); -inf at start
   float l;   // this lane's partial sum of probabilities, relative to m
+  float mb;  // what the exponentials subtract: m, or 0 while m is -inf (a row that has seen no key)
 };
 
 // The online softmax of one tile ("003-注意力机制详解…", §二: new row max, running sum and
@@ -137,6 +138,10 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[NB], int lo, int hi) {
 // Row maximum of the tile; raises the reference maximum (rescaling the running sum and the
 // accumulator) only when the tile's maximum exceeds it by more than kRescaleSlack.  Returns
 // the reference to subtract, with the -inf guard of a row that has seen no key yet.
+// A lane holds half of its row's keys; the row's maximum exceeds the reference by more than the
+// slack exactly when one of the two halves' maxima does (scaling by c > 0 keeps the order, also
+// after rounding), so the lanes test their own halves and the maximum over the lane pair is
+// formed only in the rarely taken branch that raises the reference.
 template <int NB, int ND>
 __device__ __forceinline__ float update_max(const f32x16 (&s)[NB], RowState& st, f32x16 (&o)[ND], float c) {
   float mx = -INFINITY;
@@ -144,18 +149,19 @@ __device__ __forceinline__ float update_max(const f32x16 (&s)[NB], RowState& st,
   for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-  mx = pair_max(mx);
-  const float tmax = (mx == -INFINITY) ? -INFINITY : mx * c;
-  const bool need = tmax > st.m + kRescaleSlack;
-  if (wave_any(need)) {
+  // c > 0 and finite, so a half that saw only masked keys stays at -inf
+  if (wave_any(mx * c > st.m + kRescaleSlack)) {
+    const float tmax = pair_max(mx) * c;
+    const bool need = tmax > st.m + kRescaleSlack;
     const float m_new = need ? tmax : st.m;
     const float alpha = need ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.f;
     st.l *= alpha;
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) o[dt] *= alpha;
     st.m = m_new;
+    st.mb = (m_new == -INFINITY) ? 0.f : m_new;
   }
-  return (st.m == -INFINITY) ? 0.f : st.m;
+  return st.mb;
 }
 
 // Probabilities p = exp2(s * c - mb) of a 32-key block, added to the running sum in fp32 and
@@ -163,9 +169,11 @@ __device__ __forceinline__ float update_max(const f32x16 (&s)[NB], RowState& st,
 // Masked keys hold s = -inf and c > 0, so they give exp2(-inf) = 0 without a select (a zero
 // scale is run as Q = 0 with c = 1, which yields the same all-zero scores).
 __device__ __forceinline__ void exp_block(const f32x16& s, float c, float mb, RowState& st, unsigned (&pk)[8]) {
-  float l0 = 0.f, l1 = 0.f;
+  float l0 = __builtin_amdgcn_exp2f(fmaf(s[0], c, -mb));
+  float l1 = __builtin_amdgcn_exp2f(fmaf(s[1], c, -mb));
+  pk[0] = pack_bf16x2(l0, l1);
 #pragma unroll
-  for (int i = 0; i < 16; i += 2) {
+  for (int i = 2; i < 16; i += 2) {
     const float e0 = __builtin_amdgcn_exp2f(fmaf(s[i], c, -mb));
     const float e1 = __builtin_amdgcn_exp2f(fmaf(s[i + 1], c, -mb));
     l0 += e0;
@@ -177,9 +185,11 @@ __device__ __forceinline__ void exp_block(const f32x16& s, float c, float mb, Ro
 
 // fp32 variant for the fp32 path (P stays fp32).
 __device__ __forceinline__ void exp_block_f32(const f32x16& s, float c, float mb, RowState& st, float (&p)[16]) {
-  float l0 = 0.f, l1 = 0.f;
+  p[0] = __builtin_amdgcn_exp2f(fmaf(s[0], c, -mb));
+  p[1] = __builtin_amdgcn_exp2f(fmaf(s[1], c, -mb));
+  float l0 = p[0], l1 = p[1];
 #pragma unroll
-  for (int i = 0; i < 16; i += 2) {
+  for (int i = 2; i < 16; i += 2) {
     const float e0 = __builtin_amdgcn_exp2f(fmaf(s[i], c, -mb));
     const float e1 = __builtin_amdgcn_exp2f(fmaf(s[i + 1], c, -mb));
     l0 += e0;

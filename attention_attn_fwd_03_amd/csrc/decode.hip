@@ -312,7 +312,7 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-    RowState st = {-INFINITY, 0.f};
+    RowState st = {-INFINITY, 0.f, 0.f};
 
     // Loads of the block starting at token t0 into stage STAGE.  Contiguous pool: a buffer over
     // the piece's remaining tokens.  Paged pool: the block lies inside one page (t0 is a multiple

@@ -115,6 +115,10 @@ hipError_t launch_backward(const BwdArgs& a, int d, hipStream_t stream);
 // Matrix-core ceiling probe (probe.hip): `workgroups` workgroups of four waves, each running
 // `steps` 32-key steps of the prefill loop's MFMA work (mode 0), with its LDS operand reads
 // (mode 1), and with the softmax's vector work (mode 2); sink holds workgroups * 256 floats.
+// Ceiling probe: mode 4 reads its tiles from the first kProbeSrcBytes of the sink (kProbeSrcBlocks
+// blocks of one K and one V stage) and writes its results after them.
+constexpr int kProbeSrcBlocks = 64;
+constexpr size_t kProbeSrcBytes = (size_t)kProbeSrcBlocks * (9216 + 10240);
 hipError_t launch_probe_mfma(int mode, int workgroups, int steps, float* sink, hipStream_t stream);
 
 }  // namespace attnfwd

@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256, 3) void fwd_bf16_kernel(FwdArgs a) {
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-  RowState st = {-INFINITY, 0.f};
+  RowState st = {-INFINITY, 0.f, 0.f};
   const float c = a.c;
 
   // Global -> LDS.  Wave-wide load j of a tile writes 16 bytes per lane at LDS offset
@@ -363,7 +363,7 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
   f32x16 o[D / 32];
   for (int dt = 0; dt < D / 32; ++dt)
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-  RowState st = {-INFINITY, 0.f};
+  RowState st = {-INFINITY, 0.f, 0.f};
 
   float4 kreg[C::LOADS], vreg[C::LOADS];
   auto load_tile = [&](int kt) {

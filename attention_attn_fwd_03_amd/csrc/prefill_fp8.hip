@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256, 3) void fwd_fp8_kernel(FwdArgs a) {
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-  RowState st = {-INFINITY, 0.f};
+  RowState st = {-INFINITY, 0.f, 0.f};
   const float c = a.c;
 
   // Global -> LDS, as the bf16 kernel: wave-wide load j writes 16 bytes per lane at j*1024 +

@@ -6,8 +6,13 @@
 // work, none with global loads, barriers or dependency waits on memory:
 //   0  the matrix instructions alone, operands in registers;
 //   1  with the operands read from LDS as the kernel reads them (K rows, V^T by ds_read_b64_tr_b16);
-//   2  mode 1 plus the softmax's vector work per step: a 16-value row maximum (max3), one fma, one
-//      exp2 and one add per score, the bf16 packing of P.
+//   2  mode 1 plus the softmax's vector work per step as the kernel does it when the reference
+//      maximum stays put: the lane's 16-value maximum (max3) tested against the reference, one
+//      fma, one exp2 and one add per score, the bf16 packing of P;
+//   3  mode 2 plus the kernel's end of step: wait for this wave's loads, workgroup barrier;
+//   4  mode 3 plus the kernel's loads: each step fills the other K and V stages (19 KB) from
+//      global memory by wave-wide global->LDS loads, from one of 64 blocks that stay in L2 (as
+//      the prefill's K/V tiles mostly do: the query tiles of a head read the same keys).
 // Under sustained matrix load the part runs at its power limit, so these measure how many FLOP/s
 // the matrix cores sustain with each part of the kernel's energy added: the ceilings against which
 // the prefill kernel's own fraction of the nominal peak is read.
@@ -22,9 +27,13 @@ namespace {
 constexpr int kProbeD = 128, kProbeKpb = kProbeD * 2 + 16, kProbeVpb = kProbeD * 2 + 64;
 constexpr int kProbeKTile = 9216, kProbeVTile = 10240;  // the prefill kernel's stage sizes at d = 128
 }  // namespace
+static_assert(kProbeSrcBytes == kProbeSrcBlocks * (9216 + 10240), "source blocks of one K and one V stage");
 
 template <int MODE>
 __global__ __launch_bounds__(256, 3) void probe_mfma_lds_kernel(int steps, float* sink) {
+  // mode 4 reads its tiles from the first kProbeSrcBytes of the sink and writes its results after them
+  const unsigned char* src = (const unsigned char*)sink + (blockIdx.x % kProbeSrcBlocks) * (kProbeKTile + kProbeVTile);
+  float* out = MODE == 4 ? sink + kProbeSrcBytes / 4 : sink;
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds[2][kProbeKTile];
   __shared__ __attribute__((aligned(1024))) unsigned char v_lds[2][kProbeVTile];
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
@@ -61,25 +70,41 @@ __global__ __launch_bounds__(256, 3) void probe_mfma_lds_kernel(int steps, float
       const u32x2 r1 = lds_read_tr16(Vs + (16 * half + 8) * kProbeVpb + dt * 64);
       vreg[dt][half] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3));
     }
+  // mode 4: wave-wide load j of a stage fills LDS bytes [j*1024, +1024) from the same bytes of the block
+  constexpr int KL = kProbeKTile / 1024, VL = kProbeVTile / 1024;
+  unsigned k_voff[(KL + 3) / 4], v_voff[(VL + 3) / 4];
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;
+#pragma unroll
+  for (int i = 0; i < (KL + 3) / 4; ++i) k_voff[i] = (unsigned)((wave + 4 * i) * 1024 + 16 * lane);
+#pragma unroll
+  for (int i = 0; i < (VL + 3) / 4; ++i) v_voff[i] = (unsigned)(kProbeKTile + (wave + 4 * i) * 1024 + 16 * lane);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, kProbeKTile + kProbeVTile, 0x00020000);
   float lsum = 0.f, mref = 0.f;
   for (int step = 0; step < steps; ++step) {
     const int st = step & 1;
+    if constexpr (MODE == 4) {
+      issue_loads(rs, k_lds[st ^ 1], wave, 4, KL, k_voff);
+      issue_loads(rs, v_lds[st ^ 1], wave, 4, VL, v_voff);
+    }
     f32x16 s = {};
     const unsigned char* Ks = k_lds[st] + k_lane;
 #pragma unroll
     for (int ks = 0; ks < kProbeD / 16; ++ks)
       s = mfma_32x32x16(MODE == 0 ? kreg[ks] : *(const bf16x8*)(Ks + ks * 32), qf[ks], s);
     unsigned pk[8];
-    if constexpr (MODE == 2) {
+    if constexpr (MODE >= 2) {
       // the softmax's vector work on these scores (values stay small: P <= 2^8)
-      float mx = s[0];
+      float mx = -INFINITY;
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-      mx = pair_max(mx);
-      mref = fmaxf(mref, mx * 0.125f);
-      float l0 = 0.f, l1 = 0.f;
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
+      // never taken with these values (|score| < 8), as the kernel's rescale is rarely taken
+      if (wave_any(mx * 0.125f > mref + kRescaleSlack)) mref = pair_max(mx) * 0.125f;
+      float l0 = __builtin_amdgcn_exp2f(fmaf(s[0], 0.125f, -mref));
+      float l1 = __builtin_amdgcn_exp2f(fmaf(s[1], 0.125f, -mref));
+      pk[0] = pack_bf16x2(l0, l1);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 1; i < 8; ++i) {
         const float e0 = __builtin_amdgcn_exp2f(fmaf(s[2 * i], 0.125f, -mref));
         const float e1 = __builtin_amdgcn_exp2f(fmaf(s[2 * i + 1], 0.125f, -mref));
         l0 += e0;
@@ -110,22 +135,32 @@ __global__ __launch_bounds__(256, 3) void probe_mfma_lds_kernel(int steps, float
         o[dt] = mfma_32x32x16(vf, pb, o[dt]);
       }
     }
+    if constexpr (MODE >= 3) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   }
   float acc = lsum;
   for (int dt = 0; dt < kProbeD / 32; ++dt)
     for (int i = 0; i < 16; ++i) acc += o[dt][i];
-  sink[(size_t)blockIdx.x * 256 + tid] = acc;
+  out[(size_t)blockIdx.x * 256 + tid] = acc;
 }
 
 template __global__ void probe_mfma_lds_kernel<0>(int, float*);
 template __global__ void probe_mfma_lds_kernel<1>(int, float*);
 template __global__ void probe_mfma_lds_kernel<2>(int, float*);
+template __global__ void probe_mfma_lds_kernel<3>(int, float*);
+template __global__ void probe_mfma_lds_kernel<4>(int, float*);
 
 hipError_t launch_probe_mfma(int mode, int workgroups, int steps, float* sink, hipStream_t stream) {
   const dim3 g((unsigned)workgroups), b(256);
-  if (mode == 0) hipLaunchKernelGGL(probe_mfma_lds_kernel<0>, g, b, 0, stream, steps, sink);
-  else if (mode == 1) hipLaunchKernelGGL(probe_mfma_lds_kernel<1>, g, b, 0, stream, steps, sink);
-  else hipLaunchKernelGGL(probe_mfma_lds_kernel<2>, g, b, 0, stream, steps, sink);
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(probe_mfma_lds_kernel<0>, g, b, 0, stream, steps, sink); break;
+    case 1: hipLaunchKernelGGL(probe_mfma_lds_kernel<1>, g, b, 0, stream, steps, sink); break;
+    case 2: hipLaunchKernelGGL(probe_mfma_lds_kernel<2>, g, b, 0, stream, steps, sink); break;
+    case 3: hipLaunchKernelGGL(probe_mfma_lds_kernel<3>, g, b, 0, stream, steps, sink); break;
+    default: hipLaunchKernelGGL(probe_mfma_lds_kernel<4>, g, b, 0, stream, steps, sink); break;
+  }
   return hipGetLastError();
 }
 

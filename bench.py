@@ -250,17 +250,26 @@ PART_KERNELS = {"prefill": ["fwd_bf16_kernel<128, 32, false, 1>"],
 MQA_REPLICAS = 4  # 4 x 0.62 GB of MQA pools: well past the 256 MB last-level cache
 
 
+PROBE_SOURCE_BYTES = 64 * (9216 + 10240)  # the probe's mode-4 source blocks (include/attn_probe.h)
+
+
 def mfma_ceiling(args):
-    """The ceiling probe in its three modes (matrix instructions alone, with LDS operands, with the
-    softmax's vector work too): 768 workgroups (three per CU), timed over several launches of
-    `steps` 32-key steps each, as TFLOP/s and as a fraction of the nominal bf16 peak."""
+    """The ceiling probe in its five modes, each adding one part of the prefill kernel's work: the
+    matrix instructions alone, with LDS operands, with the softmax's vector work, with the
+    per-step wait and barrier, with the global->LDS loads of K and V.  768 workgroups (three per
+    CU), timed over several launches of `steps` 32-key steps each, as TFLOP/s and as a fraction of
+    the nominal bf16 peak."""
     import torch
     import attention_attn_fwd_03_amd as af
     wgs, steps = 768, 4096
-    sink = torch.empty(wgs * 256, device="cuda", dtype=torch.float32)
+    # Source blocks of the load mode first, as bf16 pairs of 0.01 (0x3C24), then the results.
+    sink = torch.empty(PROBE_SOURCE_BYTES // 4 + wgs * 256, device="cuda", dtype=torch.float32)
+    sink.view(torch.int32).fill_(0x3C243C24)
     what = {0: "MFMAs alone, operands in registers", 1: "MFMAs with K / V^T operands read from LDS",
-            2: "MFMAs, LDS operands and the softmax's vector work (max, fma, exp2, add, bf16 pack)"}
-    for mode in (0, 1, 2):
+            2: "MFMAs, LDS operands and the softmax's vector work (max, fma, exp2, add, bf16 pack)",
+            3: "mode 2 plus the per-step wait and workgroup barrier",
+            4: "mode 3 plus the per-step global->LDS loads of K and V (19 KB per workgroup, from L2)"}
+    for mode in (0, 1, 2, 3, 4):
         for _ in range(3):
             af.probe_mfma_ceiling(wgs, steps, sink, mode=mode)
         torch.cuda.synchronize()
@@ -492,9 +501,17 @@ def run_suite(args):
     reps, warm = max(args.steps, 10), max(args.warmup, 3)
 
     def timeit(fn):
-        for _ in range(warm):
+        # Warm up for at least 0.2 s of wall time, not a fixed count: the engine clock takes some
+        # milliseconds to settle after the host-side input generation, and a short kernel's first
+        # few dozen calls would otherwise run at a clock the steady state does not have.
+        t0, n = time.perf_counter(), 0
+        while True:
             fn()
-        torch.cuda.synchronize()
+            n += 1
+            if n >= warm and n % 4 == 0:
+                torch.cuda.synchronize()
+                if time.perf_counter() - t0 >= 0.2:
+                    break
         ev = [_events(2) for _ in range(reps)]
         for e in ev:
             e[0].record()

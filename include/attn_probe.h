@@ -20,12 +20,19 @@ extern "C" {
  * wave), and, by `mode`:
  *   0  nothing else (operands held in registers);
  *   1  the operand reads from LDS (K rows for S^T = K Q^T, V^T by ds_read_b64_tr_b16);
- *   2  mode 1 plus the softmax's vector work per step (row maximum, one fma, exp2 and add per
- *      score, bf16 packing of P).
- * No global loads, no barriers.  sink: device memory of at least workgroups * 256 floats,
- * overwritten (keeps the results live).  Enqueued on `stream`; the caller times it.  Status codes
- * as attn.h: ATTN_ERR_NULL, ATTN_ERR_SHAPE (a count <= 0), ATTN_ERR_UNSUPPORTED (mode not 0-2),
- * ATTN_ERR_WORKSPACE (sink too small), ATTN_ERR_HIP. */
+ *   2  mode 1 plus the softmax's vector work per step (the lane's row maximum tested against the
+ *      reference, one fma, exp2 and add per score, bf16 packing of P);
+ *   3  mode 2 plus the end of the kernel's step: wait for the wave's loads, workgroup barrier;
+ *   4  mode 3 plus the kernel's loads: each step fills the other K and V LDS stages (19 KB per
+ *      workgroup) from global memory with wave-wide global->LDS loads.
+ * Modes 0-3 load nothing from global memory.  sink: device memory of at least workgroups * 256
+ * floats, overwritten (keeps the results live); in mode 4 it must hold ATTN_PROBE_SOURCE_BYTES
+ * more, in front: 64 blocks of 19 KB (one K and one V stage each) that the workgroups read in
+ * turn (block = workgroup index % 64), e.g. small bf16 values; the results go after them.
+ * Enqueued on `stream`; the caller times it.  Status codes as attn.h: ATTN_ERR_NULL,
+ * ATTN_ERR_SHAPE (a count <= 0), ATTN_ERR_UNSUPPORTED (mode not 0-4), ATTN_ERR_WORKSPACE (sink
+ * too small), ATTN_ERR_HIP. */
+#define ATTN_PROBE_SOURCE_BYTES ((size_t)64 * (9216 + 10240))
 int attn_probe_mfma_ceiling(int mode, int workgroups, int steps, float* sink, size_t sink_bytes, void* stream);
 
 #ifdef __cplusplus

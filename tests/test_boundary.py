@@ -534,5 +534,9 @@ def test_probe_rejects_bad_arguments():
     assert L.attn_probe_mfma_ceiling(1, 768, 10, None, 1 << 20, None) == af.ATTN_ERR_NULL
     assert L.attn_probe_mfma_ceiling(1, 0, 10, P, 1 << 20, None) == af.ATTN_ERR_SHAPE
     assert L.attn_probe_mfma_ceiling(1, 768, 0, P, 1 << 20, None) == af.ATTN_ERR_SHAPE
-    assert L.attn_probe_mfma_ceiling(3, 768, 10, P, 1 << 20, None) == af.ATTN_ERR_UNSUPPORTED
+    assert L.attn_probe_mfma_ceiling(5, 768, 10, P, 1 << 20, None) == af.ATTN_ERR_UNSUPPORTED
+    assert L.attn_probe_mfma_ceiling(-1, 768, 10, P, 1 << 20, None) == af.ATTN_ERR_UNSUPPORTED
     assert L.attn_probe_mfma_ceiling(1, 768, 10, P, 768 * 256 * 4 - 4, None) == af.ATTN_ERR_WORKSPACE
+    # the load mode needs its source blocks in front of the results
+    need4 = af.PROBE_SOURCE_BYTES + 768 * 256 * 4
+    assert L.attn_probe_mfma_ceiling(4, 768, 10, P, need4 - 4, None) == af.ATTN_ERR_WORKSPACE
