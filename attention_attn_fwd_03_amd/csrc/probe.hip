@@ -12,7 +12,9 @@
 //   3  mode 2 plus the kernel's end of step: wait for this wave's loads, workgroup barrier;
 //   4  mode 3 plus the kernel's loads: each step fills the other K and V stages (19 KB) from
 //      global memory by wave-wide global->LDS loads, from one of 64 blocks that stay in L2 (as
-//      the prefill's K/V tiles mostly do: the query tiles of a head read the same keys).
+//      the prefill's K/V tiles mostly do: the query tiles of a head read the same keys); Q comes
+//      from the same block, so every operand carries the caller's data (the matrix cores' power,
+//      and with it the clock, depends on the operands' bits).
 // Under sustained matrix load the part runs at its power limit, so these measure how many FLOP/s
 // the matrix cores sustain with each part of the kernel's energy added: the ceilings against which
 // the prefill kernel's own fraction of the nominal peak is read.
@@ -50,8 +52,15 @@ __global__ __launch_bounds__(256, 3) void probe_mfma_lds_kernel(int steps, float
   }
   __syncthreads();
   bf16x8 qf[kProbeD / 16];
-  for (int ks = 0; ks < kProbeD / 16; ++ks)
-    for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)((lane + 3 * ks + e) % 7 - 3) * (1.f / 32.f));
+  if constexpr (MODE == 4) {
+    // Q rows from the source block too (its first 32 rows of 256 bytes), so that all operands
+    // carry the caller's data
+#pragma unroll
+    for (int ks = 0; ks < kProbeD / 16; ++ks) qf[ks] = *(const bf16x8*)(src + col * 256 + ks * 32 + h * 16);
+  } else {
+    for (int ks = 0; ks < kProbeD / 16; ++ks)
+      for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)((lane + 3 * ks + e) % 7 - 3) * (1.f / 32.f));
+  }
   f32x16 o[kProbeD / 32];
   for (int dt = 0; dt < kProbeD / 32; ++dt)
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;

@@ -256,9 +256,10 @@ PROBE_SOURCE_BYTES = 64 * (9216 + 10240)  # the probe's mode-4 source blocks (in
 def mfma_ceiling(args):
     """The ceiling probe in its five modes, each adding one part of the prefill kernel's work: the
     matrix instructions alone, with LDS operands, with the softmax's vector work, with the
-    per-step wait and barrier, with the global->LDS loads of K and V.  768 workgroups (three per
-    CU), timed over several launches of `steps` 32-key steps each, as TFLOP/s and as a fraction of
-    the nominal bf16 peak."""
+    per-step wait and barrier, with the global->LDS loads of K and V; the last once more on
+    operands drawn like the workloads' (the matrix cores' power depends on the operands' bits).
+    768 workgroups (three per CU), timed over several launches of `steps` 32-key steps each, as
+    TFLOP/s and as a fraction of the nominal bf16 peak."""
     import torch
     import attention_attn_fwd_03_amd as af
     wgs, steps = 768, 4096
@@ -268,22 +269,36 @@ def mfma_ceiling(args):
     what = {0: "MFMAs alone, operands in registers", 1: "MFMAs with K / V^T operands read from LDS",
             2: "MFMAs, LDS operands and the softmax's vector work (max, fma, exp2, add, bf16 pack)",
             3: "mode 2 plus the per-step wait and workgroup barrier",
-            4: "mode 3 plus the per-step global->LDS loads of K and V (19 KB per workgroup, from L2)"}
-    for mode in (0, 1, 2, 3, 4):
+            4: "mode 3 plus the per-step global->LDS loads of K and V (19 KB per workgroup, from L2); "
+               "Q, K, V all 0.01",
+            5: "mode 4 with Q, K, V drawn from N(0, 1) in bf16, as the prefill workloads"}
+    for mode in (0, 1, 2, 3, 4, 5):
+        if args.probe_mode is not None and mode != args.probe_mode:
+            continue
+        if mode == 5:  # the same kernel as mode 4, on random operands
+            g = torch.Generator(device="cuda").manual_seed(7)
+            n = PROBE_SOURCE_BYTES // 2
+            sink[:PROBE_SOURCE_BYTES // 4].view(torch.bfloat16).copy_(
+                torch.randn(n, device="cuda", generator=g).to(torch.bfloat16))
+        mode, label = min(mode, 4), mode
         for _ in range(3):
             af.probe_mfma_ceiling(wgs, steps, sink, mode=mode)
         torch.cuda.synchronize()
         ev = _events(2)
-        reps = 10
+        # --probe-seconds: launch for that long (to sample power or clocks meanwhile), about 4 ms each
+        reps = max(10, int(args.probe_seconds * 250)) if args.probe_seconds else 10
         ev[0].record()
-        for _ in range(reps):
+        for i in range(reps):
             af.probe_mfma_ceiling(wgs, steps, sink, mode=mode)
+            if i % 250 == 249:
+                torch.cuda.synchronize()  # keep the queue short so that the launches stay timed
         ev[1].record()
         torch.cuda.synchronize()
         ms = ev[0].elapsed_time(ev[1]) / reps
         flops = wgs * 4 * steps * 16 * 2 * 32 * 32 * 16
         tf = flops / (ms * 1e-3) / 1e12
-        print(json.dumps({"probe": "mfma_ceiling", "mode": mode, "what": what[mode], "workgroups": wgs,
+        print(json.dumps({"probe": "mfma_ceiling", "mode": mode, "operands": "N(0,1)" if label == 5 else "constant",
+                          "what": what[label], "workgroups": wgs,
                           "steps": steps, "ms_per_launch": round(ms, 4), "TFLOP/s": round(tf, 1),
                           "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4), "peak_TFLOP/s": PEAK_BF16_TFLOPS}),
               flush=True)
@@ -298,6 +313,9 @@ def main():
     ap.add_argument("--suite", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--mfma-ceiling", action="store_true")
+    ap.add_argument("--probe-mode", type=int, default=None, help="with --mfma-ceiling: run only this mode (0-5)")
+    ap.add_argument("--probe-seconds", type=float, default=0.0,
+                    help="with --mfma-ceiling: keep each mode running about this long")
     ap.add_argument("--only", choices=[p[0] for p in STEP_PARTS], default=None,
                     help="profile helper: run only this part of the step")
     ap.add_argument("--workload", default=None, help="with --suite: run only this workload")

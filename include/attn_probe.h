@@ -24,7 +24,8 @@ extern "C" {
  *      reference, one fma, exp2 and add per score, bf16 packing of P);
  *   3  mode 2 plus the end of the kernel's step: wait for the wave's loads, workgroup barrier;
  *   4  mode 3 plus the kernel's loads: each step fills the other K and V LDS stages (19 KB per
- *      workgroup) from global memory with wave-wide global->LDS loads.
+ *      workgroup) from global memory with wave-wide global->LDS loads; Q rows come from the same
+ *      source, so all operands carry the caller's data.
  * Modes 0-3 load nothing from global memory.  sink: device memory of at least workgroups * 256
  * floats, overwritten (keeps the results live); in mode 4 it must hold ATTN_PROBE_SOURCE_BYTES
  * more, in front: 64 blocks of 19 KB (one K and one V stage each) that the workgroups read in
