@@ -56,7 +56,17 @@ struct DecCfg {
   static constexpr int K_LOADS = K_STAGE / 1024;  // wave-wide 16-byte-per-lane loads per stage
   static constexpr int V_LOADS = V_STAGE / 1024;
   static_assert(V_STAGE % 1024 == 0, "a V stage must be whole wave-wide loads");
-  static_assert(K_LOADS + V_LOADS <= 63, "one block's loads must fit the vmcnt counter");
+  static_assert(2 * (K_LOADS + V_LOADS) <= 63, "two blocks' loads must fit the vmcnt counter");
+};
+
+// Pipeline stages of the split: three (up to two blocks in flight per worker) for the one-head
+// bf16 layout at d = 128, which runs two workers per CU (2 x 57 KB of LDS), else two.  Measured
+// (three alternating A/B rounds): MQA 1-2% faster, MQA over a paged cache 3-6% faster; FP8 pools
+// (four workers per CU, 4 x 30 KB) were 5% slower on GQA and unchanged on MQA with three, and the
+// packed bf16 layout runs three workers per CU, for which three stages do not fit (3 x 57 KB).
+template <int D, int KV, bool PACKED>
+struct DecStages {
+  static constexpr int value = D == 128 && !PACKED && KV == kKvBf16 ? 3 : 2;
 };
 
 __device__ __forceinline__ bool decode_seq_valid(const DecArgs& a, int n, int64_t base, bool paged) {
@@ -147,15 +157,23 @@ __device__ __forceinline__ void stage_offsets(unsigned (&voff)[N], int lane, int
 // bf16 kernel carries none of the page-table or conversion code, and the one-head layout (MQA,
 // large groups) none of the packed layout's masking.
 template <int D, bool PAGED, int KV, bool PACKED>
-// At d = 128 the two LDS stages (38 KB) allow four waves per CU, one per SIMD, so the wave may use
-// the whole register file; at d = 64 two waves per SIMD fit.
+// At d = 128 at most four waves share a CU (one per SIMD), so the wave may use the whole register
+// file; at d = 64 two waves per SIMD fit.
 __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecArgs a) {
   using C = DecCfg<D, KV>;
-  // Each pipeline stage is its own LDS object, so reading one does not wait for loads into the other.
-  __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[C::K_STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[C::K_STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[C::V_STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[C::V_STAGE];
+  constexpr int NST = DecStages<D, KV, PACKED>::value;
+  // Each pipeline stage (K rows, then V rows) is its own LDS object, so reading one does not wait
+  // for loads into another.
+  __shared__ __attribute__((aligned(1024))) unsigned char kv_lds0[C::K_STAGE + C::V_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char kv_lds1[C::K_STAGE + C::V_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char kv_lds2[NST == 3 ? C::K_STAGE + C::V_STAGE : 1024];
+  auto k_stage = [&](auto stage_c) -> unsigned char* {
+    constexpr int S = decltype(stage_c)::value;
+    if constexpr (S == 0) return kv_lds0;
+    else if constexpr (S == 1) return kv_lds1;
+    else return kv_lds2;
+  };
+  auto v_stage = [&](auto stage_c) -> unsigned char* { return k_stage(stage_c) + C::K_STAGE; };
 
   const int lane = threadIdx.x, h = lane >> 5, col = lane & 31;
   const int team = blockIdx.x / a.rows, u = blockIdx.x % a.rows;
@@ -321,7 +339,6 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
     // piece bad.  A block past the piece's end reads nothing and looks nothing up.
     bool bad = false;
     auto issue = [&](int t0, auto stage_c) {
-      constexpr int STAGE = decltype(stage_c)::value;
       int64_t rbase = base;  // pool row of token 0 of the sequence, as if it were contiguous
       int end = t_end;
       if constexpr (PAGED) {
@@ -339,15 +356,12 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
           }
         }
       }
-      load_to_lds(seq_rsrc(a.k_pool, rbase, t0, end, kvh0, a.Hkv, pack, C::ROWB), STAGE == 0 ? k_lds0 : k_lds1,
-                  k_voff);
-      load_to_lds(seq_rsrc(a.v_pool, rbase, t0, end, kvh0, a.Hkv, pack, C::ROWB), STAGE == 0 ? v_lds0 : v_lds1,
-                  v_voff);
+      load_to_lds(seq_rsrc(a.k_pool, rbase, t0, end, kvh0, a.Hkv, pack, C::ROWB), k_stage(stage_c), k_voff);
+      load_to_lds(seq_rsrc(a.v_pool, rbase, t0, end, kvh0, a.Hkv, pack, C::ROWB), v_stage(stage_c), v_voff);
     };
     // One block (first token t0) held in stage STAGE.
     auto block = [&](int t0, auto stage_c) {
-      constexpr int STAGE = decltype(stage_c)::value;
-      const unsigned char* Ks = (STAGE == 0 ? k_lds0 : k_lds1) + k_lane;
+      const unsigned char* Ks = k_stage(stage_c) + k_lane;
       f32x16 sv[1];
 #pragma unroll
       for (int i = 0; i < 16; ++i) sv[0][i] = 0.f;
@@ -377,7 +391,7 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
       const float mb = update_max(sv, st, o, c);
       unsigned pk[8];
       exp_block(sv[0], c, mb, st, pk);
-      const unsigned char* Vs = (STAGE == 0 ? v_lds0 : v_lds1) + v_lane;
+      const unsigned char* Vs = v_stage(stage_c) + v_lane;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const u32x4 pw = {pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]};
@@ -397,21 +411,44 @@ __global__ __launch_bounds__(64, D == 128 ? 1 : 2) void decode_split_kernel(DecA
       }
     };
 
-    // The block after the current one is always issued, even past the piece's end (it then
-    // reads nothing), which keeps the loop free of branches around the loads.
+    // The blocks after the current one are always issued, even past the piece's end (they then
+    // read nothing), which keeps the loop free of branches around the loads.
     issue(t_begin, S0{});
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < QL; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, q_word(qraw[ks], qt, q_ok));
-    for (int t0 = t_begin;; t0 += 2 * tpb) {
-      issue(t0 + tpb, S1{});
-      __builtin_amdgcn_s_waitcnt(kWaitBlock);
-      block(t0, S0{});
-      if (t0 + tpb >= t_end) break;
-      issue(t0 + 2 * tpb, S0{});
-      __builtin_amdgcn_s_waitcnt(kWaitBlock);
-      block(t0 + tpb, S1{});
-      if (t0 + 2 * tpb >= t_end) break;
+    if constexpr (NST == 2) {
+      for (int t0 = t_begin;; t0 += 2 * tpb) {
+        issue(t0 + tpb, S1{});
+        __builtin_amdgcn_s_waitcnt(kWaitBlock);
+        block(t0, S0{});
+        if (t0 + tpb >= t_end) break;
+        issue(t0 + 2 * tpb, S0{});
+        __builtin_amdgcn_s_waitcnt(kWaitBlock);
+        block(t0 + tpb, S1{});
+        if (t0 + 2 * tpb >= t_end) break;
+      }
+    } else {
+      // Two blocks in flight while one is computed, except during the third block of each round:
+      // at the top of the loop only the block read first may be in flight.  The compiler's record
+      // of which LDS stage a global->LDS load writes does not survive the loop's back edge, so a
+      // load still in flight there into another stage would make the first read wait for it.
+      constexpr unsigned kWaitTwo = vmcnt_at_most(2 * (C::K_LOADS + C::V_LOADS));
+      using S2 = std::integral_constant<int, 2>;
+      for (int t0 = t_begin;; t0 += 3 * tpb) {
+        issue(t0 + tpb, S1{});
+        issue(t0 + 2 * tpb, S2{});
+        __builtin_amdgcn_s_waitcnt(kWaitTwo);
+        block(t0, S0{});
+        if (t0 + tpb >= t_end) break;
+        issue(t0 + 3 * tpb, S0{});
+        __builtin_amdgcn_s_waitcnt(kWaitTwo);
+        block(t0 + tpb, S1{});
+        if (t0 + 2 * tpb >= t_end) break;
+        __builtin_amdgcn_s_waitcnt(kWaitBlock);
+        block(t0 + 2 * tpb, S2{});
+        if (t0 + 3 * tpb >= t_end) break;
+      }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));  // no load may still target LDS past this point
 
@@ -639,15 +676,19 @@ int decode_workers(int d, bool fp8, bool packed) {
   if (w > 0) return w;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  // the occupancy of the variant that will run (its stage count sets its LDS)
+  auto occ = [&](auto kernel) { return hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64, 0); };
   hipError_t e;
-  if (fp8)
-    e = d == 128
-            ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<128, false, kKvE4M3, true>, 64, 0)
-            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<64, false, kKvE4M3, true>, 64, 0);
+  if (d == 128)
+    e = fp8 ? (packed ? occ(decode_split_kernel<128, false, kKvE4M3, true>)
+                      : occ(decode_split_kernel<128, false, kKvE4M3, false>))
+            : (packed ? occ(decode_split_kernel<128, false, kKvBf16, true>)
+                      : occ(decode_split_kernel<128, false, kKvBf16, false>));
   else
-    e = d == 128
-            ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<128, false, kKvBf16, true>, 64, 0)
-            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<64, false, kKvBf16, true>, 64, 0);
+    e = fp8 ? (packed ? occ(decode_split_kernel<64, false, kKvE4M3, true>)
+                      : occ(decode_split_kernel<64, false, kKvE4M3, false>))
+            : (packed ? occ(decode_split_kernel<64, false, kKvBf16, true>)
+                      : occ(decode_split_kernel<64, false, kKvBf16, false>));
   if (e != hipSuccess || cus <= 0 || per_cu <= 0) return -1;
   const int cap = fp8 ? kDecodeWorkersPerCuFp8 : packed ? kDecodeWorkersPerCu : kDecodeWorkersPerCuOneHead;
   if (per_cu > cap) per_cu = cap;
