@@ -78,8 +78,6 @@ def test_named_workload_full_size(name):
 @pytest.mark.parametrize("L", [1, 2, 63, 64, 65, 127, 129, 1000, 4097])
 @pytest.mark.parametrize("causal", [False, True])
 def test_lengths(L, causal, dtype):
-    if L == 4097 and dtype == "f32":
-        pytest.skip("covered by bf16; fp32 oracle time")
     full_case(1, 2, 1, L, L, 128, causal, 0, dtype, seed=100 + L)
 
 
