@@ -39,9 +39,20 @@ struct BwdCfg {
   static constexpr int NPB = ROWB + 16; // LDS pitch of tiles read only as the A operand
 };
 
-// Query rows per step of the dK/dV kernel (64 measured about 10% faster than 32: half the
-// barriers and step-ahead loads per product).
-constexpr int kBwdQStep = 64;
+// Query rows per step of the dK/dV kernel.  Its three Q and three dO stages, each its own LDS
+// object, must lie within the 64 KB an LDS instruction's offset reaches, or the compiler keeps a
+// separate address per stage and runs out of registers: at d = 128 that allows 32 rows (6 x 8 KB).
+// (64-row steps at d = 64 measured 14% slower than 32.)
+constexpr int kBwdQStep = 32;
+
+// s_waitcnt immediate that waits for this wave's LDS (and scalar) operations only.
+constexpr unsigned kLgkmDone = 0xC07Fu;
+
+// Workgroup barrier for a loop whose global->LDS loads stay in flight across it.
+// __syncthreads() also fences memory, which makes the compiler wait for every outstanding
+// vector-memory load first; here each wave has already waited (s_waitcnt) for what the others
+// will read.  The "memory" clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_after_waits() { asm volatile("s_barrier" ::: "memory"); }
 
 constexpr int round1k(int x) { return (x + 1023) / 1024 * 1024; }
 
@@ -335,21 +346,39 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int T_LOADS = T_TILE / 1024, TLW = (T_LOADS + 3) / 4;
   constexpr int OPB = 2 * D + 8;
   static_assert(T_TILE % 1024 == 0, "whole wave-wide loads");
-  // Three stages of Q and dO rows: the loads of step s + 2 are issued at the start of step s, so
-  // a step's loads have two steps of compute to land (one wave per SIMD hides nothing else).  The
-  // epilogue reuses the stages as its scratch (32 rows per wave).
-  constexpr int NST = 3;
-  constexpr int SMEM = 2 * NST * T_TILE > 4 * 32 * OPB ? 2 * NST * T_TILE : 4 * 32 * OPB;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
+  // Three stages of Q and dO rows, each its own LDS object, the stage of every step known at
+  // compile time (the loop below is unrolled three times): the compiler can then see that reading
+  // one stage does not depend on the loads still landing in another.  The loop is rotated so that
+  // at its top no load is in flight (the compiler's record of which object a global->LDS load
+  // writes does not survive the back edge): per round of three steps, the first two compute with
+  // the next two steps' loads in flight, the third with the next one's.  A stage array also holds
+  // one wave's 32 output rows for the epilogue.
+  constexpr int ST_BYTES = T_TILE > 32 * OPB ? T_TILE : round1k(32 * OPB);
+  __shared__ __attribute__((aligned(1024))) unsigned char q_lds0[ST_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char q_lds1[ST_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char q_lds2[ST_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char d_lds0[ST_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char d_lds1[ST_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char d_lds2[ST_BYTES];
   __shared__ __attribute__((aligned(16))) float row_lds[2][2][BQS];  // [step parity][lse offset, D][row]
-  // The stage index is a runtime (wave-uniform) value: one copy of the loop body, so the per-lane
-  // LDS offsets are held once rather than once per stage.
-  auto q_stage = [&](int st) -> unsigned char* { return smem + st * T_TILE; };
-  auto d_stage = [&](int st) -> unsigned char* { return smem + (NST + st) * T_TILE; };
-  // Every wave issues T_LOADS / 4 loads per tile and two tiles per step; waiting until at most that
-  // many loads are outstanding leaves only the newest step's in flight (loads complete in order).
+  auto q_stage = [&](auto st_c) -> unsigned char* {
+    constexpr int S = decltype(st_c)::value;
+    if constexpr (S == 0) return q_lds0;
+    else if constexpr (S == 1) return q_lds1;
+    else return q_lds2;
+  };
+  auto d_stage = [&](auto st_c) -> unsigned char* {
+    constexpr int S = decltype(st_c)::value;
+    if constexpr (S == 0) return d_lds0;
+    else if constexpr (S == 1) return d_lds1;
+    else return d_lds2;
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  // Every wave issues T_LOADS / 4 loads per tile, two tiles per step.
   static_assert(T_LOADS % 4 == 0, "every wave issues the same number of loads");
-  constexpr unsigned kWaitAhead = vmcnt_at_most(2 * (T_LOADS / 4));
+  constexpr int STEP_LOADS = 2 * (T_LOADS / 4);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;
@@ -411,19 +440,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   tile_offsets_swz<D>(t_voff, wave, 4, lane, BQS);
   // Step (qi, hd): query head hkv * group + hd, rows q_top - qi * BQS .. + BQS - 1.
   const int q_top = q0_first + (n_qsteps - 1) * BQS;
-  auto issue = [&](int st, int qi, int hd) {
-    const int q0 = q_top - qi * BQS;
-    const size_t off = ((size_t)(b * a.Hq + hkv * a.group + hd) * a.Lq) * D;
-    issue_loads(rows_rsrc((const unsigned short*)a.q + off, q0, a.Lq, C::ROWB), q_stage(st), wave, 4, T_LOADS, t_voff);
-    issue_loads(rows_rsrc((const unsigned short*)a.dout + off, q0, a.Lq, C::ROWB), d_stage(st), wave, 4, T_LOADS,
+  // Loads of step (qi, hd) into a stage.  Past the last step (`live` false) the same loads run over
+  // an empty buffer and fill the stage with zeros that nothing reads, so every step issues the
+  // same loads and the compiler can count them.
+  auto issue = [&](auto st_c, int qi, int hd, bool live) {
+    const int q0 = live ? q_top - qi * BQS : a.Lq;
+    const size_t off = ((size_t)(b * a.Hq + hkv * a.group + (live ? hd : 0)) * a.Lq) * D;
+    issue_loads(rows_rsrc((const unsigned short*)a.q + off, q0, a.Lq, C::ROWB), q_stage(st_c), wave, 4, T_LOADS,
+                t_voff);
+    issue_loads(rows_rsrc((const unsigned short*)a.dout + off, q0, a.Lq, C::ROWB), d_stage(st_c), wave, 4, T_LOADS,
                 t_voff);
   };
-  // LSE offsets (threads 0 .. BQS-1) and D (threads BQS .. 2*BQS-1) of a step's rows, fetched a
-  // step ahead and written to LDS before the barrier that precedes their use.
-  auto fetch_rows = [&](int qi, int hd, float& v) {
+  // LSE offsets (threads 0 .. BQS-1) and D (threads BQS .. 2*BQS-1) of a step's rows, fetched
+  // before that step's predecessor computes and written to LDS before the barrier that precedes
+  // their use.  Every thread loads (clamped; the others discard theirs), and the value is
+  // converted only when it is stored, so no wave waits for the load before computing.
+  auto fetch_rows = [&](int qi, int hd, float& raw, bool& valid) {
     const int r = q_top - qi * BQS + (tid % BQS);
-    const size_t idx = (size_t)(b * a.Hq + hkv * a.group + hd) * a.Lq + (r < a.Lq ? r : 0);
-    v = tid < BQS ? (r < a.Lq ? lse_offset(a.lse[idx]) : INFINITY) : (r < a.Lq ? a.dvec[idx] : 0.f);
+    valid = r < a.Lq && qi < n_qsteps;
+    const size_t idx = (size_t)(b * a.Hq + hkv * a.group + (qi < n_qsteps ? hd : 0)) * a.Lq +
+                       (valid ? r : 0);
+    raw = (tid < BQS ? a.lse : a.dvec)[idx];
+  };
+  auto row_value = [&](float raw, bool valid) {
+    return tid < BQS ? (valid ? lse_offset(raw) : INFINITY) : (valid ? raw : 0.f);
   };
   const float c = a.c2;
 
@@ -438,15 +478,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   advance(qi1, hd1);
   int qi2 = qi1, hd2 = hd1;
   advance(qi2, hd2);
-  int cur = 0;  // stage of step s; step s + 2 loads into stage (cur + 2) % NST
-  auto step = [&](int s) {
-    float next_row = 0.f;
-    const bool more = s + 1 < n_steps, more2 = s + 2 < n_steps;
-    if (more && tid < 2 * BQS) fetch_rows(qi1, hd1, next_row);
-    if (more2) issue(cur == 0 ? 2 : cur - 1, qi2, hd2);
+  // One step on stage ST: fetch the next step's rows, issue the loads given (`ahead`: how many
+  // steps' loads follow it in flight when it ends), compute, wait until only those are in flight,
+  // store the next step's rows, barrier.
+  auto step = [&](int s, auto st_c, auto issue_c, auto ahead_c) {
+    float next_raw;
+    bool next_valid;
+    fetch_rows(qi1, hd1, next_raw, next_valid);
+    __builtin_amdgcn_sched_barrier(0);  // the row load goes out before the tile loads
+    issue_c();
     const int q0 = q_top - qi * BQS;
-    const unsigned char* Qs = q_stage(cur);
-    const unsigned char* Ds = d_stage(cur);
+    const unsigned char* Qs = q_stage(st_c);
+    const unsigned char* Ds = d_stage(st_c);
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const int qb0 = q0 + 32 * qb;
@@ -494,37 +537,53 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
           }
       }
     }
-    // Step s + 1's tiles have landed (only step s + 2's may still be in flight), and so has its
-    // row fetch, which was issued before them.
-    if (more2)
-      __builtin_amdgcn_s_waitcnt(kWaitAhead);
-    else
-      __builtin_amdgcn_s_waitcnt(0);
-    if (more && tid < 2 * BQS) row_lds[(s + 1) & 1][tid / BQS][tid % BQS] = next_row;
+    // The next step's tiles have landed (only `ahead` steps' loads may still be in flight), and
+    // so has its row fetch, which was issued before them.
+    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(decltype(ahead_c)::value * STEP_LOADS));
+    const float rv = row_value(next_raw, next_valid);
+    if (tid < 2 * BQS) row_lds[(s + 1) & 1][tid / BQS][tid % BQS] = rv;
     qi = qi1;
     qi1 = qi2;
     hd1 = hd2;
     advance(qi2, hd2);
-    cur = cur == NST - 1 ? 0 : cur + 1;
-    __syncthreads();
+    // This wave's LDS reads of the stage and its row_lds writes are done before the others pass.
+    __builtin_amdgcn_s_waitcnt(kLgkmDone);
+    barrier_after_waits();
   };
+  using A0 = std::integral_constant<int, 0>;
+  using A1 = std::integral_constant<int, 1>;
 
   if (n_steps > 0) {
-    issue(0, 0, 0);
-    if (n_steps > 1) issue(1, qi1, hd1);
-    if (tid < 2 * BQS) {
-      float v;
-      fetch_rows(0, 0, v);
-      row_lds[0][tid / BQS][tid % BQS] = v;
+    issue(S0{}, 0, 0, true);
+    {
+      float raw;
+      bool valid;
+      fetch_rows(0, 0, raw, valid);
+      const float rv = row_value(raw, valid);
+      if (tid < 2 * BQS) row_lds[0][tid / BQS][tid % BQS] = rv;
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int s = 0; s < n_steps; ++s) step(s);
+    // (qi, hd) of steps s + 1 and s + 2 are (qi1, hd1) and (qi2, hd2) at the start of step s.
+    for (int s = 0; s < n_steps; s += 3) {
+      // top of the round: nothing in flight; step s's tiles are in stage 0
+      step(s, S0{}, [&] {
+        issue(S1{}, qi1, hd1, s + 1 < n_steps);
+        issue(S2{}, qi2, hd2, s + 2 < n_steps);
+      }, A1{});
+      if (s + 1 >= n_steps) break;
+      step(s + 1, S1{}, [&] { issue(S0{}, qi2, hd2, s + 3 < n_steps); }, A1{});
+      if (s + 2 >= n_steps) break;
+      step(s + 2, S2{}, [] {}, A0{});
+    }
+    // The zero-filling loads past the last step land in stages the epilogue reuses.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
   const int nrows = a.Lk - kw;
   if (nrows > 0) {
-    // Wave w stages its rows at w * 32 * OPB (the stages are free after the loop's last barrier).
-    unsigned char* scratch = smem + wave * 32 * OPB;
+    // Wave w stages its rows in a stage of its own (all are free after the loop).
+    unsigned char* scratch = wave == 0 ? q_lds0 : wave == 1 ? q_lds1 : wave == 2 ? q_lds2 : d_lds0;
     store_rows_t<D>(dk, a.scale, scratch, (unsigned short*)a.dk + kv_off + (size_t)kw * D, nrows, lane);
     store_rows_t<D>(dv, 1.f, scratch, (unsigned short*)a.dv + kv_off + (size_t)kw * D, nrows, lane);
   }
