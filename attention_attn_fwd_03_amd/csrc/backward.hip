@@ -207,12 +207,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr int KLW = (K_LOADS + 3) / 4, VLW = (V_LOADS + 3) / 4;
   constexpr int OPB = 2 * D + 8;                        // epilogue scratch pitch
   static_assert(K_TILE % 1024 == 0, "whole wave-wide loads");
-  static_assert(4 * 32 * OPB <= 2 * (K_TILE + V_TILE), "the stages hold the epilogue scratch");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * (K_TILE + V_TILE)];
+  // Each stage is its own LDS object, so the compiler can see that reading one does not depend on
+  // the loads still landing in the other and does not wait for them in the middle of a step.  Each
+  // also holds one wave's 32 output rows for the epilogue.
+  constexpr int K_BYTES = K_TILE > 32 * OPB ? K_TILE : round1k(32 * OPB);
+  static_assert(V_TILE >= 32 * OPB, "a V stage holds one wave's output rows");
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[K_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[K_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[V_TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[V_TILE];
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  auto k_stage = [&](auto st) -> unsigned char* { return smem + decltype(st)::value * K_TILE; };
-  auto v_stage = [&](auto st) -> unsigned char* { return smem + 2 * K_TILE + decltype(st)::value * V_TILE; };
+  auto k_stage = [&](auto st) -> unsigned char* {
+    if constexpr (decltype(st)::value == 0) return k_lds0;
+    else return k_lds1;
+  };
+  auto v_stage = [&](auto st) -> unsigned char* {
+    if constexpr (decltype(st)::value == 0) return v_lds0;
+    else return v_lds1;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;
@@ -322,12 +335,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       if (kt + 1 <= hi) step(kt + 1, S1{});
     }
   }
-  // The stages are free (the last step ended with a barrier, no loads in flight): wave w stages
-  // its rows at w * 32 * OPB.
+  // The stages are free (the last step ended with a barrier, no loads in flight): each wave
+  // stages its rows in a stage of its own.
   const int nrows = a.Lq - w_start;
+  unsigned char* scratch = wave == 0 ? k_lds0 : wave == 1 ? k_lds1 : wave == 2 ? v_lds0 : v_lds1;
   if (nrows > 0)
-    store_rows_t<D>(acc, a.scale, smem + wave * 32 * OPB, (unsigned short*)a.dq + q_off + (size_t)w_start * D, nrows,
-                    lane);
+    store_rows_t<D>(acc, a.scale, scratch, (unsigned short*)a.dq + q_off + (size_t)w_start * D, nrows, lane);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -354,6 +367,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // the next two steps' loads in flight, the third with the next one's.  A stage array also holds
   // one wave's 32 output rows for the epilogue.
   constexpr int ST_BYTES = T_TILE > 32 * OPB ? T_TILE : round1k(32 * OPB);
+  static_assert(6 * ST_BYTES + 2 * 2 * BQS * 4 <= 65536, "the stages stay within an LDS offset's reach");
   __shared__ __attribute__((aligned(1024))) unsigned char q_lds0[ST_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char q_lds1[ST_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char q_lds2[ST_BYTES];
