@@ -454,16 +454,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   tile_offsets_swz<D>(t_voff, wave, 4, lane, BQS);
   // Step (qi, hd): query head hkv * group + hd, rows q_top - qi * BQS .. + BQS - 1.
   const int q_top = q0_first + (n_qsteps - 1) * BQS;
+  // Row (over batch, head and position) of position 0 of the group's first query head: the rows
+  // of Q, dO, the LSE and D are addressed from it with one scalar product per step.
+  const int64_t grp_row0 = (int64_t)(b * a.Hq + hkv * a.group) * a.Lq;
   // Loads of step (qi, hd) into a stage.  Past the last step (`live` false) the same loads run over
   // an empty buffer and fill the stage with zeros that nothing reads, so every step issues the
   // same loads and the compiler can count them.
   auto issue = [&](auto st_c, int qi, int hd, bool live) {
     const int q0 = live ? q_top - qi * BQS : a.Lq;
-    const size_t off = ((size_t)(b * a.Hq + hkv * a.group + (live ? hd : 0)) * a.Lq) * D;
-    issue_loads(rows_rsrc((const unsigned short*)a.q + off, q0, a.Lq, C::ROWB), q_stage(st_c), wave, 4, T_LOADS,
-                t_voff);
-    issue_loads(rows_rsrc((const unsigned short*)a.dout + off, q0, a.Lq, C::ROWB), d_stage(st_c), wave, 4, T_LOADS,
-                t_voff);
+    const uint64_t byte = (uint64_t)(grp_row0 + (int64_t)(live ? hd : 0) * a.Lq + q0) * C::ROWB;
+    const int bytes = (a.Lq - q0 > 0 ? a.Lq - q0 : 0) * C::ROWB;
+    issue_loads(__builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned char*)a.q + byte), 0, bytes, 0x00020000),
+                q_stage(st_c), wave, 4, T_LOADS, t_voff);
+    issue_loads(__builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned char*)a.dout + byte), 0, bytes, 0x00020000),
+                d_stage(st_c), wave, 4, T_LOADS, t_voff);
   };
   // LSE offsets (threads 0 .. BQS-1) and D (threads BQS .. 2*BQS-1) of a step's rows, fetched
   // before that step's predecessor computes and written to LDS before the barrier that precedes
@@ -472,8 +476,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   auto fetch_rows = [&](int qi, int hd, float& raw, bool& valid) {
     const int r = q_top - qi * BQS + (tid % BQS);
     valid = r < a.Lq && qi < n_qsteps;
-    const size_t idx = (size_t)(b * a.Hq + hkv * a.group + (qi < n_qsteps ? hd : 0)) * a.Lq +
-                       (valid ? r : 0);
+    const size_t idx = (size_t)(grp_row0 + (int64_t)(qi < n_qsteps ? hd : 0) * a.Lq) + (valid ? r : 0);
     raw = (tid < BQS ? a.lse : a.dvec)[idx];
   };
   auto row_value = [&](float raw, bool valid) {
