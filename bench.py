@@ -20,6 +20,7 @@ to back (no other kernel between its calls) and reported beside the in-step figu
                                  # bf16 ones, both decode batches in a
                                  # paged cache, and a ragged chunked-prefill batch), for the tables
   python bench.py --mfma-ceiling # the matrix-core + LDS ceiling probe (include/attn_probe.h)
+  python bench.py --gemm-reference  # a plain bf16 GEMM through the platform library, for reference
   python bench.py --copy-calib   # a plain device copy of known size, to scale HBM counters
   python bench.py --summarize-counters FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR [MFMA_DIR]
                                  # rocprofv3 --pmc outputs -> per-launch HBM bytes (profiles/hbm_traffic.md)
@@ -304,6 +305,41 @@ def mfma_ceiling(args):
               flush=True)
 
 
+def gemm_reference(args):
+    """A plain bf16 matrix product C = A B (8192 x 8192 x 8192, fp32 accumulation, bf16 result)
+    through the platform's tuned GEMM library (torch.matmul), on operands drawn from N(0, 1) and on
+    constant operands: what the matrix cores sustain on the dense product alone, the reference
+    beside which the attention kernels' fraction of the nominal peak is read.  Not part of the
+    attention path."""
+    import torch
+    n = 8192
+    g = torch.Generator(device="cuda").manual_seed(11)
+    cases = {"N(0,1)": (torch.randn(n, n, device="cuda", generator=g).to(torch.bfloat16),
+                        torch.randn(n, n, device="cuda", generator=g).to(torch.bfloat16)),
+             "constant": (torch.full((n, n), 0.01, device="cuda", dtype=torch.bfloat16),
+                          torch.full((n, n), 0.01, device="cuda", dtype=torch.bfloat16))}
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    for label, (a, b) in cases.items():
+        for _ in range(5):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        reps = max(50, int(args.probe_seconds / 1.2e-3)) if args.probe_seconds else 50  # about 1.1 ms per call
+        ev = _events(2)
+        ev[0].record()
+        for i in range(reps):
+            torch.matmul(a, b, out=c)
+            if i % 500 == 499:
+                torch.cuda.synchronize()
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / reps
+        tf = 2 * n ** 3 / (ms * 1e-3) / 1e12
+        print(json.dumps({"reference": "bf16_gemm", "M": n, "N": n, "K": n, "operands": label,
+                          "ms_per_call": round(ms, 4), "TFLOP/s": round(tf, 1),
+                          "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4), "peak_TFLOP/s": PEAK_BF16_TFLOPS}),
+              flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -313,6 +349,7 @@ def main():
     ap.add_argument("--suite", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--mfma-ceiling", action="store_true")
+    ap.add_argument("--gemm-reference", action="store_true")
     ap.add_argument("--probe-mode", type=int, default=None, help="with --mfma-ceiling: run only this mode (0-5)")
     ap.add_argument("--probe-seconds", type=float, default=0.0,
                     help="with --mfma-ceiling: keep each mode running about this long")
@@ -358,6 +395,8 @@ def main():
         return
     if args.mfma_ceiling:
         return mfma_ceiling(args)
+    if args.gemm_reference:
+        return gemm_reference(args)
     if args.suite:
         return run_suite(args)
 
