@@ -7,6 +7,8 @@ covered too.  Every case is reproducible from its id."""
 import numpy as np
 import pytest
 
+from test_backward_gpu import bwd_case
+from test_fp8_gpu import fp8_case, fp8_fwd_case
 from test_parity_gpu import decode_case, full_case, varlen_case
 
 
@@ -68,6 +70,46 @@ def _varlen_cases(n=8, seed=20261205):
     return cases
 
 
+def _backward_cases(n=10, seed=20261206):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        Hq = Hkv * int(rng.choice([1, 2, 3, 4]))
+        B = int(rng.integers(1, 3))
+        Lq = int(rng.integers(1, 400))
+        Lk = Lq if rng.random() < 0.5 else int(rng.integers(1, 400))
+        causal = i % 4 != 1 and bool(rng.random() < 0.85)
+        window = int(rng.integers(1, Lk + 20)) if causal and i % 3 == 0 else 0
+        cases.append((B, Hq, Hkv, Lq, Lk, d, causal, window, 9300 + i))
+    return cases
+
+
+def _fp8_cases(n=10, seed=20261207):
+    """FP8 prefill (even draws) and FP8 KV decode (odd draws), both formats."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        fmt = "e4m3fn" if i % 4 < 2 else "e5m2"
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        Hq = Hkv * int(rng.choice([1, 2, 4]))
+        if i % 2 == 0:
+            Lq = int(rng.integers(1, 500))
+            Lk = Lq if rng.random() < 0.5 else int(rng.integers(1, 500))
+            causal = bool(rng.random() < 0.7)
+            window = int(rng.integers(1, Lk + 20)) if causal and rng.random() < 0.5 else 0
+            cases.append(("prefill", fmt, int(rng.integers(1, 3)), Hq, Hkv, Lq, Lk, d, causal, window, 9400 + i))
+        else:
+            n_seq = int(rng.integers(1, 50))
+            lens = rng.integers(0, 2500, n_seq)
+            lens[0] = max(int(lens[0]), 1)
+            window = 0 if rng.random() < 0.6 else int(rng.integers(1, 1500))
+            cases.append(("decode", fmt, lens.astype(np.int32).tolist(), Hq, Hkv, d, window, 9400 + i))
+    return cases
+
+
 def _id(c):
     return "-".join(str(x) if not isinstance(x, list) else f"n{len(x)}" for x in c)
 
@@ -95,6 +137,24 @@ def test_random_varlen(case):
     varlen_case(lq, lk, Hq, Hkv, d, causal=causal, window=window, seed=seed)
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", _backward_cases(), ids=_id)
+def test_random_backward(case):
+    B, Hq, Hkv, Lq, Lk, d, causal, window, seed = case
+    bwd_case(B, Hq, Hkv, Lq, Lk, d, causal=causal, window=window, seed=seed)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", _fp8_cases(), ids=_id)
+def test_random_fp8(case):
+    if case[0] == "prefill":
+        _, fmt, B, Hq, Hkv, Lq, Lk, d, causal, window, seed = case
+        fp8_fwd_case(B, Hq, Hkv, Lq, Lk, d, causal, window, fmt, seed=seed)
+    else:
+        _, fmt, lens, Hq, Hkv, d, window, seed = case
+        fp8_case(lens, Hq, Hkv, d, fmt, window=window, seed=seed)
+
+
 def test_the_draws_cover_the_space():
     """(Host only.)  The seeded draws include each kind of case at least once, so that a change of
     seed that loses one shows here."""
@@ -106,3 +166,8 @@ def test_the_draws_cover_the_space():
     assert any(0 in c[0] for c in dec) and any(c[4] for c in dec) and any(c[1] % 32 and c[1] > 32 for c in dec)
     var = _varlen_cases()
     assert any(0 in c[0] for c in var) and any(c[6] for c in var) and any(not c[5] for c in var)
+    bwd = _backward_cases()
+    assert any(c[7] for c in bwd) and any(not c[6] for c in bwd) and any(c[3] != c[4] for c in bwd)
+    assert {c[5] for c in bwd} == {64, 128}
+    f8 = _fp8_cases()
+    assert {c[0] for c in f8} == {"prefill", "decode"} and {c[1] for c in f8} == {"e4m3fn", "e5m2"}
