@@ -9,7 +9,7 @@ import pytest
 
 from test_backward_gpu import bwd_case
 from test_fp8_gpu import fp8_case, fp8_fwd_case
-from test_parity_gpu import decode_case, full_case, varlen_case
+from test_parity_gpu import decode_case, decode_paged_case, full_case, varlen_case
 
 
 def _prefill_cases(n=24, seed=20261203):
@@ -110,6 +110,24 @@ def _fp8_cases(n=10, seed=20261207):
     return cases
 
 
+def _paged_cases(n=8, seed=20261208):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        n_seq = int(rng.integers(1, 40))
+        lens = rng.integers(0, 2500, n_seq)
+        lens[0] = max(int(lens[0]), 1)
+        if i % 2 == 0:
+            lens = np.append(lens, 0)  # an empty sequence
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        Hq = Hkv * int(rng.choice([1, 2, 4, 8]))
+        d = int(rng.choice([64, 128]))
+        page = int(rng.choice([32, 64, 128, 256]))  # multiples of every layout's block
+        window = 0 if rng.random() < 0.6 else int(rng.integers(1, 1500))
+        cases.append((lens.astype(np.int32).tolist(), Hq, Hkv, d, page, window, 9500 + i))
+    return cases
+
+
 def _id(c):
     return "-".join(str(x) if not isinstance(x, list) else f"n{len(x)}" for x in c)
 
@@ -155,6 +173,13 @@ def test_random_fp8(case):
         fp8_case(lens, Hq, Hkv, d, fmt, window=window, seed=seed)
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", _paged_cases(), ids=_id)
+def test_random_paged_decode(case):
+    lens, Hq, Hkv, d, page, window, seed = case
+    decode_paged_case(lens, Hq, Hkv, d, page, window=window, seed=seed)
+
+
 def test_the_draws_cover_the_space():
     """(Host only.)  The seeded draws include each kind of case at least once, so that a change of
     seed that loses one shows here."""
@@ -171,3 +196,5 @@ def test_the_draws_cover_the_space():
     assert {c[5] for c in bwd} == {64, 128}
     f8 = _fp8_cases()
     assert {c[0] for c in f8} == {"prefill", "decode"} and {c[1] for c in f8} == {"e4m3fn", "e5m2"}
+    pg = _paged_cases()
+    assert len({c[4] for c in pg}) >= 3 and any(c[5] for c in pg) and any(0 in c[0] for c in pg)
