@@ -180,6 +180,21 @@ def test_random_paged_decode(case):
     decode_paged_case(lens, Hq, Hkv, d, page, window=window, seed=seed)
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("Hkv,d", [(8, 128), (1, 64)])
+def test_decode_many_short_sequences(Hkv, d):
+    """Thousands of sequences, most shorter than one block and some empty: far more sequences than
+    teams, so shares span many sequences and most pieces are whole short sequences."""
+    rng = np.random.default_rng(9600 + Hkv + d)
+    lens = rng.integers(0, 90, 3000).astype(np.int32)
+    lens[::7] = 0
+    lens[1] = 700
+    decode_case(lens.tolist(), 8 * Hkv if Hkv > 1 else 16, Hkv, d, seed=9600 + Hkv + d)
+    paged = rng.integers(0, 300, 1500).astype(np.int32)
+    paged[0] = 1
+    decode_paged_case(paged.tolist(), 8 * Hkv if Hkv > 1 else 16, Hkv, d, 64, seed=9650 + Hkv + d)
+
+
 def test_the_draws_cover_the_space():
     """(Host only.)  The seeded draws include each kind of case at least once, so that a change of
     seed that loses one shows here."""
