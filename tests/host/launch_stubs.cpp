@@ -28,6 +28,6 @@ void* decode_scratch() {
 
 }  // namespace attnfwd
 
-// Present only in this build: lets a test refuse to make valid-argument calls (which, in the real
+// Present only in the host-stub library: lets a test refuse to make valid-argument calls (which, in the real
 // library, would launch kernels on fake pointers) against anything else.
 extern "C" int attn_host_stub_build(void) { return 1; }
